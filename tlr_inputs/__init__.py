@@ -1,0 +1,11 @@
+"""Seeded synthetic inputs for the Tile-Low-Rank GEMM.
+
+This package only draws random numbers and arranges them per tile.  It holds
+none of the product's arithmetic, so both the CPU oracle and the GPU path may
+import it.
+"""
+from .gen import (TLRTiles, CONFIGS, config_inputs, config_ranks, random_tlr,
+                  tile_sizes, ranks_from_fn)
+
+__all__ = ["TLRTiles", "CONFIGS", "config_inputs", "config_ranks", "random_tlr",
+           "tile_sizes", "ranks_from_fn"]
