@@ -1,0 +1,69 @@
+"""Compile the HIP library libtlrgemm.so in-tree for gfx950.
+
+Usage: python -m hpc_linear_algebra_amd.build   (or call build()).
+Every source is compiled with hipcc; device code is built for gfx950 only and
+with packed-fp32 instructions disabled (the compiler would otherwise form
+v_pk_* fp32 arithmetic from ordinary float code).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libtlrgemm.so")
+SOURCES = ["planner.cpp", "abi.cpp", "executor.cpp", "gemm.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    return cand
+
+
+def _flags():
+    return ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [hipcc()] + ["-x", "hip"] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtlrgemm.so next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,989 @@
+// Host planner of the TLR GEMM: operand views, association order, rectangles
+// under a workspace budget, and the descriptor tables of every launch.
+//
+// The method follows "Tile-Low-Rank GEMM: Designing Storage Around the
+// Contraction" (sections "One product, three stages", "Where fusion stops",
+// "Association order and workspace") with the dense-diagonal and boundary
+// handling of "TLR Matrix Multiplication" ("Regular TLR GEMM", boundary
+// decomposition, "Output traversal and workspace budget").  No HIP calls here.
+//
+// Per output rectangle (I, J) the right order U (S Z^T) runs
+//   launch 1: S_k = V_{I,k}^T W_{k,J} for every contraction tile k (coupling,
+//             one GEMM per k with i fused into M and j into N), and the
+//             diagonal-term products X_i = D_A,ii W_{i,J};
+//   launch 2: for every (k, j): the right product S_ikj Z_kj^T for all i in I at
+//             once (or V_ij^T D_B,jj when k = j is a dense diagonal tile),
+//             written through an indirect column map straight into row block k
+//             of every terminal matrix T_i (stored transposed, W_J x rho_i);
+//   launch 3: for every output tile (i, j): C_ij = alpha (U_i T_i[:, j] + X_ij Z_ij^T
+//             or D_A,ii D_B,ii) + beta C_ij, so the whole sum over k is the GEMM
+//             reduction and C is read and written once.
+// The left order (U S) Z^T mirrors it with terminal matrices Y_j (W_I x gamma_j)
+// and the diagonal-term products X'_j = V_{I,j}^T D_B,jj.
+#include <algorithm>
+#include <cstring>
+#include <limits>
+#include <numeric>
+
+#include "tlr_plan.h"
+
+namespace tlr {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static void split_dim(int64_t n, int64_t b, std::vector<int64_t> &s, std::vector<int64_t> &o) {
+  s.clear();
+  o.clear();
+  if (n <= 0) return;
+  int64_t q = ceil_div(n, b);
+  for (int64_t t = 0; t < q; ++t) {
+    o.push_back(t * b);
+    s.push_back(std::min<int64_t>(b, n - t * b));
+  }
+}
+
+// Validate a stored operand and build the view of op(X).  Factor offsets follow
+// the packing rules: outer by tile row, inner by tile column, r_ij columns each.
+static tlr_status make_view(const tlr_shape *X, int op, uint8_t outer_id, uint8_t inner_id,
+                            uint8_t diag_id, const char *name, View *v) {
+  if (!X) return fail(TLR_ERR_INVALID_ARG, std::string(name) + ": null shape");
+  if (X->rows < 0 || X->cols < 0 || X->b < 1)
+    return fail(TLR_ERR_INVALID_ARG, std::string(name) + ": bad rows/cols/b");
+  if (X->has_diag && X->rows != X->cols)
+    return fail(TLR_ERR_INVALID_ARG, std::string(name) + ": a dense diagonal needs a square matrix");
+  if ((int64_t)X->b > (int64_t)std::numeric_limits<int32_t>::max() / 2)
+    return fail(TLR_ERR_INVALID_ARG, std::string(name) + ": tile size too large");
+  std::vector<int64_t> srs, sro, scs, sco;
+  split_dim(X->rows, X->b, srs, sro);
+  split_dim(X->cols, X->b, scs, sco);
+  const int qr = (int)srs.size(), qc = (int)scs.size();
+  if ((int64_t)qr * qc > 0 && !X->ranks) return fail(TLR_ERR_INVALID_ARG, std::string(name) + ": null ranks");
+  std::vector<int32_t> R((size_t)qr * qc);
+  for (int j = 0; j < qc; ++j)
+    for (int i = 0; i < qr; ++i) {
+      int32_t r = X->ranks[(size_t)i + (size_t)j * qr];
+      if (r < 0 || r > std::min(srs[i], scs[j]))
+        return fail(TLR_ERR_RANK, std::string(name) + ": rank out of range at tile (" +
+                                      std::to_string(i) + "," + std::to_string(j) + ")");
+      if (X->has_diag && i == j && r != 0)
+        return fail(TLR_ERR_RANK, std::string(name) + ": diagonal tile rank must be 0 with a dense diagonal");
+      R[(size_t)i + (size_t)j * qr] = r;
+    }
+  // stored offsets
+  std::vector<int64_t> so((size_t)qr * qc), si((size_t)qr * qc);
+  int64_t acc = 0;
+  for (int i = 0; i < qr; ++i)
+    for (int j = 0; j < qc; ++j) {
+      so[(size_t)i + (size_t)j * qr] = acc;
+      acc += R[(size_t)i + (size_t)j * qr];
+    }
+  acc = 0;
+  for (int j = 0; j < qc; ++j)
+    for (int i = 0; i < qr; ++i) {
+      si[(size_t)i + (size_t)j * qr] = acc;
+      acc += R[(size_t)i + (size_t)j * qr];
+    }
+  v->b = X->b;
+  v->diag = X->has_diag != 0;
+  v->diag_base = diag_id;
+  if (op == TLR_OP_N) {
+    v->qr = qr; v->qc = qc;
+    v->rs = srs; v->ro = sro; v->cs = scs; v->co = sco;
+    v->R = R; v->ocol = so; v->icol = si;
+    v->outer_base = outer_id; v->inner_base = inner_id;
+    v->diag_trans = false;
+  } else {
+    // tile (i,j) of X^T is V_ji U_ji^T: the inner family becomes the outer one
+    v->qr = qc; v->qc = qr;
+    v->rs = scs; v->ro = sco; v->cs = srs; v->co = sro;
+    v->R.assign((size_t)qc * qr, 0);
+    v->ocol.assign((size_t)qc * qr, 0);
+    v->icol.assign((size_t)qc * qr, 0);
+    for (int i = 0; i < qc; ++i)
+      for (int j = 0; j < qr; ++j) {
+        size_t d = (size_t)i + (size_t)j * qc, s = (size_t)j + (size_t)i * qr;
+        v->R[d] = R[s];
+        v->ocol[d] = si[s];
+        v->icol[d] = so[s];
+      }
+    v->outer_base = inner_id; v->inner_base = outer_id;
+    v->diag_trans = true;
+  }
+  return TLR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Rank prefix sums used by the accounting.
+struct Sums {
+  int qm = 0, qk = 0, qn = 0;
+  std::vector<int64_t> cumA;   // cumA[k*(qm+1) + i] = sum_{i'<i} RA(i',k)
+  std::vector<int64_t> cumB;   // cumB[k*(qn+1) + j] = sum_{j'<j} RB(k,j')
+  std::vector<int64_t> rho, gam;
+  int64_t kap(int k, int i0, int i1) const { return cumA[(size_t)k * (qm + 1) + i1] - cumA[(size_t)k * (qm + 1) + i0]; }
+  int64_t bet(int k, int j0, int j1) const { return cumB[(size_t)k * (qn + 1) + j1] - cumB[(size_t)k * (qn + 1) + j0]; }
+};
+
+static void build_sums(const Plan &p, Sums &s) {
+  s.qm = p.A.qr;
+  s.qk = p.A.qc;
+  s.qn = (int)p.ns.size();
+  s.cumA.assign((size_t)s.qk * (s.qm + 1), 0);
+  for (int k = 0; k < s.qk; ++k)
+    for (int i = 0; i < s.qm; ++i)
+      s.cumA[(size_t)k * (s.qm + 1) + i + 1] = s.cumA[(size_t)k * (s.qm + 1) + i] + p.A.r(i, k);
+  s.rho.assign(s.qm, 0);
+  for (int i = 0; i < s.qm; ++i)
+    for (int k = 0; k < s.qk; ++k) s.rho[i] += p.A.r(i, k);
+  if (!p.dense_b) {
+    s.cumB.assign((size_t)s.qk * (s.qn + 1), 0);
+    for (int k = 0; k < s.qk; ++k)
+      for (int j = 0; j < s.qn; ++j)
+        s.cumB[(size_t)k * (s.qn + 1) + j + 1] = s.cumB[(size_t)k * (s.qn + 1) + j] + p.B.r(k, j);
+    s.gam.assign(s.qn, 0);
+    for (int j = 0; j < s.qn; ++j)
+      for (int k = 0; k < s.qk; ++k) s.gam[j] += p.B.r(k, j);
+  }
+}
+
+static int64_t width(const Plan &p, int j0, int j1) {
+  return j1 > j0 ? p.no[j1 - 1] + p.ns[j1 - 1] - p.no[j0] : 0;
+}
+static int64_t height(const Plan &p, int i0, int i1) {
+  return i1 > i0 ? p.A.ro[i1 - 1] + p.A.rs[i1 - 1] - p.A.ro[i0] : 0;
+}
+
+// Exact workspace bytes of one rectangle in one order (every buffer 256-B aligned).
+static size_t rect_ws(const Plan &p, const Sums &s, int i0, int i1, int j0, int j1, int order) {
+  const size_t es = p.es;
+  size_t tot = 0;
+  const int64_t WJ = width(p, j0, j1), WI = height(p, i0, i1);
+  if (p.dense_b) {
+    for (int i = i0; i < i1; ++i)
+      if (s.rho[i] > 0) tot += align_up((size_t)WJ * s.rho[i] * es, WS_ALIGN);
+    return tot;
+  }
+  for (int k = 0; k < s.qk; ++k) {
+    int64_t M = s.kap(k, i0, i1), N = s.bet(k, j0, j1);
+    if (M > 0 && N > 0) tot += align_up((size_t)M * N * es, WS_ALIGN);
+  }
+  if (order == TLR_ORDER_RIGHT) {
+    for (int i = i0; i < i1; ++i) {
+      if (s.rho[i] > 0) tot += align_up((size_t)WJ * s.rho[i] * es, WS_ALIGN);
+      if (p.A.diag) {
+        int64_t bi = s.bet(i, j0, j1);
+        if (bi > 0) tot += align_up((size_t)p.A.rs[i] * bi * es, WS_ALIGN);
+      }
+    }
+  } else {
+    for (int j = j0; j < j1; ++j) {
+      if (s.gam[j] > 0) tot += align_up((size_t)WI * s.gam[j] * es, WS_ALIGN);
+      if (p.B.diag) {
+        int64_t kj = s.kap(j, i0, i1);
+        if (kj > 0) tot += align_up((size_t)kj * p.ns[j] * es, WS_ALIGN);
+      }
+    }
+  }
+  return tot;
+}
+
+// Useful flops of one rectangle in one order (terms with a zero rank count 0).
+static double rect_useful(const Plan &p, const Sums &s, int i0, int i1, int j0, int j1, int order) {
+  const View &A = p.A;
+  double F = 0;
+  const double WJ = (double)width(p, j0, j1);
+  if (p.dense_b) {
+    for (int k = 0; k < s.qk; ++k) F += 2.0 * WJ * A.cs[k] * s.kap(k, i0, i1);
+    for (int i = i0; i < i1; ++i) {
+      F += 2.0 * A.rs[i] * WJ * s.rho[i];
+      if (A.diag) F += 2.0 * A.rs[i] * (double)A.rs[i] * WJ;
+    }
+    return F;
+  }
+  const View &B = p.B;
+  for (int k = 0; k < s.qk; ++k) F += 2.0 * s.kap(k, i0, i1) * s.bet(k, j0, j1) * A.cs[k];
+  if (order == TLR_ORDER_RIGHT) {
+    if (A.diag)
+      for (int i = i0; i < i1; ++i) F += 2.0 * A.rs[i] * (double)A.rs[i] * s.bet(i, j0, j1);
+    for (int k = 0; k < s.qk; ++k)
+      for (int j = j0; j < j1; ++j) {
+        if (B.diag && k == j) F += 2.0 * p.ns[j] * (double)p.ns[j] * s.kap(j, i0, i1);
+        else F += 2.0 * p.ns[j] * (double)s.kap(k, i0, i1) * B.r(k, j);
+      }
+    for (int i = i0; i < i1; ++i)
+      for (int j = j0; j < j1; ++j) {
+        int64_t kk = 0;
+        for (int k = 0; k < s.qk; ++k)
+          if (B.r(k, j) > 0 || (B.diag && k == j)) kk += A.r(i, k);
+        F += 2.0 * A.rs[i] * (double)p.ns[j] * kk;
+        if (A.diag) {
+          if (B.diag && i == j) F += 2.0 * A.rs[i] * (double)A.rs[i] * A.rs[i];
+          else F += 2.0 * A.rs[i] * (double)p.ns[j] * B.r(i, j);
+        }
+      }
+  } else {
+    if (B.diag)
+      for (int j = j0; j < j1; ++j) F += 2.0 * s.kap(j, i0, i1) * (double)p.ns[j] * p.ns[j];
+    for (int i = i0; i < i1; ++i)
+      for (int k = 0; k < s.qk; ++k) {
+        if (A.diag && k == i) F += 2.0 * A.rs[i] * (double)A.rs[i] * s.bet(i, j0, j1);
+        else F += 2.0 * A.rs[i] * (double)s.bet(k, j0, j1) * A.r(i, k);
+      }
+    for (int i = i0; i < i1; ++i)
+      for (int j = j0; j < j1; ++j) {
+        int64_t kk = 0;
+        for (int k = 0; k < s.qk; ++k)
+          if (A.r(i, k) > 0 || (A.diag && k == i)) kk += B.r(k, j);
+        F += 2.0 * A.rs[i] * (double)p.ns[j] * kk;
+        if (B.diag) {
+          if (A.diag && i == j) F += 2.0 * A.rs[i] * (double)A.rs[i] * A.rs[i];
+          else F += 2.0 * A.rs[i] * (double)p.ns[j] * A.r(i, j);
+        }
+      }
+  }
+  return F;
+}
+
+static bool order_allowed(const Plan &p, int order) {
+  if (p.dense_b) return order == TLR_ORDER_RIGHT;
+  if (p.flags & TLR_PLAN_FORCE_RIGHT) return order == TLR_ORDER_RIGHT;
+  if (p.flags & TLR_PLAN_FORCE_LEFT) return order == TLR_ORDER_LEFT;
+  return true;
+}
+
+static size_t min_ws(const Plan &p, const Sums &s, int i0, int i1, int j0, int j1) {
+  size_t best = std::numeric_limits<size_t>::max();
+  for (int o = 0; o < 2; ++o)
+    if (order_allowed(p, o)) best = std::min(best, rect_ws(p, s, i0, i1, j0, j1, o));
+  return best;
+}
+
+struct Region { int i0, i1, j0, j1; };
+
+// Widest feasible block of tile columns, then the longest runs of tile rows
+// that fit, then the cheaper feasible order of each rectangle.
+static tlr_status schedule_region(const Plan &p, const Sums &s, const Region &g, size_t budget,
+                                  int group, std::vector<Rect> &out) {
+  auto fits = [&](int i0, int i1, int j0, int j1) { return min_ws(p, s, i0, i1, j0, j1) <= budget; };
+  int jc = g.j0;
+  while (jc < g.j1) {
+    auto J_ok = [&](int je) {
+      for (int i = g.i0; i < g.i1; ++i)
+        if (!fits(i, i + 1, jc, je)) return false;
+      return true;
+    };
+    if (!J_ok(jc + 1))
+      return fail(TLR_ERR_WORKSPACE, "workspace budget " + std::to_string(budget) +
+                                         " B is below what one output tile needs");
+    int je = jc + 1;
+    while (je < g.j1 && J_ok(je + 1)) ++je;
+    int ic = g.i0;
+    while (ic < g.i1) {
+      int ie = ic + 1;
+      while (ie < g.i1 && fits(ic, ie + 1, jc, je)) ++ie;
+      Rect r{ic, ie, jc, je, -1, group, 0, 0};
+      double bestF = 0;
+      for (int o = 0; o < 2; ++o) {
+        if (!order_allowed(p, o)) continue;
+        size_t w = rect_ws(p, s, ic, ie, jc, je, o);
+        if (w > budget) continue;
+        double F = rect_useful(p, s, ic, ie, jc, je, o);
+        if (r.order < 0 || F < bestF) { r.order = o; bestF = F; r.ws_bytes = w; }
+      }
+      r.useful_flops = bestF;
+      out.push_back(r);
+      ic = ie;
+    }
+    jc = je;
+  }
+  return TLR_OK;
+}
+
+// Split C into disjoint regions (interior, boundary column, boundary row,
+// corner) when the last tile row / column is a remainder, so they can run on
+// separate streams ("TLR Matrix Multiplication", four output regions).
+static std::vector<Region> make_regions(const Plan &p, bool split) {
+  const int qm = p.A.qr, qn = (int)p.ns.size();
+  std::vector<Region> regs;
+  if (qm == 0 || qn == 0) return regs;
+  const bool rrem = split && qm > 1 && p.A.rs.back() < p.A.b;
+  const bool crem = split && qn > 1 && p.ns.back() < p.A.b;
+  const int mi = rrem ? qm - 1 : qm, mj = crem ? qn - 1 : qn;
+  regs.push_back({0, mi, 0, mj});
+  if (crem) regs.push_back({0, mi, mj, qn});
+  if (rrem) regs.push_back({mi, qm, 0, mj});
+  if (rrem && crem) regs.push_back({mi, qm, mj, qn});
+  return regs;
+}
+
+static tlr_status schedule(Plan &p, const Sums &s) {
+  const size_t budget = p.budget ? p.budget : std::numeric_limits<size_t>::max();
+  p.rects.clear();
+  p.groups.clear();
+  const bool concurrent = p.n_streams >= 2 && !(p.flags & TLR_PLAN_NO_REGIONS);
+  std::vector<Region> regs = make_regions(p, concurrent);
+  if (regs.empty()) return TLR_OK;
+  if (regs.size() > 1) {
+    // boundary regions get what one run each needs, capped at a quarter of the budget
+    std::vector<size_t> need(regs.size(), 0);
+    size_t bsum = 0;
+    for (size_t g = 1; g < regs.size(); ++g) {
+      need[g] = align_up(min_ws(p, s, regs[g].i0, regs[g].i1, regs[g].j0, regs[g].j1), WS_ALIGN);
+      bsum += need[g];
+    }
+    bool ok = true;
+    std::vector<size_t> share(regs.size(), 0);
+    if (budget == std::numeric_limits<size_t>::max()) {
+      for (size_t g = 1; g < regs.size(); ++g) share[g] = need[g];
+      share[0] = budget;
+    } else {
+      size_t cap = budget / 4;
+      size_t used = 0;
+      for (size_t g = 1; g < regs.size(); ++g) {
+        share[g] = bsum <= cap ? need[g]
+                               : (size_t)((double)cap * (double)need[g] / (double)bsum) / WS_ALIGN * WS_ALIGN;
+        used += share[g];
+      }
+      share[0] = budget > used ? budget - used : 0;
+    }
+    std::vector<Rect> rects;
+    for (size_t g = 0; g < regs.size() && ok; ++g) {
+      std::vector<Rect> rr;
+      tlr_status st = schedule_region(p, s, regs[g], share[g], (int)g, rr);
+      if (st != TLR_OK) { ok = false; break; }
+      rects.insert(rects.end(), rr.begin(), rr.end());
+    }
+    if (ok) {
+      p.rects = rects;
+      size_t off = 0;
+      for (size_t g = 0; g < regs.size(); ++g) {
+        Group G;
+        G.stream = (int)(g % (size_t)p.n_streams);
+        G.arena_off = off;
+        size_t mx = 0;
+        for (size_t r = 0; r < p.rects.size(); ++r)
+          if (p.rects[r].group == (int)g) { G.rects.push_back((int)r); mx = std::max(mx, p.rects[r].ws_bytes); }
+        G.arena_bytes = align_up(mx, WS_ALIGN);
+        off += G.arena_bytes;
+        p.groups.push_back(G);
+      }
+      p.ws_bytes = off;
+      set_error("");
+      return TLR_OK;
+    }
+    regs = make_regions(p, false);   // fall back to one sequential region
+  }
+  std::vector<Rect> rr;
+  tlr_status st = schedule_region(p, s, regs[0], budget, 0, rr);
+  if (st != TLR_OK) return st;
+  p.rects = rr;
+  Group G;
+  G.stream = 0;
+  G.arena_off = 0;
+  size_t mx = 0;
+  for (size_t r = 0; r < p.rects.size(); ++r) { G.rects.push_back((int)r); mx = std::max(mx, p.rects[r].ws_bytes); }
+  G.arena_bytes = align_up(mx, WS_ALIGN);
+  p.groups.push_back(G);
+  p.ws_bytes = G.arena_bytes;
+  return TLR_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Descriptor generation.
+
+static DevOperand opnd(uint8_t base, int64_t off, int64_t ld, int trans) {
+  DevOperand o;
+  o.off = off;
+  o.ld = (int32_t)ld;
+  o.base = base;
+  o.trans = (uint8_t)trans;
+  o.pad = 0;
+  return o;
+}
+
+struct TaskList {
+  std::vector<DevTask> t;
+  std::vector<double> useful;  // per task
+};
+
+static DevTask new_task(int64_t M, int64_t N, uint8_t cbase, int64_t c_off, int64_t ldc,
+                        int64_t ctab, bool final_) {
+  DevTask d;
+  std::memset(&d, 0, sizeof(d));
+  d.M = (int32_t)M;
+  d.N = (int32_t)N;
+  d.c_off = c_off;
+  d.ctab = ctab;
+  d.ldc = (int32_t)ldc;
+  d.c_base = cbase;
+  d.final_ = final_ ? 1 : 0;
+  d.nseg = 0;
+  return d;
+}
+
+static void add_seg(DevTask &d, DevOperand a, DevOperand b, int64_t K) {
+  if (K <= 0) return;
+  DevSeg &s = d.seg[d.nseg++];
+  s.a = a;
+  s.b = b;
+  s.K = (int32_t)K;
+  s.pad = 0;
+}
+
+static double task_exec_flops(const DevTask &d) {
+  double F = 0;
+  for (int s = 0; s < d.nseg; ++s) F += 2.0 * d.M * (double)d.N * d.seg[s].K;
+  return F;
+}
+
+// Emit the workgroup table of one launch.  Stage 3 keeps neighbouring output
+// blocks on one XCD (each XCD walks a contiguous eighth of the block list, so
+// the panels they share stay in that XCD's L2), longest tasks first inside each
+// eighth; stages 1-2 are ordered longest first across the whole launch.
+static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
+  if (tl.t.empty()) return;
+  Launch L;
+  L.stage = stage;
+  L.group = group;
+  L.rect = rect;
+  L.n_tasks = (int64_t)tl.t.size();
+  L.useful_flops = 0;
+  L.executed_flops = 0;
+  const int32_t task0 = (int32_t)p.tasks.size();
+  struct Ent { int32_t task, m0, n0; int64_t cost; };
+  std::vector<Ent> ents;
+  for (size_t t = 0; t < tl.t.size(); ++t) {
+    const DevTask &d = tl.t[t];
+    L.useful_flops += tl.useful[t];
+    L.executed_flops += task_exec_flops(d);
+    int64_t K = 0;
+    for (int s = 0; s < d.nseg; ++s) K += d.seg[s].K;
+    for (int64_t n0 = 0; n0 < d.N; n0 += BN)
+      for (int64_t m0 = 0; m0 < d.M; m0 += BM)
+        ents.push_back({task0 + (int32_t)t, (int32_t)m0, (int32_t)n0, K + 32});
+    p.tasks.push_back(d);
+  }
+  const int64_t n = (int64_t)ents.size();
+  const int64_t per = ceil_div(n, NUM_XCD);
+  const int64_t padded = per * NUM_XCD;
+  std::vector<DevTile> tab((size_t)padded);
+  for (auto &x : tab) { x.task = -1; x.m0 = 0; x.n0 = 0; x.pad = 0; }
+  auto by_cost = [](const Ent &a, const Ent &b) { return a.cost > b.cost; };
+  if (stage == 3) {
+    for (int x = 0; x < NUM_XCD; ++x) {
+      int64_t lo = std::min(n, x * per), hi = std::min(n, (x + 1) * per);
+      std::stable_sort(ents.begin() + lo, ents.begin() + hi, by_cost);
+      for (int64_t t = lo; t < hi; ++t) {
+        int64_t bid = (t - lo) * NUM_XCD + x;
+        tab[(size_t)bid] = DevTile{ents[t].task, ents[t].m0, ents[t].n0, 0};
+      }
+    }
+  } else {
+    std::stable_sort(ents.begin(), ents.end(), by_cost);
+    for (int64_t t = 0; t < n; ++t) tab[(size_t)t] = DevTile{ents[t].task, ents[t].m0, ents[t].n0, 0};
+  }
+  L.tile_off = (int64_t)p.tiles.size();
+  L.n_tiles = padded;
+  p.tiles.insert(p.tiles.end(), tab.begin(), tab.end());
+  p.launches.push_back(L);
+  p.groups[group].launches.push_back((int)p.launches.size() - 1);
+}
+
+static void emit_rect(Plan &p, const Sums &s, int rect) {
+  const Rect &R = p.rects[rect];
+  const View &A = p.A;
+  const View &B = p.B;
+  const int64_t es = p.es;
+  const int64_t b = A.b;
+  const int i0 = R.i0, i1 = R.i1, j0 = R.j0, j1 = R.j1;
+  const int64_t WJ = width(p, j0, j1), WI = height(p, i0, i1);
+  const size_t arena = p.groups[R.group].arena_off;
+  size_t cur = arena;
+  auto take = [&](size_t bytes) {
+    int64_t off = (int64_t)(cur / (size_t)es);
+    cur += align_up(bytes, WS_ALIGN);
+    return off;
+  };
+  const int qk = s.qk;
+  // column offset of tile j inside the J block / row offset of tile i inside I
+  auto cJ = [&](int j) { return p.no[j] - p.no[j0]; };
+  auto rI = [&](int i) { return A.ro[i] - A.ro[i0]; };
+
+  if (p.dense_b) {
+    std::vector<int64_t> Toff(s.qm, -1);
+    for (int i = i0; i < i1; ++i)
+      if (s.rho[i] > 0) Toff[i] = take((size_t)WJ * s.rho[i] * es);
+    // launch 1: T_i^T[n, p_i(k)+a] = sum_kk op(B)[k rows, J cols]^T V_ik
+    TaskList l1;
+    const int64_t c0 = p.no[j0];
+    for (int k = 0; k < qk; ++k) {
+      int64_t kap = s.kap(k, i0, i1);
+      if (kap == 0) continue;
+      int64_t ctab = (int64_t)p.coltab.size();
+      for (int i = i0; i < i1; ++i) {
+        int64_t pik = 0;
+        for (int kk = 0; kk < k; ++kk) pik += A.r(i, kk);
+        for (int a = 0; a < A.r(i, k); ++a) p.coltab.push_back(Toff[i] + (pik + a) * WJ);
+      }
+      DevTask d = new_task(WJ, kap, BASE_WS, 0, 0, ctab, false);
+      DevOperand ao = p.opB == TLR_OP_N ? opnd(BASE_B_DENSE, A.co[k] + c0 * p.ldb, p.ldb, 1)
+                                        : opnd(BASE_B_DENSE, c0 + A.co[k] * p.ldb, p.ldb, 0);
+      add_seg(d, ao, opnd(A.inner_base, A.ic(i0, k) * b, b, 0), A.cs[k]);
+      l1.t.push_back(d);
+      l1.useful.push_back(2.0 * WJ * A.cs[k] * kap);
+    }
+    emit_launch(p, 1, R.group, rect, l1);
+    TaskList l3;
+    for (int i = i0; i < i1; ++i)
+      for (int j = j0; j < j1; ++j) {
+        DevTask d = new_task(A.rs[i], p.ns[j], BASE_C, A.ro[i] + p.no[j] * p.ldc, p.ldc, -1, true);
+        double u = 0;
+        if (s.rho[i] > 0) {
+          add_seg(d, opnd(A.outer_base, A.oc(i, 0) * b, b, 0), opnd(BASE_WS, Toff[i] + cJ(j), WJ, 1), s.rho[i]);
+          u += 2.0 * A.rs[i] * (double)p.ns[j] * s.rho[i];
+        }
+        if (A.diag) {
+          DevOperand bo = p.opB == TLR_OP_N ? opnd(BASE_B_DENSE, A.ro[i] + p.no[j] * p.ldb, p.ldb, 0)
+                                            : opnd(BASE_B_DENSE, p.no[j] + A.ro[i] * p.ldb, p.ldb, 1);
+          add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans), bo, A.rs[i]);
+          u += 2.0 * A.rs[i] * (double)A.rs[i] * p.ns[j];
+        }
+        l3.t.push_back(d);
+        l3.useful.push_back(u);
+      }
+    emit_launch(p, 3, R.group, rect, l3);
+    return;
+  }
+
+  // coupling blocks S_k (kap_k(I) x bet_k(J), column-major)
+  std::vector<int64_t> Soff(qk, -1), SM(qk, 0), SN(qk, 0);
+  for (int k = 0; k < qk; ++k) {
+    SM[k] = s.kap(k, i0, i1);
+    SN[k] = s.bet(k, j0, j1);
+    if (SM[k] > 0 && SN[k] > 0) Soff[k] = take((size_t)SM[k] * SN[k] * es);
+  }
+  TaskList l1, l2, l3;
+  for (int k = 0; k < qk; ++k) {
+    if (Soff[k] < 0) continue;
+    DevTask d = new_task(SM[k], SN[k], BASE_WS, Soff[k], SM[k], -1, false);
+    add_seg(d, opnd(A.inner_base, A.ic(i0, k) * b, b, 1), opnd(B.outer_base, B.oc(k, j0) * b, b, 0), A.cs[k]);
+    l1.t.push_back(d);
+    l1.useful.push_back(2.0 * SM[k] * (double)SN[k] * A.cs[k]);
+  }
+
+  if (R.order == TLR_ORDER_RIGHT) {
+    std::vector<int64_t> Toff(s.qm, -1), Xoff(s.qm, -1);
+    for (int i = i0; i < i1; ++i) {
+      if (s.rho[i] > 0) Toff[i] = take((size_t)WJ * s.rho[i] * es);
+      if (A.diag && s.bet(i, j0, j1) > 0) Xoff[i] = take((size_t)A.rs[i] * s.bet(i, j0, j1) * es);
+    }
+    // X_i = op(D_A,ii) W_{i,J}
+    if (A.diag)
+      for (int i = i0; i < i1; ++i) {
+        int64_t bi = s.bet(i, j0, j1);
+        if (bi == 0) continue;
+        DevTask d = new_task(A.rs[i], bi, BASE_WS, Xoff[i], A.rs[i], -1, false);
+        add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans), opnd(B.outer_base, B.oc(i, j0) * b, b, 0), A.rs[i]);
+        l1.t.push_back(d);
+        l1.useful.push_back(2.0 * A.rs[i] * (double)A.rs[i] * bi);
+      }
+    // column maps: coupling row (i, a) of contraction tile k -> column p_i(k)+a of T_i^T
+    std::vector<int64_t> ctab(qk, -1);
+    for (int k = 0; k < qk; ++k) {
+      if (SM[k] == 0) continue;
+      ctab[k] = (int64_t)p.coltab.size();
+      for (int i = i0; i < i1; ++i) {
+        int64_t pik = 0;
+        for (int kk = 0; kk < k; ++kk) pik += A.r(i, kk);
+        for (int a = 0; a < A.r(i, k); ++a) p.coltab.push_back(Toff[i] + (pik + a) * WJ);
+      }
+    }
+    for (int k = 0; k < qk; ++k) {
+      if (SM[k] == 0) continue;
+      int64_t boff = 0;   // column offset of block j inside S_k
+      for (int j = j0; j < j1; ++j) {
+        DevTask d = new_task(p.ns[j], SM[k], BASE_WS, cJ(j), 0, ctab[k], false);
+        double u = 0;
+        if (B.diag && k == j) {
+          // T_i[j-block rows, j-block cols] = V_ij^T D_B,jj, stored transposed: D^T V
+          add_seg(d, opnd(B.diag_base, (int64_t)j * b * b, b, B.diag_trans ? 0 : 1),
+                  opnd(A.inner_base, A.ic(i0, j) * b, b, 0), p.ns[j]);
+          u = 2.0 * p.ns[j] * (double)p.ns[j] * SM[k];
+        } else {
+          int32_t r = B.r(k, j);
+          if (r > 0)
+            add_seg(d, opnd(B.inner_base, B.ic(k, j) * b, b, 0), opnd(BASE_WS, Soff[k] + boff * SM[k], SM[k], 1), r);
+          u = 2.0 * p.ns[j] * (double)SM[k] * r;   // r == 0 writes a zero block
+          boff += r;
+        }
+        l2.t.push_back(d);
+        l2.useful.push_back(u);
+      }
+    }
+    for (int i = i0; i < i1; ++i) {
+      for (int j = j0; j < j1; ++j) {
+        DevTask d = new_task(A.rs[i], p.ns[j], BASE_C, A.ro[i] + p.no[j] * p.ldc, p.ldc, -1, true);
+        int64_t kk = 0;
+        for (int k = 0; k < qk; ++k)
+          if (B.r(k, j) > 0 || (B.diag && k == j)) kk += A.r(i, k);
+        double u = 2.0 * A.rs[i] * (double)p.ns[j] * kk;
+        if (s.rho[i] > 0)
+          add_seg(d, opnd(A.outer_base, A.oc(i, 0) * b, b, 0), opnd(BASE_WS, Toff[i] + cJ(j), WJ, 1), s.rho[i]);
+        if (A.diag) {
+          if (B.diag && i == j) {
+            add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans),
+                    opnd(B.diag_base, (int64_t)i * b * b, b, B.diag_trans), A.rs[i]);
+            u += 2.0 * A.rs[i] * (double)A.rs[i] * A.rs[i];
+          } else if (B.r(i, j) > 0) {
+            int64_t xo = s.bet(i, j0, j);
+            add_seg(d, opnd(BASE_WS, Xoff[i] + xo * A.rs[i], A.rs[i], 0),
+                    opnd(B.inner_base, B.ic(i, j) * b, b, 1), B.r(i, j));
+            u += 2.0 * A.rs[i] * (double)p.ns[j] * B.r(i, j);
+          }
+        }
+        l3.t.push_back(d);
+        l3.useful.push_back(u);
+      }
+    }
+  } else {
+    std::vector<int64_t> Yoff(s.qn, -1), Xoff(s.qn, -1);
+    for (int j = j0; j < j1; ++j) {
+      if (s.gam[j] > 0) Yoff[j] = take((size_t)WI * s.gam[j] * es);
+      if (B.diag && s.kap(j, i0, i1) > 0) Xoff[j] = take((size_t)s.kap(j, i0, i1) * p.ns[j] * es);
+    }
+    // X'_j = V_{I,j}^T op(D_B,jj)
+    if (B.diag)
+      for (int j = j0; j < j1; ++j) {
+        int64_t kj = s.kap(j, i0, i1);
+        if (kj == 0) continue;
+        DevTask d = new_task(kj, p.ns[j], BASE_WS, Xoff[j], kj, -1, false);
+        add_seg(d, opnd(A.inner_base, A.ic(i0, j) * b, b, 1), opnd(B.diag_base, (int64_t)j * b * b, b, B.diag_trans), p.ns[j]);
+        l1.t.push_back(d);
+        l1.useful.push_back(2.0 * kj * (double)p.ns[j] * p.ns[j]);
+      }
+    // column maps: coupling column (j, a) of contraction tile k -> column p'_j(k)+a of Y_j
+    std::vector<int64_t> ytab(qk, -1);
+    for (int k = 0; k < qk; ++k) {
+      if (SN[k] == 0) continue;
+      ytab[k] = (int64_t)p.coltab.size();
+      for (int j = j0; j < j1; ++j) {
+        int64_t pkj = 0;
+        for (int kk = 0; kk < k; ++kk) pkj += B.r(kk, j);
+        for (int a = 0; a < B.r(k, j); ++a) p.coltab.push_back(Yoff[j] + (pkj + a) * WI);
+      }
+    }
+    for (int i = i0; i < i1; ++i) {
+      for (int k = 0; k < qk; ++k) {
+        if (SN[k] == 0) continue;
+        DevTask d = new_task(A.rs[i], SN[k], BASE_WS, rI(i), 0, ytab[k], false);
+        double u = 0;
+        if (A.diag && k == i) {
+          add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans), opnd(B.outer_base, B.oc(i, j0) * b, b, 0), A.rs[i]);
+          u = 2.0 * A.rs[i] * (double)A.rs[i] * SN[k];
+        } else {
+          int32_t r = A.r(i, k);
+          if (r > 0) {
+            int64_t ao = s.kap(k, i0, i);
+            add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), opnd(BASE_WS, Soff[k] + ao, SM[k], 0), r);
+          }
+          u = 2.0 * A.rs[i] * (double)SN[k] * r;
+        }
+        l2.t.push_back(d);
+        l2.useful.push_back(u);
+      }
+    }
+    for (int j = j0; j < j1; ++j) {
+      for (int i = i0; i < i1; ++i) {
+        DevTask d = new_task(A.rs[i], p.ns[j], BASE_C, A.ro[i] + p.no[j] * p.ldc, p.ldc, -1, true);
+        int64_t kk = 0;
+        for (int k = 0; k < qk; ++k)
+          if (A.r(i, k) > 0 || (A.diag && k == i)) kk += B.r(k, j);
+        double u = 2.0 * A.rs[i] * (double)p.ns[j] * kk;
+        if (s.gam[j] > 0)
+          add_seg(d, opnd(BASE_WS, Yoff[j] + rI(i), WI, 0), opnd(B.inner_base, B.ic(0, j) * b, b, 1), s.gam[j]);
+        if (B.diag) {
+          if (A.diag && i == j) {
+            add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans),
+                    opnd(B.diag_base, (int64_t)i * b * b, b, B.diag_trans), A.rs[i]);
+            u += 2.0 * A.rs[i] * (double)A.rs[i] * A.rs[i];
+          } else if (A.r(i, j) > 0) {
+            int64_t ao = s.kap(j, i0, i);
+            add_seg(d, opnd(A.outer_base, A.oc(i, j) * b, b, 0), opnd(BASE_WS, Xoff[j] + ao, s.kap(j, i0, i1), 0), A.r(i, j));
+            u += 2.0 * A.rs[i] * (double)p.ns[j] * A.r(i, j);
+          }
+        }
+        l3.t.push_back(d);
+        l3.useful.push_back(u);
+      }
+    }
+  }
+  emit_launch(p, 1, R.group, rect, l1);
+  emit_launch(p, 2, R.group, rect, l2);
+  emit_launch(p, 3, R.group, rect, l3);
+}
+
+static double compressed_elems(const View &v) {
+  double e = 0;
+  for (int i = 0; i < v.qr; ++i)
+    for (int j = 0; j < v.qc; ++j) {
+      if (v.diag && i == j) e += (double)v.rs[i] * v.rs[i];
+      else e += (double)v.r(i, j) * (v.rs[i] + v.cs[j]);
+    }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// Descriptor self-check.  Always: every element a task's operands or output can
+// touch lies inside its buffer, and every workgroup table covers each block of
+// each task exactly once.  With TLR_PLAN_VALIDATE also: writes inside one launch
+// never overlap, every workspace element a launch reads was written by an
+// earlier launch of the same rectangle, and every element of C is written once.
+
+struct BufSizes {
+  int64_t n[NUM_BASES];
+};
+
+static int64_t view_factor_elems(const View &v) {
+  int64_t s = 0;
+  for (int32_t r : v.R) s += r;
+  return s * v.b;
+}
+
+static BufSizes buffer_sizes(const Plan &p) {
+  BufSizes z;
+  for (auto &x : z.n) x = 0;
+  z.n[BASE_A_OUTER] = z.n[BASE_A_INNER] = view_factor_elems(p.A);
+  z.n[BASE_A_DIAG] = p.A.diag ? (int64_t)p.A.qr * p.A.b * p.A.b : 0;
+  if (!p.dense_b) {
+    z.n[BASE_B_OUTER] = z.n[BASE_B_INNER] = view_factor_elems(p.B);
+    z.n[BASE_B_DIAG] = p.B.diag ? (int64_t)p.B.qr * p.B.b * p.B.b : 0;
+  } else if (p.dense_cols > 0 && p.dense_rows > 0) {
+    z.n[BASE_B_DENSE] = p.ldb * (p.dense_cols - 1) + p.dense_rows;
+  }
+  z.n[BASE_WS] = (int64_t)(p.ws_bytes / (size_t)p.es);
+  if (p.m > 0 && p.n > 0) z.n[BASE_C] = p.ldc * (p.n - 1) + p.m;
+  return z;
+}
+
+static bool operand_ok(const DevOperand &o, int64_t rows, int64_t cols, bool is_a, const BufSizes &z) {
+  // is_a: (rows, cols) = (M, K); else (K, N).  trans picks which index is contiguous.
+  if (o.base >= NUM_BASES || o.off < 0 || o.ld < 1) return false;
+  if (rows == 0 || cols == 0) return true;
+  const bool first_contig = (o.trans == 0);   // A: M contiguous / B: K contiguous
+  int64_t a = first_contig ? rows : cols, c = first_contig ? cols : rows;
+  (void)is_a;
+  int64_t last = o.off + (a - 1) + (c - 1) * (int64_t)o.ld;
+  return last < z.n[o.base];
+}
+
+static tlr_status validate(const Plan &p, bool deep) {
+  const BufSizes z = buffer_sizes(p);
+  for (size_t t = 0; t < p.tasks.size(); ++t) {
+    const DevTask &d = p.tasks[t];
+    if (d.M < 0 || d.N < 0 || d.nseg > 2) return fail(TLR_ERR_INVALID_ARG, "internal: malformed task");
+    for (int s = 0; s < d.nseg; ++s) {
+      if (d.seg[s].K <= 0) return fail(TLR_ERR_INVALID_ARG, "internal: empty segment");
+      if (!operand_ok(d.seg[s].a, d.M, d.seg[s].K, true, z) || !operand_ok(d.seg[s].b, d.seg[s].K, d.N, false, z))
+        return fail(TLR_ERR_INVALID_ARG, "internal: operand range outside its buffer (task " + std::to_string(t) + ")");
+    }
+    if (d.M == 0 || d.N == 0) continue;
+    if (d.c_base >= NUM_BASES || d.c_off < 0) return fail(TLR_ERR_INVALID_ARG, "internal: bad output");
+    int64_t lo, hi;
+    if (d.ctab < 0) {
+      if (d.ldc < d.M) return fail(TLR_ERR_INVALID_ARG, "internal: output columns overlap");
+      lo = d.c_off;
+      hi = d.c_off + (d.M - 1) + (int64_t)(d.N - 1) * d.ldc;
+    } else {
+      if (d.ctab + d.N > (int64_t)p.coltab.size()) return fail(TLR_ERR_INVALID_ARG, "internal: column map overrun");
+      lo = std::numeric_limits<int64_t>::max();
+      hi = -1;
+      for (int n = 0; n < d.N; ++n) {
+        lo = std::min(lo, d.c_off + p.coltab[d.ctab + n]);
+        hi = std::max(hi, d.c_off + p.coltab[d.ctab + n] + d.M - 1);
+      }
+    }
+    if (lo < 0 || hi >= z.n[d.c_base])
+      return fail(TLR_ERR_INVALID_ARG, "internal: output range outside its buffer (task " + std::to_string(t) + ")");
+  }
+  // workgroup tables: each block of each task exactly once
+  std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), 0);
+  for (size_t t = 0; t < p.tasks.size(); ++t)
+    want[t] = ceil_div(p.tasks[t].M, BM) * ceil_div(p.tasks[t].N, BN);
+  for (const Launch &L : p.launches) {
+    if (L.tile_off < 0 || L.tile_off + L.n_tiles > (int64_t)p.tiles.size() || L.n_tiles % NUM_XCD)
+      return fail(TLR_ERR_INVALID_ARG, "internal: launch table out of range");
+    for (int64_t e = L.tile_off; e < L.tile_off + L.n_tiles; ++e) {
+      const DevTile &x = p.tiles[e];
+      if (x.task < 0) continue;
+      if (x.task >= (int32_t)p.tasks.size()) return fail(TLR_ERR_INVALID_ARG, "internal: bad task index");
+      const DevTask &d = p.tasks[x.task];
+      if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % BM || x.n0 % BN)
+        return fail(TLR_ERR_INVALID_ARG, "internal: bad block origin");
+      seen[x.task]++;
+    }
+  }
+  for (size_t t = 0; t < p.tasks.size(); ++t)
+    if (seen[t] != want[t]) return fail(TLR_ERR_INVALID_ARG, "internal: blocks of a task missing or repeated");
+  if (!deep) return TLR_OK;
+
+  // deep check: replay every launch on per-element state
+  std::vector<uint8_t> ws((size_t)z.n[BASE_WS], 0);
+  std::vector<uint64_t> cbits((size_t)((z.n[BASE_C] + 63) / 64), 0);
+  int64_t cwrites = 0;
+  auto for_elems = [&](const DevOperand &o, int64_t rows, int64_t cols, auto &&fn) {
+    const bool fc = o.trans == 0;
+    const int64_t a = fc ? rows : cols, c = fc ? cols : rows;
+    for (int64_t y = 0; y < c; ++y)
+      for (int64_t x = 0; x < a; ++x)
+        if (!fn(o.off + x + y * (int64_t)o.ld)) return false;
+    return true;
+  };
+  for (const Group &G : p.groups) {
+    int cur_rect = -1;
+    int64_t rect_lo = 0, rect_hi = 0;
+    for (int li : G.launches) {
+      const Launch &L = p.launches[li];
+      if (L.rect != cur_rect) {   // a new rectangle reuses the group's arena from scratch
+        cur_rect = L.rect;
+        rect_lo = (int64_t)(G.arena_off / (size_t)p.es);
+        rect_hi = (int64_t)((G.arena_off + G.arena_bytes) / (size_t)p.es);
+        std::fill(ws.begin() + rect_lo, ws.begin() + rect_hi, 0);
+      }
+      const uint8_t me = (uint8_t)L.stage;
+      // collect distinct tasks of the launch
+      std::vector<int32_t> tl;
+      for (int64_t e = L.tile_off; e < L.tile_off + L.n_tiles; ++e)
+        if (p.tiles[e].task >= 0) tl.push_back(p.tiles[e].task);
+      std::sort(tl.begin(), tl.end());
+      tl.erase(std::unique(tl.begin(), tl.end()), tl.end());
+      for (int32_t ti : tl) {
+        const DevTask &d = p.tasks[ti];
+        for (int s = 0; s < d.nseg; ++s) {
+          for (int w = 0; w < 2; ++w) {
+            const DevOperand &o = w == 0 ? d.seg[s].a : d.seg[s].b;
+            if (o.base != BASE_WS) continue;
+            bool ok = w == 0 ? for_elems(o, d.M, d.seg[s].K, [&](int64_t e) {
+                                 return e >= rect_lo && e < rect_hi && ws[e] != 0 && ws[e] < me;
+                               })
+                             : for_elems(o, d.seg[s].K, d.N, [&](int64_t e) {
+                                 return e >= rect_lo && e < rect_hi && ws[e] != 0 && ws[e] < me;
+                               });
+            if (!ok) return fail(TLR_ERR_INVALID_ARG, "internal: workspace read before it is written (task " + std::to_string(ti) + ")");
+          }
+        }
+        for (int n = 0; n < d.N; ++n) {
+          int64_t col = d.ctab < 0 ? (int64_t)n * d.ldc : p.coltab[d.ctab + n];
+          for (int m = 0; m < d.M; ++m) {
+            int64_t e = d.c_off + col + m;
+            if (d.c_base == BASE_WS) {
+              if (e < rect_lo || e >= rect_hi || ws[e] != 0)
+                return fail(TLR_ERR_INVALID_ARG, "internal: overlapping workspace writes (task " + std::to_string(ti) + ")");
+              ws[e] = me;
+            } else if (d.c_base == BASE_C) {
+              uint64_t &word = cbits[(size_t)e >> 6];
+              uint64_t bit = 1ull << (e & 63);
+              if (word & bit) return fail(TLR_ERR_INVALID_ARG, "internal: element of C written twice");
+              if (e % p.ldc >= p.m) return fail(TLR_ERR_INVALID_ARG, "internal: write into C's padding");
+              word |= bit;
+              cwrites++;
+            } else {
+              return fail(TLR_ERR_INVALID_ARG, "internal: task writes an input buffer");
+            }
+          }
+        }
+      }
+    }
+  }
+  if (cwrites != p.m * p.n) return fail(TLR_ERR_INVALID_ARG, "internal: C not covered exactly once");
+  return TLR_OK;
+}
+
+tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, const tlr_shape *B,
+                      int64_t dense_rows, int64_t dense_cols, int64_t ldb, int64_t ldc, size_t budget,
+                      int n_streams, uint32_t flags, bool build_descriptors, Plan *p) {
+  if (dt != TLR_F32 && dt != TLR_F64) return fail(TLR_ERR_INVALID_ARG, "dtype must be TLR_F32 or TLR_F64");
+  if ((opA != TLR_OP_N && opA != TLR_OP_T) || (opB != TLR_OP_N && opB != TLR_OP_T))
+    return fail(TLR_ERR_INVALID_ARG, "op must be TLR_OP_N or TLR_OP_T");
+  if (n_streams < 1) return fail(TLR_ERR_INVALID_ARG, "n_streams must be >= 1");
+  if ((flags & TLR_PLAN_FORCE_RIGHT) && (flags & TLR_PLAN_FORCE_LEFT))
+    return fail(TLR_ERR_INVALID_ARG, "cannot force both orders");
+  if (flags & ~(TLR_PLAN_FORCE_RIGHT | TLR_PLAN_FORCE_LEFT | TLR_PLAN_NO_REGIONS | TLR_PLAN_VALIDATE))
+    return fail(TLR_ERR_INVALID_ARG, "unknown flag bits");
+  p->dt = dt;
+  p->es = dt == TLR_F64 ? 8 : 4;
+  p->budget = budget;
+  p->n_streams = n_streams;
+  p->flags = flags;
+  p->dense_b = (B == nullptr);
+  p->opB = opB;
+  tlr_status st = make_view(A, opA, BASE_A_OUTER, BASE_A_INNER, BASE_A_DIAG, "A", &p->A);
+  if (st != TLR_OK) return st;
+  p->m = A ? (opA == TLR_OP_N ? A->rows : A->cols) : 0;
+  p->k = A ? (opA == TLR_OP_N ? A->cols : A->rows) : 0;
+  if (p->dense_b) {
+    if (flags & TLR_PLAN_FORCE_LEFT) return fail(TLR_ERR_UNSUPPORTED, "the left order needs a TLR B");
+    if (dense_rows < 0 || dense_cols < 0) return fail(TLR_ERR_INVALID_ARG, "bad dense B dims");
+    int64_t kb = opB == TLR_OP_N ? dense_rows : dense_cols;
+    p->n = opB == TLR_OP_N ? dense_cols : dense_rows;
+    if (kb != p->k) return fail(TLR_ERR_INVALID_ARG, "op(A) columns != op(B) rows");
+    if (ldb < std::max<int64_t>(1, dense_rows)) return fail(TLR_ERR_INVALID_ARG, "ldb < rows of B");
+    if (ldb > std::numeric_limits<int32_t>::max()) return fail(TLR_ERR_INVALID_ARG, "ldb too large");
+    p->ldb = ldb;
+    p->dense_rows = dense_rows;
+    p->dense_cols = dense_cols;
+    split_dim(p->n, p->A.b, p->ns, p->no);
+  } else {
+    st = make_view(B, opB, BASE_B_OUTER, BASE_B_INNER, BASE_B_DIAG, "B", &p->B);
+    if (st != TLR_OK) return st;
+    if (B->b != A->b) return fail(TLR_ERR_INVALID_ARG, "A and B must use the same tile size");
+    int64_t kb = opB == TLR_OP_N ? B->rows : B->cols;
+    p->n = opB == TLR_OP_N ? B->cols : B->rows;
+    if (kb != p->k) return fail(TLR_ERR_INVALID_ARG, "op(A) columns != op(B) rows");
+    p->ns = p->B.cs;
+    p->no = p->B.co;
+  }
+  if (ldc < std::max<int64_t>(1, p->m)) return fail(TLR_ERR_INVALID_ARG, "ldc < rows of C");
+  if (ldc > std::numeric_limits<int32_t>::max()) return fail(TLR_ERR_INVALID_ARG, "ldc too large");
+  if (p->m > std::numeric_limits<int32_t>::max() || p->n > std::numeric_limits<int32_t>::max())
+    return fail(TLR_ERR_INVALID_ARG, "C dimensions too large");
+  p->ldc = ldc;
+
+  Sums s;
+  build_sums(*p, s);
+  const int qm = s.qm, qn = s.qn;
+  // whole-C accounting
+  p->flops_right = (qm && qn) ? rect_useful(*p, s, 0, qm, 0, qn, TLR_ORDER_RIGHT) : 0;
+  p->flops_left = p->dense_b ? -1 : ((qm && qn) ? rect_useful(*p, s, 0, qm, 0, qn, TLR_ORDER_LEFT) : 0);
+  p->final_right = 0;
+  for (int i = 0; i < qm; ++i) p->final_right += 2.0 * p->A.rs[i] * (double)s.rho[i] * p->n;
+  if (!p->dense_b) {
+    p->final_left = 0;
+    for (int j = 0; j < qn; ++j) p->final_left += 2.0 * p->ns[j] * (double)s.gam[j] * p->m;
+  }
+  p->alg_bytes = (double)p->es * (compressed_elems(p->A) +
+                                  (p->dense_b ? (double)dense_rows * dense_cols : compressed_elems(p->B)) +
+                                  (double)p->m * p->n);
+
+  st = schedule(*p, s);
+  if (st != TLR_OK) return st;
+  p->useful_flops = 0;
+  for (auto &r : p->rects) p->useful_flops += r.useful_flops;
+  if (!build_descriptors) return TLR_OK;
+
+  p->tasks.clear();
+  p->tiles.clear();
+  p->coltab.clear();
+  p->launches.clear();
+  for (size_t g = 0; g < p->groups.size(); ++g)
+    for (int r : p->groups[g].rects) emit_rect(*p, s, r);
+  p->executed_flops = 0;
+  for (auto &L : p->launches) p->executed_flops += L.executed_flops;
+  p->task_bytes_off = 0;
+  p->tile_bytes_off = align_up(p->tasks.size() * sizeof(DevTask), WS_ALIGN);
+  p->ctab_bytes_off = p->tile_bytes_off + align_up(p->tiles.size() * sizeof(DevTile), WS_ALIGN);
+  p->desc_bytes = p->ctab_bytes_off + align_up(p->coltab.size() * sizeof(int64_t), WS_ALIGN);
+  if (p->desc_bytes == 0) p->desc_bytes = WS_ALIGN;
+  return validate(*p, (flags & TLR_PLAN_VALIDATE) != 0);
+}
+
+}  // namespace tlr

@@ -1,0 +1,128 @@
+// Host-side plan of one TLR GEMM shape: operand views, schedule, descriptors.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "tlr_desc.h"
+#include "tlrgemm.h"
+
+namespace tlr {
+
+constexpr int BM = 128;            // workgroup block of every grouped launch
+constexpr int BN = 128;
+constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
+constexpr int NUM_XCD = 8;         // MI355X: workgroups go round-robin over 8 XCDs
+
+// One operand after op: tile (i,j) of op(X) is Outer_ij Inner_ij^T, or the
+// dense diagonal (transposed when op = T).
+struct View {
+  int qr = 0, qc = 0;
+  int64_t b = 0;
+  std::vector<int64_t> rs, cs, ro, co;   // tile sizes / start offsets of rows, cols
+  std::vector<int32_t> R;                // ranks of op(X), R[i + j*qr]
+  std::vector<int64_t> ocol, icol;       // first column of tile (i,j)'s outer / inner factor
+  bool diag = false, diag_trans = false;
+  uint8_t outer_base = 0, inner_base = 0, diag_base = 0;
+  int32_t r(int i, int j) const { return R[(size_t)i + (size_t)j * qr]; }
+  int64_t oc(int i, int j) const { return ocol[(size_t)i + (size_t)j * qr]; }
+  int64_t ic(int i, int j) const { return icol[(size_t)i + (size_t)j * qr]; }
+};
+
+struct Rect {
+  int i0, i1, j0, j1;
+  int order;         // tlr_order
+  int group;
+  size_t ws_bytes;   // inside the group's arena
+  double useful_flops;
+};
+
+struct Launch {
+  int stage;         // 1, 2, 3
+  int group;
+  int rect;
+  int64_t tile_off;  // first DevTile of the launch in the tile table
+  int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)
+  int64_t n_tasks;
+  double useful_flops, executed_flops;
+};
+
+struct Group {
+  int stream;        // index into the streams given to execute
+  size_t arena_off;  // byte offset of the group's arena in the workspace
+  size_t arena_bytes;
+  std::vector<int> rects;
+  std::vector<int> launches;
+};
+
+struct Plan {
+  tlr_dtype dt = TLR_F64;
+  int es = 8;
+  bool dense_b = false;
+  View A, B;                  // B unused (except sizes) for a dense B
+  int opB = 0;
+  int64_t m = 0, n = 0, k = 0;
+  int64_t ldb = 0, ldc = 0;
+  int64_t dense_rows = 0, dense_cols = 0;
+  std::vector<int64_t> ns, no;    // C column tiles (B view columns, or b-wide for a dense B)
+  size_t budget = 0;
+  int n_streams = 1;
+  uint32_t flags = 0;
+
+  std::vector<Rect> rects;
+  std::vector<Group> groups;
+  std::vector<Launch> launches;
+  std::vector<DevTask> tasks;
+  std::vector<DevTile> tiles;
+  std::vector<int64_t> coltab;
+
+  size_t ws_bytes = 0;
+  size_t task_bytes_off = 0, tile_bytes_off = 0, ctab_bytes_off = 0, desc_bytes = 0;
+  double useful_flops = 0, executed_flops = 0;
+  double flops_right = 0, flops_left = -1, final_right = 0, final_left = -1;
+  double alg_bytes = 0;
+
+  // device state (set by bind / profile)
+  void *dev_desc = nullptr;
+  int device = -1;
+  std::vector<void *> join_events;   // hipEvent_t, one per group
+  void *fork_event = nullptr;
+  int prof_max = 0, prof_count = 0;
+  std::vector<void *> prof_events;   // 2 per launch per execute + 2 per execute (whole)
+  ~Plan();
+};
+
+// Planner (host only).
+tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB,
+                      const tlr_shape *B, int64_t dense_rows, int64_t dense_cols,
+                      int64_t ldb, int64_t ldc, size_t budget, int n_streams,
+                      uint32_t flags, bool build_descriptors, Plan *out);
+
+// Executor (HIP runtime).
+tlr_status plan_bind(Plan *p, void *dev_desc, size_t bytes, void *stream);
+tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_buffers *B,
+                        const void *B_dense, int64_t ldb, double beta, void *C, int64_t ldc,
+                        void *ws, size_t ws_bytes, void *const *streams, int n_streams);
+tlr_status plan_profile(Plan *p, int max_exec);
+tlr_status plan_profile_read(Plan *p, double *stage_ms, double *launch_ms, int32_t *execs);
+void plan_release_device(Plan *p);
+tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n, int64_t k,
+                      double alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                      double beta, void *C, int64_t ldc, void *stream);
+
+// Kernel launchers (gemm.hip).
+int launch_grouped(tlr_dtype dt, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
+                   const int64_t *coltab, const Bases &bases, double alpha, double beta,
+                   void *stream);
+int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double alpha,
+                  double beta, void *stream);
+int launch_scale(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta,
+                 void *stream);
+
+// Error reporting.
+void set_error(const std::string &msg);
+tlr_status fail(tlr_status s, const std::string &msg);
+
+}  // namespace tlr

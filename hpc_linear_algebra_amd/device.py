@@ -1,0 +1,95 @@
+"""PyTorch plumbing around the C ABI: device copies of packed operands and a
+plan object that owns its descriptor and workspace buffers.
+
+torch is used only for device memory and streams.  A column-major m x n
+matrix with leading dimension ld is a contiguous torch tensor of shape
+(n, ld); element (r, c) is tensor[c, r].
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import layout
+from . import tlrgemm as T
+from tlr_inputs import TLRTiles
+
+_TORCH = {"f64": torch.float64, "f32": torch.float32}
+
+
+def _dev(x: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
+    if x is None or x.size == 0:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+class DeviceTLR:
+    """A TLR operand packed on the host and copied to the GPU."""
+
+    def __init__(self, t: TLRTiles, device="cuda"):
+        pk = layout.pack(t)
+        self.rows, self.cols, self.b = t.rows, t.cols, t.b
+        self.dtype = t.dtype
+        self.has_diag = t.has_diag
+        self.ranks = np.asarray(t.ranks, dtype=np.int32)
+        self.shape = T.Shape(t.rows, t.cols, t.b, self.ranks, t.has_diag)
+        self.outer = _dev(pk["outer"], device)
+        self.inner = _dev(pk["inner"], device)
+        self.diag = _dev(pk["diag"], device)
+
+    def buffers(self) -> T.tlr_buffers:
+        return T.buffers(_ptr(self.diag), _ptr(self.outer), _ptr(self.inner))
+
+
+def dense_to_device(M: np.ndarray, device="cuda", ld: Optional[int] = None) -> torch.Tensor:
+    """Column-major device copy: tensor of shape (cols, ld)."""
+    rows, cols = M.shape
+    ld = rows if ld is None else ld
+    return torch.from_numpy(layout.to_colmajor(M, ld).reshape(cols, ld)).to(device)
+
+
+def dense_from_device(t: torch.Tensor, rows: int, cols: int) -> np.ndarray:
+    return t.detach().cpu().numpy()[:, :rows].T
+
+
+class TLRGemm:
+    """Analyse, allocate descriptor + workspace tensors, bind; then execute."""
+
+    def __init__(self, dtype: str, opA: str, A: DeviceTLR, opB: str, B, ldc: int,
+                 dense_shape: Optional[tuple] = None, ldb: int = 0, budget: int = 0,
+                 n_streams: int = 1, flags: int = 0, device="cuda"):
+        self.dtype = dtype
+        self.dense = B is None
+        dr, dc = dense_shape if self.dense else (0, 0)
+        self.plan = T.tlr_gemm_analyze(dtype, opA, A.shape, opB, None if self.dense else B.shape,
+                                       dr, dc, ldb, ldc, budget, n_streams, flags)
+        self.info = T.tlr_plan_info(self.plan)
+        self.ldb, self.ldc = ldb, ldc
+        self.desc = torch.empty(self.info["descriptor_bytes"], dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(self.info["workspace_bytes"], 256), dtype=torch.uint8, device=device)
+        T.tlr_plan_bind(self.plan, self.desc.data_ptr(), self.desc.numel(),
+                        torch.cuda.current_stream().cuda_stream)
+
+    def rects(self):
+        return [T.tlr_plan_rect(self.plan, r) for r in range(self.info["runs"])]
+
+    def launches(self):
+        return [T.tlr_plan_launch(self.plan, l) for l in range(self.info["launches"])]
+
+    def __call__(self, alpha: float, A: DeviceTLR, B, beta: float, C: torch.Tensor,
+                 streams: Optional[Sequence[int]] = None):
+        if streams is None:
+            streams = [torch.cuda.current_stream().cuda_stream]
+        if self.dense:
+            Bb, Bd = None, B.data_ptr()
+        else:
+            Bb, Bd = B.buffers(), 0
+        T.tlr_gemm_execute(self.plan, alpha, A.buffers(), Bb, Bd, self.ldb, beta, C.data_ptr(), self.ldc,
+                           self.ws.data_ptr(), self.ws.numel(), list(streams))
+        return C

@@ -1,0 +1,271 @@
+/*
+ * tlrgemm.h - Tile-Low-Rank GEMM with a dense output on AMD Instinct MI355X (gfx950).
+ *
+ *   C <- alpha * op(A) * op(B) + beta * C,   C dense, A TLR, B TLR or dense.
+ *
+ * The operation is the one stated in the introduction of "Tile-Low-Rank GEMM:
+ * Designing Storage Around the Contraction" (dense C, one or both operands in
+ * TLR format, op in {N, T}).  A TLR matrix is a regular grid of b x b tiles
+ * (the last tile row / column is smaller when b does not divide the
+ * dimension); diagonal tiles may be stored densely, every other tile (i,j) is
+ * a factor pair U_ij V_ij^T of its own rank r_ij ("TLR Matrix
+ * Multiplication", section "Introduction: TLR GEMM").
+ *
+ * Storage (section "Packing for the contraction" of the first page):
+ *   outer  U: packed by tile row.  Column-major, leading dimension b.  Tile
+ *             (i,j) occupies r_ij consecutive columns starting at column
+ *             sum_{i'<i} rho_i' + sum_{j'<j} r_ij'      (rho_i = sum_j r_ij),
+ *             of which its first s_i rows are used.
+ *   inner  V: packed by tile column.  Column-major, leading dimension b.  Tile
+ *             (i,j) occupies r_ij consecutive columns starting at column
+ *             sum_{j'<j} kappa_j' + sum_{i'<i} r_i'j    (kappa_j = sum_i r_ij),
+ *             of which its first s_j rows are used.
+ *   diag   D: q slots of b*b elements; slot i holds tile (i,i) column-major
+ *             with leading dimension b (top-left s_i x s_i used).  Only when
+ *             the matrix is square and has_diag != 0; r_ii must then be 0.
+ * Each tile takes exactly r_ij columns: no padding to a common rank.  Because
+ * U is packed by tile row and V by tile column, a row panel of U and a column
+ * panel of V are ordinary column-major matrices, which is what lets the
+ * library fold tile indices into GEMM dimensions without copies.
+ * op(X) = X^T is taken by swapping the roles of the two factor families and
+ * the tile coordinates (section "Where fusion stops", Transposes); no data
+ * moves.
+ *
+ * Dense matrices (C, a dense B) are column-major with a leading dimension.
+ * All element types are float (TLR_F32) or double (TLR_F64), the same for
+ * every buffer of one call.
+ *
+ * Ownership: every device buffer (factors, diagonals, dense B, C, workspace,
+ * descriptor buffer) belongs to the caller.  The library never allocates
+ * device memory.  A plan owns host memory and the HIP events it creates; the
+ * plan copies the rank tables at analysis time.
+ *
+ * Errors: every entry point returns a tlr_status and writes its outputs only
+ * on TLR_OK.  tlr_last_error() returns a thread-local description of the most
+ * recent failure.  Kernel faults are asynchronous and surface at the caller's
+ * next synchronisation, as usual for HIP.
+ *
+ * Streams are passed as opaque pointers (hipStream_t values, e.g.
+ * torch.cuda.Stream().cuda_stream under ROCm); NULL means the default stream.
+ */
+#ifndef TLRGEMM_H
+#define TLRGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TLR_OK = 0,
+  TLR_ERR_INVALID_ARG = -1,  /* null pointer, bad size, mismatched shapes or leading dims */
+  TLR_ERR_RANK = -2,         /* r_ij < 0, r_ij > min(s_i, s_j), or r_ii != 0 with a dense diagonal */
+  TLR_ERR_WORKSPACE = -3,    /* budget below what one output tile needs, or workspace too small */
+  TLR_ERR_UNSUPPORTED = -4,  /* combination not provided (e.g. forcing the left order with a dense B) */
+  TLR_ERR_HIP = -5,          /* a HIP runtime call failed */
+  TLR_ERR_NOT_BOUND = -6     /* execute before tlr_plan_bind */
+} tlr_status;
+
+typedef enum { TLR_F32 = 0, TLR_F64 = 1 } tlr_dtype;
+typedef enum { TLR_OP_N = 0, TLR_OP_T = 1 } tlr_op;
+typedef enum { TLR_ORDER_RIGHT = 0, TLR_ORDER_LEFT = 1 } tlr_order;
+
+/* Flags of tlr_gemm_analyze / tlr_gemm_workspace_bytes. */
+#define TLR_PLAN_FORCE_RIGHT 0x1u  /* every rectangle uses U (S Z^T) */
+#define TLR_PLAN_FORCE_LEFT  0x2u  /* every rectangle uses (U S) Z^T (TLR x TLR only) */
+#define TLR_PLAN_NO_REGIONS  0x4u  /* do not split boundary regions onto their own streams */
+#define TLR_PLAN_VALIDATE    0x8u  /* also run the exhaustive descriptor self-check (slow; for tests) */
+
+/* Structure of one stored TLR operand (host data; no device pointers). */
+typedef struct {
+  int64_t rows, cols;      /* stored dimensions (before op) */
+  int32_t b;               /* tile size, >= 1; q_r = ceil(rows/b), q_c = ceil(cols/b) */
+  int32_t has_diag;        /* 1: diagonal tiles dense (rows == cols required) */
+  const int32_t *ranks;    /* q_r*q_c ranks, column-major: rank of tile (i,j) at ranks[i + j*q_r] */
+} tlr_shape;
+
+/* Device buffers of one stored TLR operand, laid out as described above. */
+typedef struct {
+  const void *diag;        /* NULL iff has_diag == 0 */
+  const void *outer;       /* U, packed by tile row;  may be NULL when every rank is 0 */
+  const void *inner;       /* V, packed by tile column; may be NULL when every rank is 0 */
+} tlr_buffers;
+
+typedef struct tlr_plan tlr_plan;
+
+/* Counts describing a plan (tlr_plan_info). */
+typedef struct {
+  int64_t m, n, k;             /* C is m x n; the contraction has k columns of op(A) */
+  double useful_flops;         /* flops of the method for the chosen orders, from rank metadata */
+  double executed_flops;       /* sum over kernel tasks of 2*M*N*K (>= useful when some ranks are 0) */
+  double flops_right;          /* whole-C useful flops if every tile used the right order */
+  double flops_left;           /* ... the left order (-1 for a dense B) */
+  double final_flops_right;    /* 2 sum_i m_i rho_i sum_j n_j */
+  double final_flops_left;     /* 2 sum_j n_j gamma_j sum_i m_i (-1 for a dense B) */
+  double algorithmic_bytes;    /* compressed A + (compressed or dense) B + C written once (add m*n elements
+                                  for the read of C when beta != 0) */
+  size_t workspace_bytes;      /* device workspace execute needs (<= the analysis budget) */
+  size_t descriptor_bytes;     /* device buffer size tlr_plan_bind needs */
+  int32_t runs;                /* output rectangles */
+  int32_t groups;              /* region groups (each on its own stream when streams allow) */
+  int32_t launches;            /* kernel launches per execute */
+  int32_t dtype;               /* tlr_dtype */
+} tlr_plan_summary;
+
+/* ---- host-only entry points (no HIP calls) --------------------------------- */
+
+/*
+ * tlr_gemm_analyze: build the plan of one product shape ("Association order and
+ * workspace": rank prefixes, association order per rectangle, rectangles under
+ * the workspace budget, grouped descriptors; reusable for every product with
+ * the same rank structure).
+ *   dt          element type of every buffer.
+ *   opA, A      op and structure of A (required).
+ *   opB, B      op and structure of B; B == NULL selects a dense B of
+ *               dense_rows x dense_cols (stored, column-major, leading dim ldb).
+ *   ldb         leading dimension of a dense B (ignored for a TLR B).
+ *   ldc         leading dimension of C (>= m).
+ *   workspace_budget  bytes of device workspace execute may use; 0 means no limit.
+ *   n_streams   streams execute will be given (>= 1); boundary regions of C
+ *               (last tile row / column smaller than b) run concurrently when >= 2.
+ *   flags       TLR_PLAN_* bits.
+ *   plan_out    receives a new plan (free with tlr_plan_destroy).
+ * Every plan is checked before it is returned: each operand and output range a
+ * kernel task can touch must lie inside the buffer sizes the layout above
+ * implies (factor buffers b * sum(r_ij) elements, diagonal q*b*b, dense B
+ * ldb * cols, C ldc * n, workspace workspace_bytes); with TLR_PLAN_VALIDATE it
+ * also checks that writes inside one launch never overlap, that every
+ * workspace element a launch reads was written earlier for the same output
+ * rectangle, and that each element of C is written exactly once.
+ * Errors: TLR_ERR_INVALID_ARG (shapes, tile sizes or leading dims inconsistent),
+ * TLR_ERR_RANK, TLR_ERR_WORKSPACE (budget below one output tile's needs),
+ * TLR_ERR_UNSUPPORTED.
+ */
+tlr_status tlr_gemm_analyze(tlr_dtype dt, tlr_op opA, const tlr_shape *A,
+                            tlr_op opB, const tlr_shape *B,
+                            int64_t dense_rows, int64_t dense_cols, int64_t ldb,
+                            int64_t ldc, size_t workspace_budget, int32_t n_streams,
+                            uint32_t flags, tlr_plan **plan_out);
+
+/*
+ * tlr_gemm_workspace_bytes: the smallest budget whose schedule has at most
+ * `runs` rectangles (runs >= 1; runs == 1 gives the budget of one rectangle
+ * covering all of C), found by bisection over the scheduler
+ * ("Association order and workspace": workspace bytes for a target number of
+ * runs).  Arguments as for tlr_gemm_analyze.  Errors as for analyze.
+ */
+tlr_status tlr_gemm_workspace_bytes(tlr_dtype dt, tlr_op opA, const tlr_shape *A,
+                                    tlr_op opB, const tlr_shape *B,
+                                    int64_t dense_rows, int64_t dense_cols,
+                                    int32_t n_streams, uint32_t flags, int32_t runs,
+                                    size_t *bytes_out);
+
+/* tlr_plan_info: fill *out.  Errors: TLR_ERR_INVALID_ARG on NULL. */
+tlr_status tlr_plan_info(const tlr_plan *p, tlr_plan_summary *out);
+
+/*
+ * tlr_plan_rect: rectangle `idx` (0 <= idx < runs) of the schedule.
+ *   out_i32[0..5] = first tile row, end tile row (exclusive), first tile
+ *                   column, end tile column, order (tlr_order), group.
+ *   ws_bytes      workspace the rectangle uses inside its group's arena.
+ *   useful_flops  useful flops of the rectangle.
+ */
+tlr_status tlr_plan_rect(const tlr_plan *p, int32_t idx, int32_t *out_i32,
+                         size_t *ws_bytes, double *useful_flops);
+
+/*
+ * tlr_plan_stage_shapes: (M, N, K) triples of the logical GEMMs of one stage of
+ * rectangle `rect`, in order:
+ *   stage 1  one coupling GEMM per contraction tile k ("One product, three
+ *            stages", Stage 1): (sum_{i in I} r_ik, sum_{j in J} r_kj, s_k);
+ *   stage 3  the final GEMMs: per tile row i (right order) (m_i, sum_J n_j, rho_i),
+ *            per tile column j (left order) (sum_I m_i, n_j, gamma_j).
+ * Writes min(count, cap) triples to mnk[3*t..3*t+2]; *count = number available.
+ */
+tlr_status tlr_plan_stage_shapes(const tlr_plan *p, int32_t rect, int32_t stage,
+                                 int64_t *mnk, int32_t cap, int32_t *count);
+
+/*
+ * tlr_plan_launch: launch `idx` (0 <= idx < launches) of one execute.
+ *   out_i32[0..3] = stage (1, 2 or 3), tasks, workgroups, group.
+ *   out_f64[0..1] = useful flops, executed flops of the launch.
+ */
+tlr_status tlr_plan_launch(const tlr_plan *p, int32_t idx, int32_t *out_i32, double *out_f64);
+
+/* tlr_plan_destroy: free the plan and its events (NULL is accepted). */
+tlr_status tlr_plan_destroy(tlr_plan *p);
+
+/* ---- device entry points ------------------------------------------------- */
+
+/*
+ * tlr_plan_bind: copy the plan's descriptor tables into `dev_desc`, a caller
+ * device buffer of at least descriptor_bytes bytes (256-byte aligned), on
+ * `stream`, and create the plan's fork/join events on the current device.
+ * The buffer must stay alive and unmodified while the plan is executed.
+ * Errors: TLR_ERR_INVALID_ARG (NULL, too small, misaligned), TLR_ERR_HIP.
+ */
+tlr_status tlr_plan_bind(tlr_plan *p, void *dev_desc, size_t bytes, void *stream);
+
+/*
+ * tlr_gemm_execute: C <- alpha op(A) op(B) + beta C with the bound plan.
+ *   A, B        device buffers of the analysed operands (B NULL for a dense B).
+ *   B_dense     dense B (when analysed with B == NULL), leading dim ldb.
+ *   C           m x n column-major, leading dim ldc (both as analysed).
+ *   workspace   device buffer of at least workspace_bytes (256-byte aligned).
+ *   streams     n_streams >= 1 streams; streams[0] is the caller's: the call is
+ *               ordered after earlier work on streams[0] and later work on
+ *               streams[0] is ordered after it.  Other streams are forked from
+ *               and joined back to streams[0] with events.
+ * beta == 0 never reads C (NaN in C does not propagate); alpha == 0 only scales C.
+ * Asynchronous: no host synchronisation.
+ * Errors: TLR_ERR_NOT_BOUND, TLR_ERR_INVALID_ARG (NULL buffers, ld mismatch),
+ * TLR_ERR_WORKSPACE (workspace too small), TLR_ERR_HIP (launch failure).
+ */
+tlr_status tlr_gemm_execute(tlr_plan *p, double alpha,
+                            const tlr_buffers *A, const tlr_buffers *B,
+                            const void *B_dense, int64_t ldb,
+                            double beta, void *C, int64_t ldc,
+                            void *workspace, size_t workspace_bytes,
+                            void *const *streams, int32_t n_streams);
+
+/*
+ * tlr_plan_profile: record a HIP event pair around every launch of the next
+ * `max_executes` executes (0 switches recording off).  Creates the events on
+ * the current device.  Errors: TLR_ERR_HIP.
+ * tlr_plan_profile_read: after the caller has synchronised, sum the recorded
+ * kernel time per stage: stage_ms[0..2] = stages 1..3, stage_ms[3] = the whole
+ * execute (first launch start to last launch end on streams[0]);
+ * launch_ms (may be NULL) receives the per-launch sums, `launches` entries.
+ * *executes = executes recorded.  Resets the record.
+ */
+tlr_status tlr_plan_profile(tlr_plan *p, int32_t max_executes);
+tlr_status tlr_plan_profile_read(tlr_plan *p, double *stage_ms, double *launch_ms,
+                                 int32_t *executes);
+
+/*
+ * tlr_dense_gemm: C <- alpha op(A) op(B) + beta C for dense column-major
+ * matrices, on the same MFMA kernel (one K segment per output tile).  It is
+ * the same-chip dense reference the TLR product is compared with ("Results":
+ * dense-GEMM time scaled by the ratio of executed flops).
+ *   op(A) is m x k, op(B) is k x n, C is m x n; lda/ldb/ldc >= rows of the
+ *   stored matrices.  beta == 0 never reads C.  No workspace.
+ * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_HIP.
+ */
+tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n,
+                          int64_t k, double alpha, const void *A, int64_t lda,
+                          const void *B, int64_t ldb, double beta, void *C, int64_t ldc,
+                          void *stream);
+
+/* Static description of a status code. */
+const char *tlr_status_string(tlr_status s);
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *tlr_last_error(void);
+/* Library version string. */
+const char *tlr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TLRGEMM_H */

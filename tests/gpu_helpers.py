@@ -1,0 +1,98 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and compare with the oracle.  (Not collected by pytest: no test_ prefix.)"""
+from __future__ import annotations
+
+import copy
+import sys
+
+import numpy as np
+
+from oracle import reference
+from tlr_inputs import TLRTiles
+
+TOL = {"f64": 1e-12, "f32": 1e-5}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_ready():
+    try:
+        import torch
+        if not torch.cuda.is_available():
+            return False
+        from hpc_linear_algebra_amd import tlrgemm
+        tlrgemm.lib()
+        return True
+    except Exception:
+        return False
+
+
+def op_dims(t, op):
+    return (t.rows, t.cols) if op == "N" else (t.cols, t.rows)
+
+
+def run_tlr(A: TLRTiles, B, opA: str, opB: str, alpha: float, beta: float, C_in,
+            budget: int = 0, n_streams: int = 1, flags: int = 0, ld_pad: int = 0, return_plan=False):
+    """C = alpha op(A) op(B) + beta C_in on the GPU; C_in None -> NaN-filled C."""
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_from_device, dense_to_device
+    dtype = A.dtype
+    m = op_dims(A, opA)[0]
+    dense = not isinstance(B, TLRTiles)
+    if dense:
+        n = B.shape[1] if opB == "N" else B.shape[0]
+    else:
+        n = op_dims(B, opB)[1]
+    ldc = max(1, m + ld_pad)
+    npd = np.float64 if dtype == "f64" else np.float32
+    Cstart = np.full((m, n), np.nan, dtype=npd) if C_in is None else np.asarray(C_in, dtype=npd)
+    dA = DeviceTLR(A)
+    if dense:
+        ldb = max(1, B.shape[0] + ld_pad)
+        dB = dense_to_device(np.asarray(B, dtype=npd), ld=ldb)
+        g = TLRGemm(dtype, opA, dA, opB, None, ldc=ldc, dense_shape=B.shape, ldb=ldb, budget=budget,
+                    n_streams=n_streams, flags=flags)
+    else:
+        dB = DeviceTLR(B)
+        g = TLRGemm(dtype, opA, dA, opB, dB, ldc=ldc, budget=budget, n_streams=n_streams, flags=flags)
+    Cd = dense_to_device(Cstart, ld=ldc)
+    side = [torch.cuda.Stream() for _ in range(n_streams - 1)]
+    streams = [torch.cuda.current_stream().cuda_stream] + [s.cuda_stream for s in side]
+    g(alpha, dA, dB, beta, Cd, streams)
+    torch.cuda.synchronize()
+    out = dense_from_device(Cd, m, n)
+    if return_plan:
+        return out, g
+    return out
+
+
+def check_tlr(A, B, opA, opB, alpha, beta, C_in, **kw):
+    got = run_tlr(A, B, opA, opB, alpha, beta, C_in, **kw)
+    ref = reference.gemm_reference(alpha, opA, A, opB, B, beta, C_in)
+    err = reference.rel_fro(got, ref)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    assert err <= TOL[A.dtype], f"relative Frobenius error {err:.3e} > {TOL[A.dtype]:.0e}"
+    return err
+
+
+def transpose_tlr(t: TLRTiles) -> TLRTiles:
+    U = {(j, i): t.V[(i, j)].copy() for (i, j) in t.U}
+    V = {(j, i): t.U[(i, j)].copy() for (i, j) in t.U}
+    D = None if t.diag is None else [d.T.copy() for d in t.diag]
+    return TLRTiles(t.cols, t.rows, t.b, t.ranks.T.copy(), D, U, V, t.dtype)
+
+
+def padded_tlr(t: TLRTiles, rmax: int) -> TLRTiles:
+    p = copy.deepcopy(t)
+    for key in list(p.U):
+        u, v = p.U[key], p.V[key]
+        r = u.shape[1]
+        want = min(rmax, u.shape[0], v.shape[0])
+        if want > r:
+            p.U[key] = np.concatenate([u, np.zeros((u.shape[0], want - r), u.dtype)], axis=1)
+            p.V[key] = np.concatenate([v, np.zeros((v.shape[0], want - r), v.dtype)], axis=1)
+            p.ranks[key] = want
+    return p
