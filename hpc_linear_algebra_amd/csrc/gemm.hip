@@ -27,18 +27,26 @@ namespace {
 
 constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 16, NTHR = 256;
 
+// Lane layout of the 16x16x4 MFMAs (measured on gfx950): lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; accumulator element v of lane l is
+// D[row][l % 16] with row = 4*(l/16) + v for fp32 but row = l/16 + 4*v for
+// fp64.  For fp64 the A fragment is therefore read with its rows permuted by
+// arow(x) = 4*(x%4) + x/4, which makes both types leave rows 4*(l/16)+v, i.e.
+// four consecutive rows of one column, in lane l.
 template <typename T> struct Mfma;
 template <> struct Mfma<double> {
   typedef double v4 __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ v4 mma(double a, double b, v4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ int arow(int x) { return ((x & 3) << 2) | (x >> 2); }
 };
 template <> struct Mfma<float> {
   typedef float v4 __attribute__((ext_vector_type(4)));
   static __device__ __forceinline__ v4 mma(float a, float b, v4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ int arow(int x) { return x; }
 };
 
 struct SegState {
@@ -129,6 +137,7 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int arow = Mfma<T>::arow(lane & 15);
   const int M = t.M, N = t.N;
 
   v4 acc[4][4];
@@ -160,7 +169,7 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
         const int kr = kq * 4 + (lane >> 4);
         T a[4], b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[buf][kr][wm + 16 * i + (lane & 15)];
+        for (int i = 0; i < 4; ++i) a[i] = As[buf][kr][wm + 16 * i + arow];
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = Bs[buf][kr][wn + 16 * j + (lane & 15)];
 #pragma unroll

@@ -78,8 +78,10 @@ def test_budget_split_and_regions(dtype, n_streams):
         assert g.info["workspace_bytes"] <= w
         ref = reference.gemm_reference(1.0, "N", A, "N", B, 1.0, C)
         assert reference.rel_fro(got, ref) <= TOL[dtype]
-        if n_streams > 1:
+        if n_streams > 1 and runs == 1:
+            # enough workspace: the three boundary regions run beside the interior
             assert g.info["groups"] == 4
+        assert g.info["groups"] in (1, 4)
 
 
 def test_rank_zero_tiles_contribute_nothing():
