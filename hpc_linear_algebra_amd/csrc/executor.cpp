@@ -182,7 +182,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
     for (int l : p->groups[g].launches) {
       const Launch &L = p->launches[l];
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
-      int e = launch_grouped(p->dt, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases, alpha, beta, sg);
+      int e = launch_grouped(p->dt, L.stage, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases, alpha, beta, sg);
       if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
       if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));
     }
@@ -209,8 +209,8 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
   if ((opA != TLR_OP_N && opA != TLR_OP_T) || (opB != TLR_OP_N && opB != TLR_OP_T))
     return fail(TLR_ERR_INVALID_ARG, "dense: bad op");
   if (m < 0 || n < 0 || k < 0) return fail(TLR_ERR_INVALID_ARG, "dense: negative size");
-  const int64_t lim = 0x7fffffff;
-  if (m > lim || n > lim || k > lim || lda > lim || ldb > lim || ldc > lim)
+  const int64_t lim = 0x7fffffff, ldlim = (int64_t)1 << 24;
+  if (m > lim || n > lim || k > lim || lda >= ldlim || ldb >= ldlim || ldc > lim)
     return fail(TLR_ERR_INVALID_ARG, "dense: size or leading dim too large");
   const int64_t arows = opA == TLR_OP_N ? m : k, brows = opB == TLR_OP_N ? k : n;
   if (lda < std::max<int64_t>(1, arows) || ldb < std::max<int64_t>(1, brows) || ldc < std::max<int64_t>(1, m))
@@ -234,6 +234,7 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
   t.c_base = BASE_C;
   t.final_ = 1;
   t.nseg = 1;
+  t.flags = ldc % 4 == 0 ? TASK_VEC : 0;
   t.seg[0].a.off = 0;
   t.seg[0].a.ld = (int32_t)lda;
   t.seg[0].a.base = BASE_A_OUTER;

@@ -767,7 +767,8 @@ static BufSizes buffer_sizes(const Plan &p) {
 
 static bool operand_ok(const DevOperand &o, int64_t rows, int64_t cols, bool is_a, const BufSizes &z) {
   // is_a: (rows, cols) = (M, K); else (K, N).  trans picks which index is contiguous.
-  if (o.base >= NUM_BASES || o.off < 0 || o.ld < 1) return false;
+  // the kernel forms intra-tile offsets up to 127*ld in 32 bits
+  if (o.base >= NUM_BASES || o.off < 0 || o.ld < 1 || o.ld >= (1 << 24)) return false;
   if (rows == 0 || cols == 0) return true;
   const bool first_contig = (o.trans == 0);   // A: M contiguous / B: K contiguous
   int64_t a = first_contig ? rows : cols, c = first_contig ? cols : rows;
@@ -976,6 +977,14 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   p->launches.clear();
   for (size_t g = 0; g < p->groups.size(); ++g)
     for (int r : p->groups[g].rects) emit_rect(*p, s, r);
+  // output columns that start on a 4-element boundary allow 4-row vector stores
+  for (DevTask &d : p->tasks) {
+    bool v = d.c_off % 4 == 0;
+    if (d.ctab < 0) v = v && d.ldc % 4 == 0;
+    else
+      for (int n = 0; n < d.N && v; ++n) v = p->coltab[d.ctab + n] % 4 == 0;
+    d.flags = v ? TASK_VEC : 0;
+  }
   p->executed_flops = 0;
   for (auto &L : p->launches) p->executed_flops += L.executed_flops;
   p->task_bytes_off = 0;

@@ -51,9 +51,11 @@ struct DevTask {         // 112 bytes
   uint8_t c_base;
   uint8_t final_;        // 1: alpha/beta update of C
   uint8_t nseg;
-  uint8_t pad0;
+  uint8_t flags;         // TASK_VEC: every output column starts 4-element aligned
   DevSeg seg[2];
 };
+
+enum TaskFlags : uint8_t { TASK_VEC = 1 };
 
 struct DevTile {         // 16 bytes
   int32_t task;          // < 0: idle workgroup (launch padding)

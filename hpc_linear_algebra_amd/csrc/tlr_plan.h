@@ -113,7 +113,7 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
                       double beta, void *C, int64_t ldc, void *stream);
 
 // Kernel launchers (gemm.hip).
-int launch_grouped(tlr_dtype dt, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
+int launch_grouped(tlr_dtype dt, int stage, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
                    const int64_t *coltab, const Bases &bases, double alpha, double beta,
                    void *stream);
 int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double alpha,
