@@ -18,7 +18,6 @@ the CPU oracle timed on a bounded sample of output tiles.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -38,10 +37,8 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "tlr_desc.h"):
-        h.update(open(os.path.join(ROOT, "hpc_linear_algebra_amd", "csrc", f), "rb").read())
-    return h.hexdigest()[:16]
+    from hpc_linear_algebra_amd.profiling import kernel_source_hash
+    return kernel_source_hash()
 
 
 def traffic_from_profiles(stage: int):
@@ -149,7 +146,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-GEMM reference")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = (1 << 30) // 8
+        src = torch.ones(n, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 8, "copy_bytes_written": n * 8, "dispatches": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the TLR GEMM here runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)

@@ -209,7 +209,7 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
   if ((opA != TLR_OP_N && opA != TLR_OP_T) || (opB != TLR_OP_N && opB != TLR_OP_T))
     return fail(TLR_ERR_INVALID_ARG, "dense: bad op");
   if (m < 0 || n < 0 || k < 0) return fail(TLR_ERR_INVALID_ARG, "dense: negative size");
-  const int64_t lim = 0x7fffffff, ldlim = (int64_t)1 << 24;
+  const int64_t lim = 0x7fffffff, ldlim = (int64_t)1 << 21;
   if (m > lim || n > lim || k > lim || lda >= ldlim || ldb >= ldlim || ldc > lim)
     return fail(TLR_ERR_INVALID_ARG, "dense: size or leading dim too large");
   const int64_t arows = opA == TLR_OP_N ? m : k, brows = opB == TLR_OP_N ? k : n;

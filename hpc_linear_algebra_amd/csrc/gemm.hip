@@ -8,13 +8,13 @@
 // Layout of the descriptors: tlr_desc.h.  Each stage gets its own kernel symbol
 // so that profilers report the stages separately.
 //
-// Work split: 256 threads = 4 wave64s in a 2 x 2 arrangement, each wave owns
-// a 64 x 64 sub-block = 4 x 4 MFMA tiles of 16 x 16
-// (v_mfma_f64_16x16x4_f64 / v_mfma_f32_16x16x4_f32).  K advances in stages of
-// BK = 16, staged through LDS and double-buffered: the global loads of stage
-// s+1 are in flight while the MFMAs of stage s run.  Register use is held to
-// 256 per lane so that two workgroups share a CU: while one waits on memory
-// (its first stage, its C update) the other keeps the matrix cores busy.
+// Work split: the 128 x 128 block is shared by 4 or 8 wave64s (64 x 64 or
+// 64 x 32 per wave, MFMA tiles of 16 x 16: v_mfma_f64_16x16x4_f64 /
+// v_mfma_f32_16x16x4_f32).  K advances in stages of BK = 16, staged through LDS
+// and double-buffered: the global loads of stage s+1 are in flight while the
+// MFMAs of stage s run.  Registers are held so that two workgroups share a CU:
+// while one waits on memory (its first stage, its C update) the other keeps
+// the matrix cores busy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,7 +26,10 @@ namespace tlr {
 
 namespace {
 
-constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 16, NTHR = 256;
+// LDS rows hold 145 elements: an odd stride sends the 16 k-rows that one
+// K-contiguous operand store touches to 16 different banks, and a 16-element
+// fragment read still covers each bank once.
+constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 17;
 constexpr int LDS_A = KBM + KPAD, LDS_B = KBN + KPAD;
 
 // Lane layout of the 16x16x4 MFMAs (measured on gfx950): lane l supplies
@@ -51,29 +54,45 @@ template <> struct Mfma<float> {
   static __device__ __forceinline__ int arow(int x) { return x; }
 };
 
-// Which 8 elements of a 128 x 16 (A) or 16 x 128 (B) stage one thread moves.
+// Wave layout of a 128 x 128 workgroup block: WM x WN per wave (MI x NJ MFMA
+// tiles of 16 x 16), NT threads.  64 x 64 waves (4 per workgroup) hold 128
+// accumulator registers; 64 x 32 waves (8 per workgroup) hold 64, which lets
+// two workgroups keep four waves on every SIMD.
+template <int WM_, int WN_> struct Layout {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = KBM / WM, WAVES_N = KBN / WN;
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int MI = WM / 16, NJ = WN / 16;
+  static constexpr int EPT = KBM * KBK / NT;     // elements per thread per operand per stage
+  static constexpr int WPE = NW / 2;             // waves per SIMD with two workgroups per CU
+};
+
+// Which EPT elements of a 128 x 16 (A) or 16 x 128 (B) stage one thread moves.
 // When the 128-long index x (m for A, n for B) is the contiguous one, lanes
-// walk x and each thread takes k = k0, k0+2, ...; otherwise lanes walk k and
-// each thread takes x = x0, x0+16, ....  Element p sits at intra-tile offset
-// lin + p*step of the operand and at LDS index lds + p*lds_step.
+// walk x and each thread takes k = k0, k0+NT/128, ...; otherwise lanes walk k
+// and each thread takes x = x0, x0+NT/16, ....  Element p sits at intra-tile
+// offset lin + p*step of the operand and at LDS index lds + p*lds_step.
 struct ThreadMap {
   int32_t lin, step;
   int32_t x, dx, k, dk;
   int32_t lds, lds_step;
 };
 
+template <int NT>
 __device__ __forceinline__ ThreadMap thread_map(bool x_contig, int32_t ld, int tid, int lds_row) {
   ThreadMap t;
   if (x_contig) {
     const int x = tid & 127, k = tid >> 7;
-    t.lin = x + k * ld; t.step = 2 * ld;
-    t.x = x; t.dx = 0; t.k = k; t.dk = 2;
-    t.lds = k * lds_row + x; t.lds_step = 2 * lds_row;
+    constexpr int dk = NT / 128;
+    t.lin = x + k * ld; t.step = dk * ld;
+    t.x = x; t.dx = 0; t.k = k; t.dk = dk;
+    t.lds = k * lds_row + x; t.lds_step = dk * lds_row;
   } else {
     const int k = tid & 15, x = tid >> 4;
-    t.lin = k + x * ld; t.step = 16 * ld;
-    t.x = x; t.dx = 16; t.k = k; t.dk = 0;
-    t.lds = k * lds_row + x; t.lds_step = 16;
+    constexpr int dx = NT / 16;
+    t.lin = k + x * ld; t.step = dx * ld;
+    t.x = x; t.dx = dx; t.k = k; t.dk = 0;
+    t.lds = k * lds_row + x; t.lds_step = dx;
   }
   return t;
 }
@@ -86,7 +105,7 @@ struct Seg {
   ThreadMap ma, mb;
 };
 
-template <typename T>
+template <typename T, int NT>
 __device__ __forceinline__ Seg<T> make_seg(const DevSeg &g, const Bases &bases, int tid) {
   Seg<T> s;
   s.a = static_cast<const T *>(bases.p[g.a.base]) + g.a.off;
@@ -96,86 +115,135 @@ __device__ __forceinline__ Seg<T> make_seg(const DevSeg &g, const Bases &bases, 
   s.K = g.K;
   s.a_xc = g.a.trans == 0;   // A(m,k) = A[m + k*lda]
   s.b_xc = g.b.trans == 1;   // B(k,n) = B[n + k*ldb]
-  s.ma = thread_map(s.a_xc, s.lda, tid, LDS_A);
-  s.mb = thread_map(s.b_xc, s.ldb, tid, LDS_B);
+  s.ma = thread_map<NT>(s.a_xc, s.lda, tid, LDS_A);
+  s.mb = thread_map<NT>(s.b_xc, s.ldb, tid, LDS_B);
   return s;
 }
 
-template <typename T>
+// Operand loads are raw buffer loads from a resource whose base is the tile
+// origin: an element outside the operand gets the offset 2^31, which lies past
+// the resource's 2^31 - 1 byte range, and the hardware returns zero for it
+// without touching memory.  Valid elements are at byte offsets below 2^31
+// (leading dimensions are below 2^21), so no select or branch follows the loads
+// and all eight of a thread's loads can be in flight together.
+template <typename T> struct BufLoad;
+template <> struct BufLoad<double> {
+  static __device__ __forceinline__ double ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+};
+template <> struct BufLoad<float> {
+  static __device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+constexpr int BUF_WORD3 = 0x00020000;   // raw (untyped) buffer access on CDNA
+
+template <typename T, int EPT>
 __device__ __forceinline__ void load_op(const T *base, int64_t x0, int64_t k0, int32_t ld, bool xc, int xrem,
-                                        int krem, const ThreadMap &m, T (&r)[8]) {
+                                        int krem, const ThreadMap &m, T (&r)[EPT]) {
   const T *p0 = xc ? base + x0 + k0 * ld : base + k0 + x0 * ld;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(p0), (short)0, 0x7fffffff, BUF_WORD3);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
+  for (int p = 0; p < EPT; ++p) {
     const int x = m.x + p * m.dx, k = m.k + p * m.dk;
-    r[p] = (x < xrem && k < krem) ? p0[m.lin + p * m.step] : T(0);
+    const bool ok = x < xrem && k < krem;
+    const uint32_t off = ok ? (uint32_t)(m.lin + p * m.step) * (uint32_t)sizeof(T) : OOB_OFFSET;
+    r[p] = BufLoad<T>::ld(rs, off);
   }
 }
 
-template <typename T>
+template <typename T, int EPT>
 __device__ __forceinline__ void load_stage(const Seg<T> &s, int k0, int m0, int n0, int M, int N,
-                                           T (&ra)[8], T (&rb)[8]) {
+                                           T (&ra)[EPT], T (&rb)[EPT]) {
   const int krem = s.K - k0;
-  load_op<T>(s.a, m0, k0, s.lda, s.a_xc, M - m0, krem, s.ma, ra);
-  load_op<T>(s.b, n0, k0, s.ldb, s.b_xc, N - n0, krem, s.mb, rb);
+  load_op<T, EPT>(s.a, m0, k0, s.lda, s.a_xc, M - m0, krem, s.ma, ra);
+  load_op<T, EPT>(s.b, n0, k0, s.ldb, s.b_xc, N - n0, krem, s.mb, rb);
 }
 
-template <typename T>
-__device__ __forceinline__ void store_stage(const Seg<T> &s, const T (&ra)[8], const T (&rb)[8], T *As, T *Bs) {
+template <typename T, int EPT>
+__device__ __forceinline__ void store_stage(const Seg<T> &s, const T (&ra)[EPT], const T (&rb)[EPT], T *As, T *Bs) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) As[s.ma.lds + p * s.ma.lds_step] = ra[p];
+  for (int p = 0; p < EPT; ++p) As[s.ma.lds + p * s.ma.lds_step] = ra[p];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) Bs[s.mb.lds + p * s.mb.lds_step] = rb[p];
+  for (int p = 0; p < EPT; ++p) Bs[s.mb.lds + p * s.mb.lds_step] = rb[p];
 }
 
-template <typename T>
+template <typename T, typename L>
 __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, const int64_t *coltab,
-                                           const Bases &bases, T alpha, T beta) {
+                                           const Bases &bases, T alpha, T beta, T cscale) {
   typedef typename Mfma<T>::v4 v4;
+  constexpr int MI = L::MI, NJ = L::NJ, EPT = L::EPT;
   __shared__ T As[2][KBK * LDS_A];
   __shared__ T Bs[2][KBK * LDS_B];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int wm = (wave % L::WAVES_M) * L::WM, wn = (wave / L::WAVES_M) * L::WN;
   const int arow = Mfma<T>::arow(lane & 15);
   const int M = t.M, N = t.N;
 
-  v4 acc[4][4];
+  // C <- alpha*(acc + (beta/alpha)*C): when the host found beta/alpha finite the
+  // old C is read into the accumulators before the K loop (its latency hides
+  // behind the first loads) and the epilogue only stores.
+  T *C = static_cast<T *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
+  const bool fin = t.final_ != 0;
+  const bool vec = (t.flags & TASK_VEC) && (reinterpret_cast<uintptr_t>(C) % (4 * sizeof(T)) == 0);
+  const bool preload = fin && cscale != T(0);
+  const bool rd = fin && beta != T(0) && !preload;
+  v4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn + 16 * j + (lane & 15);
+    const int64_t col = (!preload || n >= N) ? 0 : (t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n]);
+    const T *cp = C + col;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4{0, 0, 0, 0};
+    for (int i = 0; i < MI; ++i) {
+      acc[i][j] = v4{0, 0, 0, 0};
+      if (!preload || n >= N) continue;
+      const int mb = m0 + wm + 16 * i + 4 * (lane >> 4);
+      if (vec && mb + 3 < M) {
+        acc[i][j] = cscale * *reinterpret_cast<const v4 *>(cp + mb);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (mb + v < M) acc[i][j][v] = cscale * cp[mb + v];
+      }
+    }
+  }
 
   const int nseg = t.nseg;
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {   // constant segment index: no dynamic indexing into the task
     if (sg >= nseg) break;
-    const Seg<T> s = make_seg<T>(t.seg[sg], bases, tid);
+    const Seg<T> s = make_seg<T, L::NT>(t.seg[sg], bases, tid);
     const int nst = (s.K + KBK - 1) / KBK;
-    T ra[8], rb[8];
-    load_stage<T>(s, 0, m0, n0, M, N, ra, rb);
+    T ra[EPT], rb[EPT];
+    load_stage<T, EPT>(s, 0, m0, n0, M, N, ra, rb);
     __syncthreads();   // the previous segment's last reads of buffer 0 are done
-    store_stage<T>(s, ra, rb, As[0], Bs[0]);
+    store_stage<T, EPT>(s, ra, rb, As[0], Bs[0]);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
       const bool more = st + 1 < nst;
-      if (more) load_stage<T>(s, (st + 1) * KBK, m0, n0, M, N, ra, rb);
+      if (more) load_stage<T, EPT>(s, (st + 1) * KBK, m0, n0, M, N, ra, rb);
       const T *Ab = As[st & 1];
       const T *Bb = Bs[st & 1];
 #pragma unroll
       for (int kq = 0; kq < KBK / 4; ++kq) {
         const int kr = kq * 4 + (lane >> 4);
-        T a[4], b[4];
+        T a[MI], b[NJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = Ab[kr * LDS_A + wm + 16 * i + arow];
+        for (int i = 0; i < MI; ++i) a[i] = Ab[kr * LDS_A + wm + 16 * i + arow];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bb[kr * LDS_B + wn + 16 * j + (lane & 15)];
+        for (int j = 0; j < NJ; ++j) b[j] = Bb[kr * LDS_B + wn + 16 * j + (lane & 15)];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
       }
-      if (more) store_stage<T>(s, ra, rb, As[(st + 1) & 1], Bs[(st + 1) & 1]);
+      if (more) store_stage<T, EPT>(s, ra, rb, As[(st + 1) & 1], Bs[(st + 1) & 1]);
       __syncthreads();
     }
   }
@@ -183,18 +251,14 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   // epilogue: lane holds rows 4*(lane/16)+v (v = 0..3), column lane%16 of each
   // 16x16 tile; when the column start is 4-element aligned those four rows go
   // out as one vector access.
-  T *C = static_cast<T *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
-  const bool fin = t.final_ != 0;
-  const bool rd = fin && beta != T(0);
-  const bool vec = (t.flags & TASK_VEC) && (reinterpret_cast<uintptr_t>(C) % (4 * sizeof(T)) == 0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn + 16 * j + (lane & 15);
     if (n >= N) continue;
     const int64_t col = t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n];
     T *cp = C + col;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       const int mb = m0 + wm + 16 * i + 4 * (lane >> 4);
       v4 x = acc[i][j];
       if (fin) x = alpha * x;
@@ -217,23 +281,23 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   }
 }
 
-template <typename T, int STAGE>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int STAGE, typename L>
+__global__ __launch_bounds__(L::NT) __attribute__((amdgpu_waves_per_eu(L::WPE)))
 void grouped_gemm_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
-                         const int64_t *__restrict__ coltab, Bases bases, T alpha, T beta) {
+                         const int64_t *__restrict__ coltab, Bases bases, T alpha, T beta, T cscale) {
   const DevTile e = tiles[blockIdx.x];
   if (e.task < 0) return;
   const DevTask t = tasks[e.task];
   const bool fin = t.final_ != 0;
-  gemm_block<T>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0));
+  gemm_block<T, L>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0), fin ? cscale : T(0));
 }
 
 // Single task given by value; blockIdx.x walks the output blocks so that each
 // XCD (workgroups are dealt to the 8 XCDs round-robin) takes a contiguous run
 // of block indices, ordered in bands of 8 block rows for L2 reuse.
-template <typename T>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
-void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, int mt, int nt, int per) {
+template <typename T, typename L>
+__global__ __launch_bounds__(L::NT) __attribute__((amdgpu_waves_per_eu(L::WPE)))
+void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int mt, int nt, int per) {
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * per + (bid >> 3);
   if (logical >= mt * nt) return;
@@ -244,7 +308,7 @@ void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, int mt, int nt,
   const int in = logical - group * band * nt;
   const int mtile = first_m + in % rows;
   const int ntile = in / rows;
-  gemm_block<T>(t, mtile * KBM, ntile * KBN, nullptr, bases, alpha, beta);
+  gemm_block<T, L>(t, mtile * KBM, ntile * KBN, nullptr, bases, alpha, beta, cscale);
 }
 
 template <typename T>
@@ -258,16 +322,46 @@ __global__ void scale_kernel(T *C, int64_t m, int64_t n, int64_t ldc, T beta) {
   }
 }
 
+// beta/alpha when C can be pre-scaled into the accumulators, else 0 (then the
+// epilogue reads C).
 template <typename T>
-void launch_grouped_t(int stage, dim3 grid, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
-                      const int64_t *coltab, const Bases &bases, T alpha, T beta) {
-  dim3 block(NTHR);
+T preload_scale(double alpha, double beta) {
+  if (beta == 0.0 || alpha == 0.0) return T(0);
+  const double r = beta / alpha;
+  const double lim = sizeof(T) == 8 ? 1e300 : 1e30;
+  return (r == r && r < lim && r > -lim) ? T(r) : T(0);
+}
+
+// 64 x 32 waves (8 per workgroup, four waves per SIMD with two workgroups per
+// CU) measured faster than 64 x 64 waves at every K on this chip: more waves
+// cover the barrier and memory phases of a workgroup.
+using WaveLayout = Layout<64, 32>;
+
+template <typename T, typename L>
+void launch_grouped_l(int stage, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                      const int64_t *coltab, const Bases &bases, T a, T b, T c) {
+  dim3 grid(n), block(L::NT);
   if (stage == 1)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 1>), grid, block, 0, s, tasks, tiles, coltab, bases, alpha, beta);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, 1, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
   else if (stage == 2)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 2>), grid, block, 0, s, tasks, tiles, coltab, bases, alpha, beta);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, 2, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 3>), grid, block, 0, s, tasks, tiles, coltab, bases, alpha, beta);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, 3, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+}
+
+template <typename T>
+void launch_grouped_t(int stage, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                      const int64_t *coltab, const Bases &bases, double alpha, double beta) {
+  const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
+  launch_grouped_l<T, WaveLayout>(stage, n, s, tasks, tiles, coltab, bases, a, b, c);
+}
+
+template <typename T>
+void launch_single_t(unsigned n, hipStream_t s, const DevTask &task, const Bases &bases, double alpha,
+                     double beta, int mt, int nt, int per) {
+  const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
+  hipLaunchKernelGGL((single_gemm_kernel<T, WaveLayout>), dim3(n), dim3(WaveLayout::NT), 0, s, task, bases, a, b,
+                     c, mt, nt, per);
 }
 
 }  // namespace
@@ -276,11 +370,10 @@ int launch_grouped(tlr_dtype dt, int stage, const DevTask *tasks, const DevTile 
                    const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
   if (n_tiles <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)n_tiles);
   if (dt == TLR_F64)
-    launch_grouped_t<double>(stage, grid, s, tasks, tiles, coltab, bases, alpha, beta);
+    launch_grouped_t<double>(stage, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   else
-    launch_grouped_t<float>(stage, grid, s, tasks, tiles, coltab, bases, (float)alpha, (float)beta);
+    launch_grouped_t<float>(stage, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   return (int)hipGetLastError();
 }
 
@@ -291,12 +384,10 @@ int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double 
   const int64_t n = (int64_t)mt * nt;
   const int per = (int)((n + 7) / 8);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)(per * 8)), block(NTHR);
   if (dt == TLR_F64)
-    hipLaunchKernelGGL(single_gemm_kernel<double>, grid, block, 0, s, task, bases, alpha, beta, mt, nt, per);
+    launch_single_t<double>((unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
   else
-    hipLaunchKernelGGL(single_gemm_kernel<float>, grid, block, 0, s, task, bases, (float)alpha,
-                       (float)beta, mt, nt, per);
+    launch_single_t<float>((unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
   return (int)hipGetLastError();
 }
 

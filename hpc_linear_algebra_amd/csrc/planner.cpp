@@ -436,10 +436,12 @@ static double task_exec_flops(const DevTask &d) {
   return F;
 }
 
-// Emit the workgroup table of one launch.  Stage 3 keeps neighbouring output
-// blocks on one XCD (each XCD walks a contiguous eighth of the block list, so
-// the panels they share stay in that XCD's L2), longest tasks first inside each
-// eighth; stages 1-2 are ordered longest first across the whole launch.
+// Emit the workgroup table of one launch.  Workgroups are dealt to the 8 XCDs
+// round-robin by index (index x, x+8, x+16, ... run on XCD x, each XCD in its
+// own order), so the table is built per XCD: whole tasks (all blocks of one
+// output tile stay on one XCD and share its L2) go, longest first, to the XCD
+// with the least work so far, and each XCD's list runs longest first.  Lists
+// are padded with idle entries to a common length.
 static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   if (tl.t.empty()) return;
   Launch L;
@@ -450,40 +452,38 @@ static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.useful_flops = 0;
   L.executed_flops = 0;
   const int32_t task0 = (int32_t)p.tasks.size();
-  struct Ent { int32_t task, m0, n0; int64_t cost; };
-  std::vector<Ent> ents;
+  struct TaskCost { int32_t t; int64_t per_block, blocks; };
+  std::vector<TaskCost> order;
   for (size_t t = 0; t < tl.t.size(); ++t) {
     const DevTask &d = tl.t[t];
     L.useful_flops += tl.useful[t];
     L.executed_flops += task_exec_flops(d);
     int64_t K = 0;
     for (int s = 0; s < d.nseg; ++s) K += d.seg[s].K;
-    for (int64_t n0 = 0; n0 < d.N; n0 += BN)
-      for (int64_t m0 = 0; m0 < d.M; m0 += BM)
-        ents.push_back({task0 + (int32_t)t, (int32_t)m0, (int32_t)n0, K + 32});
+    const int64_t blocks = ceil_div(d.M, BM) * ceil_div(d.N, BN);
+    // one block costs its K steps plus a fixed share for the C update
+    order.push_back({(int32_t)t, K + 32, blocks});
     p.tasks.push_back(d);
   }
-  const int64_t n = (int64_t)ents.size();
-  const int64_t per = ceil_div(n, NUM_XCD);
-  const int64_t padded = per * NUM_XCD;
-  std::vector<DevTile> tab((size_t)padded);
-  for (auto &x : tab) { x.task = -1; x.m0 = 0; x.n0 = 0; x.pad = 0; }
-  auto by_cost = [](const Ent &a, const Ent &b) { return a.cost > b.cost; };
-  if (stage == 3) {
-    for (int x = 0; x < NUM_XCD; ++x) {
-      int64_t lo = std::min(n, x * per), hi = std::min(n, (x + 1) * per);
-      std::stable_sort(ents.begin() + lo, ents.begin() + hi, by_cost);
-      for (int64_t t = lo; t < hi; ++t) {
-        int64_t bid = (t - lo) * NUM_XCD + x;
-        tab[(size_t)bid] = DevTile{ents[t].task, ents[t].m0, ents[t].n0, 0};
-      }
-    }
-  } else {
-    std::stable_sort(ents.begin(), ents.end(), by_cost);
-    for (int64_t t = 0; t < n; ++t) tab[(size_t)t] = DevTile{ents[t].task, ents[t].m0, ents[t].n0, 0};
+  std::stable_sort(order.begin(), order.end(),
+                   [](const TaskCost &a, const TaskCost &b) { return a.per_block > b.per_block; });
+  std::vector<std::vector<DevTile>> xl(NUM_XCD);
+  std::vector<int64_t> load(NUM_XCD, 0);
+  for (const TaskCost &c : order) {
+    int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += c.per_block * c.blocks;
+    const DevTask &d = tl.t[c.t];
+    for (int64_t m0 = 0; m0 < d.M; m0 += BM)
+      for (int64_t n0 = 0; n0 < d.N; n0 += BN)
+        xl[x].push_back(DevTile{task0 + c.t, (int32_t)m0, (int32_t)n0, 0});
   }
+  size_t per = 0;
+  for (auto &v : xl) per = std::max(per, v.size());
+  std::vector<DevTile> tab(per * NUM_XCD, DevTile{-1, 0, 0, 0});
+  for (int x = 0; x < NUM_XCD; ++x)
+    for (size_t t = 0; t < xl[x].size(); ++t) tab[t * NUM_XCD + x] = xl[x][t];
   L.tile_off = (int64_t)p.tiles.size();
-  L.n_tiles = padded;
+  L.n_tiles = (int64_t)tab.size();
   p.tiles.insert(p.tiles.end(), tab.begin(), tab.end());
   p.launches.push_back(L);
   p.groups[group].launches.push_back((int)p.launches.size() - 1);
@@ -767,8 +767,8 @@ static BufSizes buffer_sizes(const Plan &p) {
 
 static bool operand_ok(const DevOperand &o, int64_t rows, int64_t cols, bool is_a, const BufSizes &z) {
   // is_a: (rows, cols) = (M, K); else (K, N).  trans picks which index is contiguous.
-  // the kernel forms intra-tile offsets up to 127*ld in 32 bits
-  if (o.base >= NUM_BASES || o.off < 0 || o.ld < 1 || o.ld >= (1 << 24)) return false;
+  // the kernel forms intra-tile byte offsets up to (127*ld + 15)*8, below 2^31
+  if (o.base >= NUM_BASES || o.off < 0 || o.ld < 1 || o.ld >= (1 << 21)) return false;
   if (rows == 0 || cols == 0) return true;
   const bool first_contig = (o.trans == 0);   // A: M contiguous / B: K contiguous
   int64_t a = first_contig ? rows : cols, c = first_contig ? cols : rows;
@@ -928,7 +928,7 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
     p->n = opB == TLR_OP_N ? dense_cols : dense_rows;
     if (kb != p->k) return fail(TLR_ERR_INVALID_ARG, "op(A) columns != op(B) rows");
     if (ldb < std::max<int64_t>(1, dense_rows)) return fail(TLR_ERR_INVALID_ARG, "ldb < rows of B");
-    if (ldb > std::numeric_limits<int32_t>::max()) return fail(TLR_ERR_INVALID_ARG, "ldb too large");
+    if (ldb >= (int64_t)1 << 21) return fail(TLR_ERR_INVALID_ARG, "ldb must be below 2^21");
     p->ldb = ldb;
     p->dense_rows = dense_rows;
     p->dense_cols = dense_cols;

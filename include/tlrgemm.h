@@ -125,7 +125,7 @@ typedef struct {
  *   opA, A      op and structure of A (required).
  *   opB, B      op and structure of B; B == NULL selects a dense B of
  *               dense_rows x dense_cols (stored, column-major, leading dim ldb).
- *   ldb         leading dimension of a dense B (ignored for a TLR B).
+ *   ldb         leading dimension of a dense B (ignored for a TLR B; < 2^21).
  *   ldc         leading dimension of C (>= m).
  *   workspace_budget  bytes of device workspace execute may use; 0 means no limit.
  *   n_streams   streams execute will be given (>= 1); boundary regions of C
@@ -250,7 +250,7 @@ tlr_status tlr_plan_profile_read(tlr_plan *p, double *stage_ms, double *launch_m
  * the same-chip dense reference the TLR product is compared with ("Results":
  * dense-GEMM time scaled by the ratio of executed flops).
  *   op(A) is m x k, op(B) is k x n, C is m x n; lda/ldb/ldc >= rows of the
- *   stored matrices.  beta == 0 never reads C.  No workspace.
+ *   stored matrices, lda and ldb < 2^21.  beta == 0 never reads C.  No workspace.
  * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_HIP.
  */
 tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n,
