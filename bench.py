@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-GEMM reference")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pipeline", type=int, default=1,
+                    help="1: rectangles alternate between two workspace arenas on two streams")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -177,14 +179,18 @@ def main():
     A, B, C_in = config_inputs(WORKLOAD)
     dA, dB = DeviceTLR(A), DeviceTLR(B)
     Cd = dense_to_device(C_in)
-    g = TLRGemm(dtype, cfg["opA"], dA, cfg["opB"], dB, ldc=N, budget=cfg["budget"] or 0, n_streams=1)
+    n_streams = 2 if args.pipeline else 1
+    g = TLRGemm(dtype, cfg["opA"], dA, cfg["opB"], dB, ldc=N, budget=cfg["budget"] or 0, n_streams=n_streams,
+                flags=T.TLR_PLAN_PIPELINE if args.pipeline else 0)
     info = g.info
     launches = g.launches()
     stream = torch.cuda.current_stream()
+    side = [torch.cuda.Stream() for _ in range(n_streams - 1)]
+    streams = [stream.cuda_stream] + [x.cuda_stream for x in side]
     log(f"bench: plan runs={info['runs']} launches={info['launches']} ws={info['workspace_bytes']/2**30:.2f} GiB "
         f"useful={info['useful_flops']:.4e}")
     for _ in range(args.warmup):
-        g(cfg["alpha"], dA, dB, cfg["beta"], Cd)
+        g(cfg["alpha"], dA, dB, cfg["beta"], Cd, streams)
     torch.cuda.synchronize()
     # timed region: K steps, HIP events around every launch on its own stream
     T.tlr_plan_profile(g.plan, args.steps)
@@ -193,7 +199,7 @@ def main():
     w0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        g(cfg["alpha"], dA, dB, cfg["beta"], Cd)
+        g(cfg["alpha"], dA, dB, cfg["beta"], Cd, streams)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -255,14 +261,16 @@ def main():
         log("bench: CPU oracle baseline on a bounded sample")
         cpu = cpu_baseline(cfg, A, B, C_in, F, args.cpu_seconds)
 
-    order = "left" if T.tlr_plan_rect(g.plan, 0)["order"] == T.TLR_ORDER_LEFT else "right"
+    order = ",".join("left" if T.tlr_plan_rect(g.plan, r)["order"] == T.TLR_ORDER_LEFT else "right"
+                     for r in range(info["runs"]))
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": cfg["name"], "N": N, "b": cfg["b"], "opA": cfg["opA"], "opB": cfg["opB"],
                    "alpha": cfg["alpha"], "beta": cfg["beta"], "useful_flops": F, "order": order,
-                   "runs": info["runs"], "workspace_GiB": round(info["workspace_bytes"] / 2 ** 30, 3)},
+                   "runs": info["runs"], "streams": n_streams, "pipelined": bool(args.pipeline),
+                   "workspace_GiB": round(info["workspace_bytes"] / 2 ** 30, 3)},
         "roofline": roofline,
         "path_roofline": {"bound": "mfma" if roof >= peak else "hbm", "achieved": round(value, 3),
                           "roof": round(roof, 2), "unit": "TFLOP/s", "frac": round(value / roof, 4),

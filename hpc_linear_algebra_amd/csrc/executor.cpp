@@ -24,6 +24,7 @@ static void destroy_events(std::vector<void *> &ev) {
 
 void plan_release_device(Plan *p) {
   destroy_events(p->join_events);
+  destroy_events(p->dep_events);
   destroy_events(p->prof_events);
   if (p->fork_event) {
     (void)hipEventDestroy(static_cast<hipEvent_t>(p->fork_event));
@@ -55,6 +56,13 @@ tlr_status plan_bind(Plan *p, void *dev, size_t bytes, void *stream) {
     hipEvent_t je;
     HIP_TRY(hipEventCreateWithFlags(&je, hipEventDisableTiming));
     p->join_events.push_back(je);
+  }
+  for (size_t l = 0; l < p->launches.size(); ++l) {
+    hipEvent_t de = nullptr;
+    bool awaited = false;
+    for (const Launch &L : p->launches) awaited = awaited || L.wait_launch == (int)l;
+    if (awaited) HIP_TRY(hipEventCreateWithFlags(&de, hipEventDisableTiming));
+    p->dep_events.push_back(de);
   }
   p->device = devno;
   p->dev_desc = dev;
@@ -181,10 +189,15 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
     hipStream_t sg = stream_of((int)g);
     for (int l : p->groups[g].launches) {
       const Launch &L = p->launches[l];
+      if (L.wait_launch >= 0) {
+        hipStream_t sw = stream_of(p->launches[L.wait_launch].group);
+        if (sw != sg) HIP_TRY(hipStreamWaitEvent(sg, static_cast<hipEvent_t>(p->dep_events[L.wait_launch]), 0));
+      }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
       int e = launch_grouped(p->dt, L.stage, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases, alpha, beta, sg);
       if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
       if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));
+      if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sg));
     }
   }
   for (size_t g = 0; g < p->groups.size(); ++g) {

@@ -316,10 +316,56 @@ static std::vector<Region> make_regions(const Plan &p, bool split) {
   return regs;
 }
 
+// Rectangle pipelining: the schedule of one arena's budget, rectangles dealt
+// alternately to two groups (streams 0 and 1) with an arena each.
+static tlr_status schedule_pipelined(Plan &p, const Sums &s) {
+  const Region whole{0, p.A.qr, 0, (int)p.ns.size()};
+  size_t per_arena;
+  if (p.budget) {
+    per_arena = p.budget / 2 / WS_ALIGN * WS_ALIGN;
+  } else {
+    // no limit: the smallest arena for which C splits into at most 4 rectangles
+    std::vector<Rect> rr;
+    size_t hi = min_ws(p, s, whole.i0, whole.i1, whole.j0, whole.j1), lo = 0;
+    while (hi - lo > WS_ALIGN) {
+      size_t mid = lo + (hi - lo) / 2;
+      rr.clear();
+      if (schedule_region(p, s, whole, mid, 0, rr) == TLR_OK && rr.size() <= 4) hi = mid;
+      else lo = mid;
+    }
+    per_arena = hi;
+  }
+  std::vector<Rect> rr;
+  tlr_status st = schedule_region(p, s, whole, per_arena, 0, rr);
+  if (st != TLR_OK) return st;
+  p.rects = rr;
+  for (int g = 0; g < 2; ++g) {
+    Group G;
+    G.stream = g;
+    size_t mx = 0;
+    for (size_t r = g; r < p.rects.size(); r += 2) {
+      p.rects[r].group = g;
+      G.rects.push_back((int)r);
+      mx = std::max(mx, p.rects[r].ws_bytes);
+    }
+    G.arena_bytes = align_up(mx, WS_ALIGN);
+    G.arena_off = g == 0 ? 0 : p.groups[0].arena_bytes;
+    if (!G.rects.empty()) p.groups.push_back(G);
+  }
+  p.ws_bytes = 0;
+  for (auto &G : p.groups) p.ws_bytes += G.arena_bytes;
+  set_error("");
+  return TLR_OK;
+}
+
 static tlr_status schedule(Plan &p, const Sums &s) {
   const size_t budget = p.budget ? p.budget : std::numeric_limits<size_t>::max();
   p.rects.clear();
   p.groups.clear();
+  if (p.flags & TLR_PLAN_PIPELINE) {
+    if (p.A.qr == 0 || p.ns.empty()) return TLR_OK;
+    return schedule_pipelined(p, s);
+  }
   const bool concurrent = p.n_streams >= 2 && !(p.flags & TLR_PLAN_NO_REGIONS);
   std::vector<Region> regs = make_regions(p, concurrent);
   if (regs.empty()) return TLR_OK;
@@ -448,6 +494,7 @@ static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.stage = stage;
   L.group = group;
   L.rect = rect;
+  L.wait_launch = -1;
   L.n_tasks = (int64_t)tl.t.size();
   L.useful_flops = 0;
   L.executed_flops = 0;
@@ -908,8 +955,10 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   if (n_streams < 1) return fail(TLR_ERR_INVALID_ARG, "n_streams must be >= 1");
   if ((flags & TLR_PLAN_FORCE_RIGHT) && (flags & TLR_PLAN_FORCE_LEFT))
     return fail(TLR_ERR_INVALID_ARG, "cannot force both orders");
-  if (flags & ~(TLR_PLAN_FORCE_RIGHT | TLR_PLAN_FORCE_LEFT | TLR_PLAN_NO_REGIONS | TLR_PLAN_VALIDATE))
+  if (flags & ~(TLR_PLAN_FORCE_RIGHT | TLR_PLAN_FORCE_LEFT | TLR_PLAN_NO_REGIONS | TLR_PLAN_VALIDATE | TLR_PLAN_PIPELINE))
     return fail(TLR_ERR_INVALID_ARG, "unknown flag bits");
+  if ((flags & TLR_PLAN_PIPELINE) && n_streams < 2)
+    return fail(TLR_ERR_INVALID_ARG, "pipelining needs n_streams >= 2");
   p->dt = dt;
   p->es = dt == TLR_F64 ? 8 : 4;
   p->budget = budget;
@@ -984,6 +1033,15 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
     else
       for (int n = 0; n < d.N && v; ++n) v = p->coltab[d.ctab + n] % 4 == 0;
     d.flags = v ? TASK_VEC : 0;
+  }
+  // pipelining: the second stream starts once the first rectangle's stage 2
+  // (its last launch before the final update) is done, so that its first
+  // stages run beside that final update
+  if ((flags & TLR_PLAN_PIPELINE) && p->groups.size() == 2 && !p->groups[1].launches.empty()) {
+    int dep = -1;
+    for (int l : p->groups[0].launches)
+      if (p->launches[l].rect == p->groups[0].rects[0] && p->launches[l].stage < 3) dep = l;
+    p->launches[p->groups[1].launches[0]].wait_launch = dep;
   }
   p->executed_flops = 0;
   for (auto &L : p->launches) p->executed_flops += L.executed_flops;

@@ -43,6 +43,7 @@ struct Launch {
   int stage;         // 1, 2, 3
   int group;
   int rect;
+  int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int64_t tile_off;  // first DevTile of the launch in the tile table
   int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)
   int64_t n_tasks;
@@ -88,6 +89,7 @@ struct Plan {
   void *dev_desc = nullptr;
   int device = -1;
   std::vector<void *> join_events;   // hipEvent_t, one per group
+  std::vector<void *> dep_events;    // hipEvent_t, one per launch (recorded only when awaited)
   void *fork_event = nullptr;
   int prof_max = 0, prof_count = 0;
   std::vector<void *> prof_events;   // 2 per launch per execute + 2 per execute (whole)

@@ -77,6 +77,8 @@ typedef enum { TLR_ORDER_RIGHT = 0, TLR_ORDER_LEFT = 1 } tlr_order;
 #define TLR_PLAN_FORCE_LEFT  0x2u  /* every rectangle uses (U S) Z^T (TLR x TLR only) */
 #define TLR_PLAN_NO_REGIONS  0x4u  /* do not split boundary regions onto their own streams */
 #define TLR_PLAN_VALIDATE    0x8u  /* also run the exhaustive descriptor self-check (slow; for tests) */
+#define TLR_PLAN_PIPELINE    0x10u /* two arenas on two streams: stages 1-2 of one rectangle run beside
+                                      stage 3 of the previous one (needs n_streams >= 2) */
 
 /* Structure of one stored TLR operand (host data; no device pointers). */
 typedef struct {
@@ -130,6 +132,13 @@ typedef struct {
  *   workspace_budget  bytes of device workspace execute may use; 0 means no limit.
  *   n_streams   streams execute will be given (>= 1); boundary regions of C
  *               (last tile row / column smaller than b) run concurrently when >= 2.
+ *               With TLR_PLAN_PIPELINE the rectangles alternate between two
+ *               workspace arenas and streams 0 and 1 ("Association order and
+ *               workspace": rectangles write disjoint parts of C, so with two
+ *               arenas and two streams the first stages of one rectangle can
+ *               overlap the final GEMMs of the previous one, at twice the
+ *               workspace); the budget then covers both arenas, and with no
+ *               budget each arena is sized for a quarter of C.
  *   flags       TLR_PLAN_* bits.
  *   plan_out    receives a new plan (free with tlr_plan_destroy).
  * Every plan is checked before it is returned: each operand and output range a

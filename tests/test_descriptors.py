@@ -79,3 +79,20 @@ def test_boundary_workload_structure_validates():
         w = T.tlr_gemm_workspace_bytes("f32", "N", A, "N", B, n_streams=ns, runs=8)
         p = T.tlr_gemm_analyze("f32", "N", A, "N", B, ldc=N, workspace_budget=w, n_streams=ns, flags=V)
         assert T.tlr_plan_info(p)["runs"] >= 2
+
+
+def test_pipelined_plans_validate():
+    rng = np.random.default_rng(9)
+    for n, b in ((640, 64), (1000, 128), (513, 32)):
+        sz = tile_sizes(n, b)
+        RA, RB = _ranks(rng, len(sz), sz, True, 1, 24), _ranks(rng, len(sz), sz, True, 1, 24)
+        A, B = T.Shape(n, n, b, RA, True), T.Shape(n, n, b, RB, True)
+        for budget in (0, 2_000_000):
+            p = T.tlr_gemm_analyze("f64", "T", A, "N", B, ldc=n, workspace_budget=budget, n_streams=2,
+                                   flags=T.TLR_PLAN_PIPELINE | V)
+            info = T.tlr_plan_info(p)
+            assert info["groups"] == 2 and info["runs"] >= 2
+            if budget:
+                assert info["workspace_bytes"] <= budget
+    with pytest.raises(T.TLRError):
+        T.tlr_gemm_analyze("f64", "N", A, "N", B, ldc=n, n_streams=1, flags=T.TLR_PLAN_PIPELINE)

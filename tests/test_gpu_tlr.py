@@ -142,3 +142,16 @@ def test_single_tile_and_full_rank():
     check_tlr(A, B, "T", "N", 1.0, 0.5, C)
     A, B, C = _pair(17, 96, 32, lo=32, hi=32)               # every tile full rank
     check_tlr(A, B, "N", "N", 1.0, 0.5, C, flags=F_LEFT)
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_pipelined_rectangles_two_streams(dtype):
+    # rectangles alternate between two arenas on two streams; the second stream
+    # starts after the first rectangle's right product
+    A, B, C = _pair(21, 700, 64, dtype=dtype, lo=1, hi=30)
+    for budget in (0, 3_000_000):
+        got, g = run_tlr(A, B, "T", "N", 1.0, 1.0, C, budget=budget, n_streams=2, flags=0x10,
+                         return_plan=True)
+        assert g.info["groups"] == 2 and g.info["runs"] >= 2
+        ref = reference.gemm_reference(1.0, "T", A, "N", B, 1.0, C)
+        assert reference.rel_fro(got, ref) <= TOL[dtype]
