@@ -10,6 +10,13 @@
 
 namespace tlr {
 
+static bool bases_pair_aligned(const Bases &b, int es) {
+  for (const void *x : b.p)
+    if (reinterpret_cast<uintptr_t>(x) % (uintptr_t)(2 * es) != 0) return false;
+  return true;
+}
+
+
 #define HIP_TRY(expr)                                                                     \
   do {                                                                                    \
     hipError_t e_ = (expr);                                                               \
@@ -158,6 +165,9 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
   bases.p[BASE_B_DENSE] = B_dense;
   bases.p[BASE_WS] = ws;
   bases.p[BASE_C] = C;
+  // the pair load modes assume every buffer aligned to a pair of elements;
+  // otherwise each launch runs its whole table in single-element mode
+  const bool pairs_ok = bases_pair_aligned(bases, p->es);
   const char *dd = static_cast<const char *>(p->dev_desc);
   const DevTask *tasks = reinterpret_cast<const DevTask *>(dd + p->task_bytes_off);
   const DevTile *tiles = reinterpret_cast<const DevTile *>(dd + p->tile_bytes_off);
@@ -194,8 +204,17 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
         if (sw != sg) HIP_TRY(hipStreamWaitEvent(sg, static_cast<hipEvent_t>(p->dep_events[L.wait_launch]), 0));
       }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
-      int e = launch_grouped(p->dt, L.stage, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases, alpha, beta, sg);
-      if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
+      if (pairs_ok) {
+        for (int m = 0; m < NUM_LOAD_MODES; ++m) {
+          int e = launch_grouped(p->dt, L.stage, m, tasks, tiles + L.tile_off + L.mode_off[m], L.mode_tiles[m],
+                                 ctab, bases, alpha, beta, sg);
+          if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
+        }
+      } else {
+        int e = launch_grouped(p->dt, L.stage, LOAD_SINGLE, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases,
+                               alpha, beta, sg);
+        if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
+      }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));
       if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sg));
     }
@@ -262,7 +281,8 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
   bases.p[BASE_A_OUTER] = A;
   bases.p[BASE_B_OUTER] = B;
   bases.p[BASE_C] = C;
-  int e = launch_single(dt, t, bases, alpha, beta, stream);
+  const int mode = bases_pair_aligned(bases, dt == TLR_F64 ? 8 : 4) ? task_load_mode(t) : LOAD_SINGLE;
+  int e = launch_single(dt, mode, t, bases, alpha, beta, stream);
   if (e) return fail(TLR_ERR_HIP, std::string("dense GEMM launch: ") + hipGetErrorString((hipError_t)e));
   return TLR_OK;
 }

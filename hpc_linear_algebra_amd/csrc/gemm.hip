@@ -8,17 +8,20 @@
 // Layout of the descriptors: tlr_desc.h.  Each stage gets its own kernel symbol
 // so that profilers report the stages separately.
 //
-// Work split: the 128 x 128 block is shared by 4 or 8 wave64s (64 x 64 or
-// 64 x 32 per wave, MFMA tiles of 16 x 16: v_mfma_f64_16x16x4_f64 /
-// v_mfma_f32_16x16x4_f32).  K advances in stages of BK = 16, staged through LDS
-// and double-buffered: the global loads of stage s+1 are in flight while the
-// MFMAs of stage s run.  Registers are held so that two workgroups share a CU:
-// while one waits on memory (its first stage, its C update) the other keeps
-// the matrix cores busy.
+// Work split: four wave64s, 2 x 2, each owning a 64 x 64 quarter of the block
+// as 4 x 4 MFMA tiles of 16 x 16 (v_mfma_f64_16x16x4_f64 /
+// v_mfma_f32_16x16x4_f32).  K advances in stages of 16.  The A operand goes
+// from global memory straight into registers in MFMA operand order (each wave
+// loads its own 64 rows; no LDS round trip), refilled for the next stage as the
+// current stage's MFMAs release each register.  The B operand, shared by the
+// two waves of a column, is staged through a double-buffered LDS tile whose
+// global loads are in flight during the previous stage.  Registers are sized
+// for two workgroups per CU (two waves per SIMD).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tlr_plan.h"
 
@@ -26,18 +29,22 @@ namespace tlr {
 
 namespace {
 
-// LDS rows hold 145 elements: an odd stride sends the 16 k-rows that one
-// K-contiguous operand store touches to 16 different banks, and a 16-element
+// LDS rows of the B tile hold 145 elements: an odd stride sends the 16 k-rows
+// that one K-contiguous store touches to 16 different banks, and a 16-element
 // fragment read still covers each bank once.
 constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 17;
-constexpr int LDS_A = KBM + KPAD, LDS_B = KBN + KPAD;
+constexpr int LDS_B = KBN + KPAD;
+constexpr int NT = 256;               // threads per workgroup: four wave64s
+constexpr int WM = 32, WN = 128;      // per-wave block: four waves stacked along M
+constexpr int MI = 2, NJ = 8;         // 16 x 16 MFMA tiles per wave
+constexpr int EPT = KBN * KBK / NT;   // B elements per thread per stage
 
 // Lane layout of the 16x16x4 MFMAs (measured on gfx950): lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16]; accumulator element v of lane l is
 // D[row][l % 16] with row = 4*(l/16) + v for fp32 but row = l/16 + 4*v for
-// fp64.  For fp64 the A fragment is therefore read with its rows permuted by
-// arow(x) = 4*(x%4) + x/4, which makes both types leave rows 4*(l/16)+v, i.e.
-// four consecutive rows of one column, in lane l.
+// fp64.  For fp64 the A operand rows are therefore fed permuted by
+// arow(x) = 4*(x%4) + x/4, which makes both types leave MFMA rows 4*(l/16)+v
+// in lane l.
 template <typename T> struct Mfma;
 template <> struct Mfma<double> {
   typedef double v4 __attribute__((ext_vector_type(4)));
@@ -54,135 +61,252 @@ template <> struct Mfma<float> {
   static __device__ __forceinline__ int arow(int x) { return x; }
 };
 
-// Wave layout of a 128 x 128 workgroup block: WM x WN per wave (MI x NJ MFMA
-// tiles of 16 x 16), NT threads.  64 x 64 waves (4 per workgroup) hold 128
-// accumulator registers; 64 x 32 waves (8 per workgroup) hold 64, which lets
-// two workgroups keep four waves on every SIMD.
-template <int WM_, int WN_> struct Layout {
-  static constexpr int WM = WM_, WN = WN_;
-  static constexpr int WAVES_M = KBM / WM, WAVES_N = KBN / WN;
-  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-  static constexpr int MI = WM / 16, NJ = WN / 16;
-  static constexpr int EPT = KBM * KBK / NT;     // elements per thread per operand per stage
-  static constexpr int WPE = NW / 2;             // waves per SIMD with two workgroups per CU
-};
-
-// Which EPT elements of a 128 x 16 (A) or 16 x 128 (B) stage one thread moves.
-// When the 128-long index x (m for A, n for B) is the contiguous one, lanes
-// walk x and each thread takes k = k0, k0+NT/128, ...; otherwise lanes walk k
-// and each thread takes x = x0, x0+NT/16, ....  Element p sits at intra-tile
-// offset lin + p*step of the operand and at LDS index lds + p*lds_step.
-struct ThreadMap {
-  int32_t lin, step;
-  int32_t x, dx, k, dk;
-  int32_t lds, lds_step;
-};
-
-template <int NT>
-__device__ __forceinline__ ThreadMap thread_map(bool x_contig, int32_t ld, int tid, int lds_row) {
-  ThreadMap t;
-  if (x_contig) {
-    const int x = tid & 127, k = tid >> 7;
-    constexpr int dk = NT / 128;
-    t.lin = x + k * ld; t.step = dk * ld;
-    t.x = x; t.dx = 0; t.k = k; t.dk = dk;
-    t.lds = k * lds_row + x; t.lds_step = dk * lds_row;
-  } else {
-    const int k = tid & 15, x = tid >> 4;
-    constexpr int dx = NT / 16;
-    t.lin = k + x * ld; t.step = dx * ld;
-    t.x = x; t.dx = dx; t.k = k; t.dk = 0;
-    t.lds = k * lds_row + x; t.lds_step = dx;
-  }
-  return t;
-}
-
-template <typename T>
-struct Seg {
-  const T *a, *b;
-  int32_t lda, ldb, K;
-  bool a_xc, b_xc;        // the M (for A) / N (for B) index is the contiguous one
-  ThreadMap ma, mb;
-};
-
-template <typename T, int NT>
-__device__ __forceinline__ Seg<T> make_seg(const DevSeg &g, const Bases &bases, int tid) {
-  Seg<T> s;
-  s.a = static_cast<const T *>(bases.p[g.a.base]) + g.a.off;
-  s.b = static_cast<const T *>(bases.p[g.b.base]) + g.b.off;
-  s.lda = g.a.ld;
-  s.ldb = g.b.ld;
-  s.K = g.K;
-  s.a_xc = g.a.trans == 0;   // A(m,k) = A[m + k*lda]
-  s.b_xc = g.b.trans == 1;   // B(k,n) = B[n + k*ldb]
-  s.ma = thread_map<NT>(s.a_xc, s.lda, tid, LDS_A);
-  s.mb = thread_map<NT>(s.b_xc, s.ldb, tid, LDS_B);
-  return s;
-}
-
-// Operand loads are raw buffer loads from a resource whose base is the tile
-// origin: an element outside the operand gets the offset 2^31, which lies past
-// the resource's 2^31 - 1 byte range, and the hardware returns zero for it
-// without touching memory.  Valid elements are at byte offsets below 2^31
-// (leading dimensions are below 2^21), so no select or branch follows the loads
-// and all eight of a thread's loads can be in flight together.
-template <typename T> struct BufLoad;
-template <> struct BufLoad<double> {
-  static __device__ __forceinline__ double ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-  }
-};
-template <> struct BufLoad<float> {
-  static __device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-  }
-};
+// Which A row and which k a lane feeds to the MFMAs.  Lane (r, g) = (lane % 16,
+// lane / 16) supplies, to MFMA tile i at k-step q of a stage, element
+//   row(i, r) = 32*(i/2) + 2*arow(r) + i%2,   k(q, g) = 8*(q/2) + 2*g + q%2
+// of the wave's 64 x 16 slice of A, and reads the matching B element from LDS
+// row k(q, g).  Rows come in adjacent pairs (tiles 2h, 2h+1) and k in adjacent
+// pairs (steps 2p, 2p+1), so one 16-byte load fills two MFMA operands whichever
+// index of A is the contiguous one.  After the MFMAs lane (r, g) holds, for
+// column r of each 16-column tile j, the eight consecutive rows
+// 32h + 8g + t, t = 2v + e, in acc[2h + e][j][v].
+__device__ __forceinline__ int a_row(int i, int arow) { return 32 * (i >> 1) + 2 * arow + (i & 1); }
+__device__ __forceinline__ int k_of(int q, int g) { return 8 * (q >> 1) + 2 * g + (q & 1); }
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;   // raw (untyped) buffer access on CDNA
 
-template <typename T, int EPT>
-__device__ __forceinline__ void load_op(const T *base, int64_t x0, int64_t k0, int32_t ld, bool xc, int xrem,
-                                        int krem, const ThreadMap &m, T (&r)[EPT]) {
-  const T *p0 = xc ? base + x0 + k0 * ld : base + k0 + x0 * ld;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(p0), (short)0, 0x7fffffff, BUF_WORD3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff, BUF_WORD3);
+}
+
+// Every load is (per-lane byte offset, wave-uniform byte offset): the uniform
+// part goes in the instruction's scalar offset, so one vector register per
+// operand carries the lane's address.  An element outside the operand gets
+// the per-lane offset 2^31, past the resource's 2^31 - 1 byte range, and the
+// hardware returns zero for it without touching memory.  Valid elements are at
+// byte offsets below 2^31 (leading dimensions are below 2^21).
+template <typename T> struct Ld;
+template <> struct Ld<double> {
+  typedef double v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ double one(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0));
+  }
+  static __device__ __forceinline__ v2 two(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return __builtin_bit_cast(v2, __builtin_amdgcn_raw_buffer_load_b128(r, v, s, 0));
+  }
+};
+template <> struct Ld<float> {
+  typedef float v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float one(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, v, s, 0));
+  }
+  static __device__ __forceinline__ v2 two(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+    return __builtin_bit_cast(v2, __builtin_amdgcn_raw_buffer_load_b64(r, v, s, 0));
+  }
+};
+
+__device__ __forceinline__ uint32_t lane_off(bool ok, uint32_t v) { return ok ? v : OOB_OFFSET; }
+
+// Load modes (tlr_desc.h): LOAD_PAIR_M (A M-contiguous, one 16-byte load gives
+// rows 2h and 2h+1 of one k), LOAD_PAIR_K (A K-contiguous, one load gives
+// k-steps 2p and 2p+1 of one row) and LOAD_SINGLE (one element per load).  The
+// pair modes move B two elements per load as well.  The host only gives a
+// pair mode to a task whose operands allow it: pair-aligned bases and
+// offsets, even leading dimensions and an even extent along every paired
+// index, so that a pair lies wholly inside an operand or wholly outside it.
+constexpr int SINGLE = LOAD_SINGLE, PAIR_M = LOAD_PAIR_M, PAIR_K = LOAD_PAIR_K;
+
+template <typename T>
+struct SegCtx {
+  const T *aw;          // A at the wave's first row
+  const T *b;           // B at (k = 0, n = n0)
+  int32_t lda, ldb, K;
+  bool a_xc, b_xc;      // A: M contiguous; B: N contiguous
+  int mrem, nrem;       // rows of the wave's slice / columns of the block inside the operand
+  int32_t sr, sk;       // element strides of A along a row step and a k step
+  uint32_t a_lane;      // byte offset of the lane's (row 2*arow, k 2*g) in the slice
+  int row2, g2;         // 2*arow, 2*g
+};
+
+// A fragments needed after k-step q of a stage are loaded for the stage that
+// starts at k0.  Row and k split into a lane part (2*arow, 2*g) and a
+// wave-uniform part (ri, qk), and so does the bounds check.
+template <typename T, int MODE>
+__device__ __forceinline__ void load_a(const SegCtx<T> &c, int k0, int q, T (&fa)[MI][4]) {
+  const int krem = c.K - k0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(c.a_xc ? c.aw + (int64_t)k0 * c.lda : c.aw + k0);
+  constexpr uint32_t SZ = sizeof(T);
+  if (MODE == PAIR_M) {
+    const int qk = 8 * (q >> 1) + (q & 1);
+    const bool kok = c.g2 < krem - qk;
 #pragma unroll
-  for (int p = 0; p < EPT; ++p) {
-    const int x = m.x + p * m.dx, k = m.k + p * m.dk;
-    const bool ok = x < xrem && k < krem;
-    const uint32_t off = ok ? (uint32_t)(m.lin + p * m.step) * (uint32_t)sizeof(T) : OOB_OFFSET;
-    r[p] = BufLoad<T>::ld(rs, off);
+    for (int h = 0; h < MI / 2; ++h) {
+      const int ri = 32 * h;
+      const bool ok = kok && c.row2 < c.mrem - ri;
+      const typename Ld<T>::v2 v = Ld<T>::two(rs, lane_off(ok, c.a_lane), (uint32_t)(ri * c.sr + qk * c.sk) * SZ);
+      fa[2 * h][q] = v.x;
+      fa[2 * h + 1][q] = v.y;
+    }
+  } else if (MODE == PAIR_K) {
+    if (q & 1) {
+      const int qk = 8 * (q >> 1);
+      const bool kok = c.g2 < krem - qk;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int ri = 32 * (i >> 1) + (i & 1);
+        const bool ok = kok && c.row2 < c.mrem - ri;
+        const typename Ld<T>::v2 v = Ld<T>::two(rs, lane_off(ok, c.a_lane), (uint32_t)(ri * c.sr + qk * c.sk) * SZ);
+        fa[i][q - 1] = v.x;
+        fa[i][q] = v.y;
+      }
+    }
+  } else {
+    const int qk = 8 * (q >> 1) + (q & 1);
+    const bool kok = c.g2 < krem - qk;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int ri = 32 * (i >> 1) + (i & 1);
+      const bool ok = kok && c.row2 < c.mrem - ri;
+      fa[i][q] = Ld<T>::one(rs, lane_off(ok, c.a_lane), (uint32_t)(ri * c.sr + qk * c.sk) * SZ);
+    }
   }
 }
 
-template <typename T, int EPT>
-__device__ __forceinline__ void load_stage(const Seg<T> &s, int k0, int m0, int n0, int M, int N,
-                                           T (&ra)[EPT], T (&rb)[EPT]) {
-  const int krem = s.K - k0;
-  load_op<T, EPT>(s.a, m0, k0, s.lda, s.a_xc, M - m0, krem, s.ma, ra);
-  load_op<T, EPT>(s.b, n0, k0, s.ldb, s.b_xc, N - n0, krem, s.mb, rb);
+// Which B elements one thread moves per stage.  Single mode: EPT elements
+// (x + p*dx, k + p*dk) (x = n inside the block); pair mode: EPT/2 pairs, the
+// second element of a pair one further along the contiguous index (in LDS +1
+// along n, +LDS_B along k).  Entry p sits at byte offset lane + p*step of the
+// stage's resource and at LDS index lds + p*lds_step.
+struct BMap {
+  uint32_t lane, step;
+  int32_t x, dx, k, dk;
+  int32_t lds, lds_step, lds2;
+};
+
+template <int MODE, typename T>
+__device__ __forceinline__ BMap b_map(bool xc, int32_t ld, int tid) {
+  BMap m;
+  int32_t lin, st;
+  if (MODE == SINGLE) {
+    if (xc) {   // lanes walk n
+      m.x = tid & 127; m.dx = 0; m.k = tid >> 7; m.dk = NT / 128;
+      lin = m.x + m.k * ld; st = m.dk * ld;
+    } else {    // lanes walk k
+      m.k = tid & 15; m.dk = 0; m.x = tid >> 4; m.dx = NT / 16;
+      lin = m.k + m.x * ld; st = m.dx * ld;
+    }
+    m.lds2 = 0;
+  } else {
+    if (xc) {   // pairs along n: 64 pairs cover a k-row
+      m.x = 2 * (tid & 63); m.dx = 0; m.k = tid >> 6; m.dk = NT / 64;
+      lin = m.x + m.k * ld; st = m.dk * ld;
+      m.lds2 = 1;
+    } else {    // pairs along k: 8 pairs cover a column
+      m.k = 2 * (tid & 7); m.dk = 0; m.x = tid >> 3; m.dx = NT / 8;
+      lin = m.k + m.x * ld; st = m.dx * ld;
+      m.lds2 = LDS_B;
+    }
+  }
+  m.lane = (uint32_t)lin * (uint32_t)sizeof(T);
+  m.step = (uint32_t)st * (uint32_t)sizeof(T);
+  m.lds = m.k * LDS_B + m.x;
+  m.lds_step = m.dk * LDS_B + m.dx;
+  return m;
 }
 
-template <typename T, int EPT>
-__device__ __forceinline__ void store_stage(const Seg<T> &s, const T (&ra)[EPT], const T (&rb)[EPT], T *As, T *Bs) {
+template <typename T, int MODE>
+__device__ __forceinline__ void load_b(const SegCtx<T> &c, const BMap &m, int k0, T (&rb)[EPT]) {
+  const int krem = c.K - k0;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(c.b_xc ? c.b + (int64_t)k0 * c.ldb : c.b + k0);
+  if (MODE == SINGLE) {
 #pragma unroll
-  for (int p = 0; p < EPT; ++p) As[s.ma.lds + p * s.ma.lds_step] = ra[p];
+    for (int p = 0; p < EPT; ++p) {
+      const bool ok = m.x < c.nrem - p * m.dx && m.k < krem - p * m.dk;
+      rb[p] = Ld<T>::one(rs, lane_off(ok, m.lane), p * m.step);
+    }
+  } else {
 #pragma unroll
-  for (int p = 0; p < EPT; ++p) Bs[s.mb.lds + p * s.mb.lds_step] = rb[p];
+    for (int p = 0; p < EPT / 2; ++p) {
+      const bool ok = m.x < c.nrem - p * m.dx && m.k < krem - p * m.dk;
+      const typename Ld<T>::v2 v = Ld<T>::two(rs, lane_off(ok, m.lane), p * m.step);
+      rb[2 * p] = v.x;
+      rb[2 * p + 1] = v.y;
+    }
+  }
 }
 
-template <typename T, typename L>
+template <int MODE, typename T>
+__device__ __forceinline__ void store_b(const BMap &m, const T (&rb)[EPT], T *Bs) {
+  if (MODE == SINGLE) {
+#pragma unroll
+    for (int p = 0; p < EPT; ++p) Bs[m.lds + p * m.lds_step] = rb[p];
+  } else {
+#pragma unroll
+    for (int p = 0; p < EPT / 2; ++p) {
+      T *q = Bs + m.lds + p * m.lds_step;
+      q[0] = rb[2 * p];
+      q[m.lds2] = rb[2 * p + 1];
+    }
+  }
+}
+
+template <typename T, int MODE>
+__device__ __forceinline__ void run_segment(const SegCtx<T> &c, int tid, int arow, int g, int r, int wn,
+                                            T (*Bs)[KBK * LDS_B], typename Mfma<T>::v4 (&acc)[MI][NJ]) {
+  const int nst = (c.K + KBK - 1) / KBK;
+  if (nst <= 0) return;
+  const BMap bm = b_map<MODE, T>(c.b_xc, c.ldb, tid);
+  T fa[MI][4];
+  T rb[EPT];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_a<T, MODE>(c, 0, q, fa);
+  load_b<T, MODE>(c, bm, 0, rb);
+  __syncthreads();   // the previous segment's last reads of buffer 0 are done
+  store_b<MODE>(bm, rb, Bs[0]);
+  __syncthreads();
+  // One K stage: MFMAs on LDS buffer st & 1 and on fa; with MORE the next
+  // stage's loads are issued as their registers free up.  The last stage is
+  // peeled so that the loop body holds no conditional loads (a load under a
+  // branch makes the compiler wait for every outstanding load at the join).
+  auto stage = [&](int st, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    const int k1 = (st + 1) * KBK;
+    if (MORE) load_b<T, MODE>(c, bm, k1, rb);
+    const T *Bb = Bs[st & 1];
+#pragma unroll
+    for (int q = 0; q < KBK / 4; ++q) {
+      const T *br = Bb + k_of(q, g) * LDS_B + wn + r;
+      T b[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[j] = br[16 * j];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(fa[i][q], b[j], acc[i][j]);
+      if (MORE) load_a<T, MODE>(c, k1, q, fa);
+    }
+    if (MORE) {
+      store_b<MODE>(bm, rb, Bs[(st + 1) & 1]);
+      __syncthreads();
+    }
+  };
+  for (int st = 0; st + 1 < nst; ++st) stage(st, std::true_type{});
+  stage(nst - 1, std::false_type{});
+}
+
+template <typename T, int MODE0>
 __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, const int64_t *coltab,
                                            const Bases &bases, T alpha, T beta, T cscale) {
   typedef typename Mfma<T>::v4 v4;
-  constexpr int MI = L::MI, NJ = L::NJ, EPT = L::EPT;
-  __shared__ T As[2][KBK * LDS_A];
   __shared__ T Bs[2][KBK * LDS_B];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave % L::WAVES_M) * L::WM, wn = (wave / L::WAVES_M) * L::WN;
-  const int arow = Mfma<T>::arow(lane & 15);
+  // the wave index is uniform across the wave: readfirstlane tells the compiler
+  // so, which keeps operand addresses and buffer resources in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave * WM, wn = 0;
+  const int r = lane & 15, g = lane >> 4;
+  const int arow = Mfma<T>::arow(r);
   const int M = t.M, N = t.N;
 
   // C <- alpha*(acc + (beta/alpha)*C): when the host found beta/alpha finite the
@@ -196,84 +320,86 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   v4 acc[MI][NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn + 16 * j + (lane & 15);
+    const int n = n0 + wn + 16 * j + r;
     const int64_t col = (!preload || n >= N) ? 0 : (t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n]);
     const T *cp = C + col;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      acc[i][j] = v4{0, 0, 0, 0};
+    for (int h = 0; h < MI / 2; ++h) {
+      acc[2 * h][j] = v4{0, 0, 0, 0};
+      acc[2 * h + 1][j] = v4{0, 0, 0, 0};
       if (!preload || n >= N) continue;
-      const int mb = m0 + wm + 16 * i + 4 * (lane >> 4);
-      if (vec && mb + 3 < M) {
-        acc[i][j] = cscale * *reinterpret_cast<const v4 *>(cp + mb);
-      } else {
+      const int mb = m0 + wm + 32 * h + 8 * g;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (mb + v < M) acc[i][j][v] = cscale * cp[mb + v];
+      for (int u = 0; u < 2; ++u) {
+        const int m = mb + 4 * u;
+        if (vec && m + 3 < M) {
+          const v4 x = cscale * *reinterpret_cast<const v4 *>(cp + m);
+          acc[2 * h][j][2 * u] = x[0];
+          acc[2 * h + 1][j][2 * u] = x[1];
+          acc[2 * h][j][2 * u + 1] = x[2];
+          acc[2 * h + 1][j][2 * u + 1] = x[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m + e < M) acc[2 * h + (e & 1)][j][2 * u + (e >> 1)] = cscale * cp[m + e];
+        }
       }
     }
   }
 
+  // t lives in global (or kernel-argument) memory: the segment descriptor is
+  // read with scalar loads per iteration instead of being held in registers
   const int nseg = t.nseg;
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {   // constant segment index: no dynamic indexing into the task
-    if (sg >= nseg) break;
-    const Seg<T> s = make_seg<T, L::NT>(t.seg[sg], bases, tid);
-    const int nst = (s.K + KBK - 1) / KBK;
-    T ra[EPT], rb[EPT];
-    load_stage<T, EPT>(s, 0, m0, n0, M, N, ra, rb);
-    __syncthreads();   // the previous segment's last reads of buffer 0 are done
-    store_stage<T, EPT>(s, ra, rb, As[0], Bs[0]);
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-      const bool more = st + 1 < nst;
-      if (more) load_stage<T, EPT>(s, (st + 1) * KBK, m0, n0, M, N, ra, rb);
-      const T *Ab = As[st & 1];
-      const T *Bb = Bs[st & 1];
-#pragma unroll
-      for (int kq = 0; kq < KBK / 4; ++kq) {
-        const int kr = kq * 4 + (lane >> 4);
-        T a[MI], b[NJ];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) a[i] = Ab[kr * LDS_A + wm + 16 * i + arow];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) b[j] = Bb[kr * LDS_B + wn + 16 * j + (lane & 15)];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
-      }
-      if (more) store_stage<T, EPT>(s, ra, rb, As[(st + 1) & 1], Bs[(st + 1) & 1]);
-      __syncthreads();
-    }
-  }
+  auto setup = [&](const DevSeg &d, SegCtx<T> &c) {
+    const T *a = static_cast<const T *>(bases.p[d.a.base]) + d.a.off;
+    const T *b = static_cast<const T *>(bases.p[d.b.base]) + d.b.off;
+    c.lda = d.a.ld;
+    c.ldb = d.b.ld;
+    c.K = d.K;
+    c.a_xc = d.a.trans == 0;
+    c.b_xc = d.b.trans == 1;
+    c.aw = c.a_xc ? a + (m0 + wm) : a + (int64_t)(m0 + wm) * c.lda;
+    c.b = c.b_xc ? b + n0 : b + (int64_t)n0 * c.ldb;
+    c.mrem = M - m0 - wm;
+    c.nrem = N - n0;
+    c.sr = c.a_xc ? 1 : c.lda;
+    c.sk = c.a_xc ? c.lda : 1;
+    c.row2 = 2 * arow;
+    c.g2 = 2 * g;
+    c.a_lane = (uint32_t)(c.row2 * c.sr + c.g2 * c.sk) * (uint32_t)sizeof(T);
+  };
+  if (nseg > 0) { SegCtx<T> c; setup(t.seg[0], c); run_segment<T, MODE0>(c, tid, arow, g, r, wn, Bs, acc); }
+  if (nseg > 1) { SegCtx<T> c; setup(t.seg[1], c); run_segment<T, SINGLE>(c, tid, arow, g, r, wn, Bs, acc); }
 
-  // epilogue: lane holds rows 4*(lane/16)+v (v = 0..3), column lane%16 of each
-  // 16x16 tile; when the column start is 4-element aligned those four rows go
-  // out as one vector access.
+  // epilogue: eight consecutive rows per lane and column, as two 4-element
+  // vectors when the column start is 4-element aligned
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn + 16 * j + (lane & 15);
+    const int n = n0 + wn + 16 * j + r;
     if (n >= N) continue;
     const int64_t col = t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n];
     T *cp = C + col;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int mb = m0 + wm + 16 * i + 4 * (lane >> 4);
-      v4 x = acc[i][j];
-      if (fin) x = alpha * x;
-      if (vec && mb + 3 < M) {
-        v4 *vp = reinterpret_cast<v4 *>(cp + mb);
-        if (rd) x += beta * *vp;
-        *vp = x;
-      } else {
+    for (int h = 0; h < MI / 2; ++h) {
+      const int mb = m0 + wm + 32 * h + 8 * g;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = mb + v;
-          if (m < M) {
-            T y = x[v];
-            if (rd) y += beta * cp[m];
-            cp[m] = y;
+      for (int u = 0; u < 2; ++u) {
+        v4 x = v4{acc[2 * h][j][2 * u], acc[2 * h + 1][j][2 * u], acc[2 * h][j][2 * u + 1],
+                  acc[2 * h + 1][j][2 * u + 1]};
+        if (fin) x = alpha * x;
+        const int m = mb + 4 * u;
+        if (vec && m + 3 < M) {
+          v4 *vp = reinterpret_cast<v4 *>(cp + m);
+          if (rd) x += beta * *vp;
+          *vp = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (m + e < M) {
+              T y = x[e];
+              if (rd) y += beta * cp[m + e];
+              cp[m + e] = y;
+            }
           }
         }
       }
@@ -281,22 +407,25 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   }
 }
 
-template <typename T, int STAGE, typename L>
-__global__ __launch_bounds__(L::NT) __attribute__((amdgpu_waves_per_eu(L::WPE)))
+// MODE: load mode of the first segment of every task in the table (the
+// table is split by mode on the host); a second segment, the small diagonal
+// term of a tile, always runs in single-element mode.
+template <typename T, int STAGE, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void grouped_gemm_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
                          const int64_t *__restrict__ coltab, Bases bases, T alpha, T beta, T cscale) {
   const DevTile e = tiles[blockIdx.x];
   if (e.task < 0) return;
-  const DevTask t = tasks[e.task];
+  const DevTask &t = tasks[e.task];
   const bool fin = t.final_ != 0;
-  gemm_block<T, L>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0), fin ? cscale : T(0));
+  gemm_block<T, MODE>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0), fin ? cscale : T(0));
 }
 
 // Single task given by value; blockIdx.x walks the output blocks so that each
 // XCD (workgroups are dealt to the 8 XCDs round-robin) takes a contiguous run
 // of block indices, ordered in bands of 8 block rows for L2 reuse.
-template <typename T, typename L>
-__global__ __launch_bounds__(L::NT) __attribute__((amdgpu_waves_per_eu(L::WPE)))
+template <typename T, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int mt, int nt, int per) {
   const int bid = blockIdx.x;
   const int logical = (bid & 7) * per + (bid >> 3);
@@ -308,7 +437,7 @@ void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int m
   const int in = logical - group * band * nt;
   const int mtile = first_m + in % rows;
   const int ntile = in / rows;
-  gemm_block<T, L>(t, mtile * KBM, ntile * KBN, nullptr, bases, alpha, beta, cscale);
+  gemm_block<T, MODE>(t, mtile * KBM, ntile * KBN, nullptr, bases, alpha, beta, cscale);
 }
 
 template <typename T>
@@ -332,52 +461,58 @@ T preload_scale(double alpha, double beta) {
   return (r == r && r < lim && r > -lim) ? T(r) : T(0);
 }
 
-// 64 x 32 waves (8 per workgroup, four waves per SIMD with two workgroups per
-// CU) measured faster than 64 x 64 waves at every K on this chip: more waves
-// cover the barrier and memory phases of a workgroup.
-using WaveLayout = Layout<64, 32>;
-
-template <typename T, typename L>
-void launch_grouped_l(int stage, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+template <typename T, int STAGE>
+void launch_grouped_s(int mode, dim3 grid, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                       const int64_t *coltab, const Bases &bases, T a, T b, T c) {
-  dim3 grid(n), block(L::NT);
-  if (stage == 1)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 1, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
-  else if (stage == 2)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 2, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+  const dim3 block(NT);
+  if (mode == LOAD_PAIR_M)
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_M>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (mode == LOAD_PAIR_K)
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_K>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, 3, L>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_SINGLE>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
 }
 
 template <typename T>
-void launch_grouped_t(int stage, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+void launch_grouped_t(int stage, int mode, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                       const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
-  launch_grouped_l<T, WaveLayout>(stage, n, s, tasks, tiles, coltab, bases, a, b, c);
+  const dim3 grid(n);
+  if (stage == 1)
+    launch_grouped_s<T, 1>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (stage == 2)
+    launch_grouped_s<T, 2>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else
+    launch_grouped_s<T, 3>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
 }
 
 template <typename T>
-void launch_single_t(unsigned n, hipStream_t s, const DevTask &task, const Bases &bases, double alpha,
+void launch_single_t(int mode, unsigned n, hipStream_t s, const DevTask &task, const Bases &bases, double alpha,
                      double beta, int mt, int nt, int per) {
   const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
-  hipLaunchKernelGGL((single_gemm_kernel<T, WaveLayout>), dim3(n), dim3(WaveLayout::NT), 0, s, task, bases, a, b,
-                     c, mt, nt, per);
+  const dim3 grid(n), block(NT);
+  if (mode == LOAD_PAIR_M)
+    hipLaunchKernelGGL((single_gemm_kernel<T, LOAD_PAIR_M>), grid, block, 0, s, task, bases, a, b, c, mt, nt, per);
+  else if (mode == LOAD_PAIR_K)
+    hipLaunchKernelGGL((single_gemm_kernel<T, LOAD_PAIR_K>), grid, block, 0, s, task, bases, a, b, c, mt, nt, per);
+  else
+    hipLaunchKernelGGL((single_gemm_kernel<T, LOAD_SINGLE>), grid, block, 0, s, task, bases, a, b, c, mt, nt, per);
 }
 
 }  // namespace
 
-int launch_grouped(tlr_dtype dt, int stage, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
+int launch_grouped(tlr_dtype dt, int stage, int mode, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
                    const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
   if (n_tiles <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64)
-    launch_grouped_t<double>(stage, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+    launch_grouped_t<double>(stage, mode, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   else
-    launch_grouped_t<float>(stage, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+    launch_grouped_t<float>(stage, mode, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   return (int)hipGetLastError();
 }
 
-int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double alpha, double beta,
+int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &bases, double alpha, double beta,
                   void *stream) {
   const int mt = (task.M + KBM - 1) / KBM, nt = (task.N + KBN - 1) / KBN;
   if (mt == 0 || nt == 0) return 0;
@@ -385,9 +520,9 @@ int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double 
   const int per = (int)((n + 7) / 8);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64)
-    launch_single_t<double>((unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
+    launch_single_t<double>(mode, (unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
   else
-    launch_single_t<float>((unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
+    launch_single_t<float>(mode, (unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
   return (int)hipGetLastError();
 }
 

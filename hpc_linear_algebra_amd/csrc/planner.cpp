@@ -482,12 +482,15 @@ static double task_exec_flops(const DevTask &d) {
   return F;
 }
 
-// Emit the workgroup table of one launch.  Workgroups are dealt to the 8 XCDs
-// round-robin by index (index x, x+8, x+16, ... run on XCD x, each XCD in its
-// own order), so the table is built per XCD: whole tasks (all blocks of one
-// output tile stay on one XCD and share its L2) go, longest first, to the XCD
-// with the least work so far, and each XCD's list runs longest first.  Lists
-// are padded with idle entries to a common length.
+// Emit the workgroup table of one launch: one sub-table per load mode of the
+// tasks (tlr_desc.h), each built the same way.  Workgroups are dealt to the 8
+// XCDs round-robin by index (index x, x+8, x+16, ... run on XCD x, each XCD in
+// its own order), so a sub-table is built per XCD: whole tasks (all blocks of
+// one output tile stay on one XCD and share its L2) go, longest first, to the
+// XCD with the least work so far, and each XCD's list runs longest first.
+// Lists are padded with idle entries to a common length, so every sub-table
+// is a multiple of NUM_XCD entries and the XCD of an entry does not depend on
+// which sub-tables precede it.
 static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   if (tl.t.empty()) return;
   Launch L;
@@ -499,7 +502,7 @@ static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.useful_flops = 0;
   L.executed_flops = 0;
   const int32_t task0 = (int32_t)p.tasks.size();
-  struct TaskCost { int32_t t; int64_t per_block, blocks; };
+  struct TaskCost { int32_t t; int64_t per_block, blocks; int mode; };
   std::vector<TaskCost> order;
   for (size_t t = 0; t < tl.t.size(); ++t) {
     const DevTask &d = tl.t[t];
@@ -509,29 +512,34 @@ static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
     for (int s = 0; s < d.nseg; ++s) K += d.seg[s].K;
     const int64_t blocks = ceil_div(d.M, BM) * ceil_div(d.N, BN);
     // one block costs its K steps plus a fixed share for the C update
-    order.push_back({(int32_t)t, K + 32, blocks});
+    order.push_back({(int32_t)t, K + 32, blocks, task_load_mode(d)});
     p.tasks.push_back(d);
   }
   std::stable_sort(order.begin(), order.end(),
                    [](const TaskCost &a, const TaskCost &b) { return a.per_block > b.per_block; });
-  std::vector<std::vector<DevTile>> xl(NUM_XCD);
-  std::vector<int64_t> load(NUM_XCD, 0);
-  for (const TaskCost &c : order) {
-    int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    load[x] += c.per_block * c.blocks;
-    const DevTask &d = tl.t[c.t];
-    for (int64_t m0 = 0; m0 < d.M; m0 += BM)
-      for (int64_t n0 = 0; n0 < d.N; n0 += BN)
-        xl[x].push_back(DevTile{task0 + c.t, (int32_t)m0, (int32_t)n0, 0});
-  }
-  size_t per = 0;
-  for (auto &v : xl) per = std::max(per, v.size());
-  std::vector<DevTile> tab(per * NUM_XCD, DevTile{-1, 0, 0, 0});
-  for (int x = 0; x < NUM_XCD; ++x)
-    for (size_t t = 0; t < xl[x].size(); ++t) tab[t * NUM_XCD + x] = xl[x][t];
   L.tile_off = (int64_t)p.tiles.size();
-  L.n_tiles = (int64_t)tab.size();
-  p.tiles.insert(p.tiles.end(), tab.begin(), tab.end());
+  for (int mode = 0; mode < NUM_LOAD_MODES; ++mode) {
+    std::vector<std::vector<DevTile>> xl(NUM_XCD);
+    std::vector<int64_t> load(NUM_XCD, 0);
+    for (const TaskCost &c : order) {
+      if (c.mode != mode) continue;
+      int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      load[x] += c.per_block * c.blocks;
+      const DevTask &d = tl.t[c.t];
+      for (int64_t m0 = 0; m0 < d.M; m0 += BM)
+        for (int64_t n0 = 0; n0 < d.N; n0 += BN)
+          xl[x].push_back(DevTile{task0 + c.t, (int32_t)m0, (int32_t)n0, 0});
+    }
+    size_t per = 0;
+    for (auto &v : xl) per = std::max(per, v.size());
+    std::vector<DevTile> tab(per * NUM_XCD, DevTile{-1, 0, 0, 0});
+    for (int x = 0; x < NUM_XCD; ++x)
+      for (size_t t = 0; t < xl[x].size(); ++t) tab[t * NUM_XCD + x] = xl[x][t];
+    L.mode_off[mode] = (int64_t)p.tiles.size() - L.tile_off;
+    L.mode_tiles[mode] = (int64_t)tab.size();
+    p.tiles.insert(p.tiles.end(), tab.begin(), tab.end());
+  }
+  L.n_tiles = (int64_t)p.tiles.size() - L.tile_off;
   p.launches.push_back(L);
   p.groups[group].launches.push_back((int)p.launches.size() - 1);
 }
@@ -860,11 +868,25 @@ static tlr_status validate(const Plan &p, bool deep) {
   for (const Launch &L : p.launches) {
     if (L.tile_off < 0 || L.tile_off + L.n_tiles > (int64_t)p.tiles.size() || L.n_tiles % NUM_XCD)
       return fail(TLR_ERR_INVALID_ARG, "internal: launch table out of range");
+    // the per-mode sub-tables tile the launch's table, and a pair mode only
+    // holds tasks that qualify for it: its loads rely on that for staying
+    // inside the operands
+    int64_t covered = 0;
+    for (int m = 0; m < NUM_LOAD_MODES; ++m) {
+      if (L.mode_off[m] != covered || L.mode_tiles[m] < 0 || L.mode_tiles[m] % NUM_XCD)
+        return fail(TLR_ERR_INVALID_ARG, "internal: load-mode tables malformed");
+      covered += L.mode_tiles[m];
+    }
+    if (covered != L.n_tiles) return fail(TLR_ERR_INVALID_ARG, "internal: load-mode tables malformed");
     for (int64_t e = L.tile_off; e < L.tile_off + L.n_tiles; ++e) {
       const DevTile &x = p.tiles[e];
       if (x.task < 0) continue;
       if (x.task >= (int32_t)p.tasks.size()) return fail(TLR_ERR_INVALID_ARG, "internal: bad task index");
       const DevTask &d = p.tasks[x.task];
+      int mode = 0;
+      while (mode + 1 < NUM_LOAD_MODES && e >= L.tile_off + L.mode_off[mode + 1]) ++mode;
+      if (mode != LOAD_SINGLE && task_load_mode(d) != mode)
+        return fail(TLR_ERR_INVALID_ARG, "internal: task in the table of a load mode it does not qualify for");
       if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % BM || x.n0 % BN)
         return fail(TLR_ERR_INVALID_ARG, "internal: bad block origin");
       seen[x.task]++;

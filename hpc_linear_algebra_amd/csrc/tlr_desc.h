@@ -57,6 +57,27 @@ struct DevTask {         // 112 bytes
 
 enum TaskFlags : uint8_t { TASK_VEC = 1 };
 
+// How the kernel loads the first K segment of a task (a launch's workgroup
+// table is split into one contiguous sub-table per mode).  The pair modes load
+// two adjacent elements per instruction: along M (PAIR_M, A M-contiguous) or
+// along K (PAIR_K, A K-contiguous) for A, and along the contiguous index for B.
+// A task qualifies for a pair mode when, for both operands of that segment,
+// the element offset and the leading dimension are even and the extent along
+// each paired index is even; the buffer bases must be aligned to a pair
+// (checked when the plan runs).
+enum LoadMode : int { LOAD_SINGLE = 0, LOAD_PAIR_M = 1, LOAD_PAIR_K = 2, NUM_LOAD_MODES = 3 };
+
+inline int task_load_mode(const DevTask &t) {
+  if (t.nseg < 1) return LOAD_SINGLE;
+  const DevSeg &s = t.seg[0];
+  const bool b_even = (s.b.off % 2) == 0 && (s.b.ld % 2) == 0 &&
+                      (s.b.trans == 1 ? (t.N % 2) == 0 : (s.K % 2) == 0);
+  const bool a_even = (s.a.off % 2) == 0 && (s.a.ld % 2) == 0;
+  if (!a_even || !b_even) return LOAD_SINGLE;
+  if (s.a.trans == 0) return (t.M % 2) == 0 ? LOAD_PAIR_M : LOAD_SINGLE;
+  return (s.K % 2) == 0 ? LOAD_PAIR_K : LOAD_SINGLE;
+}
+
 struct DevTile {         // 16 bytes
   int32_t task;          // < 0: idle workgroup (launch padding)
   int32_t m0, n0;

@@ -46,6 +46,11 @@ struct Launch {
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int64_t tile_off;  // first DevTile of the launch in the tile table
   int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)
+  // the table is the concatenation of one sub-table per load mode (each a
+  // multiple of NUM_XCD entries, possibly empty): mode m covers entries
+  // [tile_off + mode_off[m], tile_off + mode_off[m] + mode_tiles[m])
+  int64_t mode_off[NUM_LOAD_MODES];
+  int64_t mode_tiles[NUM_LOAD_MODES];
   int64_t n_tasks;
   double useful_flops, executed_flops;
 };
@@ -115,10 +120,10 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
                       double beta, void *C, int64_t ldc, void *stream);
 
 // Kernel launchers (gemm.hip).
-int launch_grouped(tlr_dtype dt, int stage, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
-                   const int64_t *coltab, const Bases &bases, double alpha, double beta,
+int launch_grouped(tlr_dtype dt, int stage, int mode, const DevTask *tasks, const DevTile *tiles,
+                   int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,
                    void *stream);
-int launch_single(tlr_dtype dt, const DevTask &task, const Bases &bases, double alpha,
+int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &bases, double alpha,
                   double beta, void *stream);
 int launch_scale(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta,
                  void *stream);

@@ -23,10 +23,11 @@ def _short(name: str) -> str:
     m = re.search(r"(grouped_gemm_kernel<[^>]*>|single_gemm_kernel<[^>]*>|scale_kernel<[^>]*>)", name)
     if m:
         return m.group(1)
-    m = re.search(r"(grouped_gemm_kernel|single_gemm_kernel|scale_kernel)I([df])(Li(\d)E)?", name)
+    m = re.search(r"(grouped_gemm_kernel|single_gemm_kernel|scale_kernel)I([df])((?:Li\d+E)*)", name)
     if m:
         t = "double" if m.group(2) == "d" else "float"
-        return f"{m.group(1)}<{t}{', ' + m.group(4) if m.group(4) else ''}>"
+        args = re.findall(r"Li(\d+)E", m.group(3))
+        return f"{m.group(1)}<{', '.join([t] + args)}>"
     return name[:90]
 
 
