@@ -33,6 +33,10 @@ void plan_release_device(Plan *p) {
   destroy_events(p->join_events);
   destroy_events(p->dep_events);
   destroy_events(p->prof_events);
+  destroy_events(p->mode_events);
+  for (void *s : p->aux_streams)
+    if (s) (void)hipStreamDestroy(static_cast<hipStream_t>(s));
+  p->aux_streams.clear();
   if (p->fork_event) {
     (void)hipEventDestroy(static_cast<hipEvent_t>(p->fork_event));
     p->fork_event = nullptr;
@@ -71,6 +75,24 @@ tlr_status plan_bind(Plan *p, void *dev, size_t bytes, void *stream) {
     if (awaited) HIP_TRY(hipEventCreateWithFlags(&de, hipEventDisableTiming));
     p->dep_events.push_back(de);
   }
+  bool split = false;
+  for (size_t l = 0; l < p->launches.size(); ++l) {
+    const Launch &L = p->launches[l];
+    int parts = 0;
+    for (int m = 0; m < NUM_LOAD_MODES; ++m) parts += L.mode_tiles[m] > 0;
+    for (int e = 0; e < 3; ++e) {
+      hipEvent_t me = nullptr;
+      if (parts > 1) HIP_TRY(hipEventCreateWithFlags(&me, hipEventDisableTiming));
+      p->mode_events.push_back(me);
+    }
+    split = split || parts > 1;
+  }
+  if (split)
+    for (size_t i = 0; i < 2 * p->groups.size(); ++i) {
+      hipStream_t as;
+      HIP_TRY(hipStreamCreateWithFlags(&as, hipStreamNonBlocking));   // ordered by events only
+      p->aux_streams.push_back(as);
+    }
   p->device = devno;
   p->dev_desc = dev;
   return TLR_OK;
@@ -205,10 +227,28 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
       }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
       if (pairs_ok) {
+        // one kernel per load mode; several non-empty ones run side by side
+        // (the first on the group's stream, the others on its auxiliary
+        // streams) so that a small sub-table does not run alone on the GPU
+        int part = 0;
+        hipEvent_t fork = static_cast<hipEvent_t>(p->mode_events[3 * l]);
+        if (fork) HIP_TRY(hipEventRecord(fork, sg));   // before the first sub-launch: all start together
         for (int m = 0; m < NUM_LOAD_MODES; ++m) {
+          if (L.mode_tiles[m] == 0) continue;
+          hipStream_t sm = sg;
+          if (part > 0) {
+            sm = static_cast<hipStream_t>(p->aux_streams[2 * L.group + part - 1]);
+            HIP_TRY(hipStreamWaitEvent(sm, fork, 0));
+          }
           int e = launch_grouped(p->dt, L.stage, m, tasks, tiles + L.tile_off + L.mode_off[m], L.mode_tiles[m],
-                                 ctab, bases, alpha, beta, sg);
+                                 ctab, bases, alpha, beta, sm);
           if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
+          if (part > 0) {
+            hipEvent_t join = static_cast<hipEvent_t>(p->mode_events[3 * l + part]);
+            HIP_TRY(hipEventRecord(join, sm));
+            HIP_TRY(hipStreamWaitEvent(sg, join, 0));
+          }
+          ++part;
         }
       } else {
         int e = launch_grouped(p->dt, L.stage, LOAD_SINGLE, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases,

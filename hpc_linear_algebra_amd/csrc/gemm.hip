@@ -63,15 +63,19 @@ template <> struct Mfma<float> {
 
 // Which A row and which k a lane feeds to the MFMAs.  Lane (r, g) = (lane % 16,
 // lane / 16) supplies, to MFMA tile i at k-step q of a stage, element
-//   row(i, r) = 32*(i/2) + 2*arow(r) + i%2,   k(q, g) = 8*(q/2) + 2*g + q%2
-// of the wave's 64 x 16 slice of A, and reads the matching B element from LDS
-// row k(q, g).  Rows come in adjacent pairs (tiles 2h, 2h+1) and k in adjacent
-// pairs (steps 2p, 2p+1), so one 16-byte load fills two MFMA operands whichever
-// index of A is the contiguous one.  After the MFMAs lane (r, g) holds, for
-// column r of each 16-column tile j, the eight consecutive rows
-// 32h + 8g + t, t = 2v + e, in acc[2h + e][j][v].
+//   row(i, r) = 32*(i/2) + 2*arow(r) + i%2
+// of the wave's slice of A at k = kq(q) + kg(g), and reads the matching B
+// element from LDS row k.  Rows come in adjacent pairs (tiles 2h, 2h+1), so
+// one 16-byte load fills two MFMA operands when A is M-contiguous.  When A is
+// K-contiguous (PAIR_K) k comes in adjacent pairs instead (steps 2p, 2p+1):
+//   kq(q) = 8*(q/2) + q%2, kg(g) = 2*g;  otherwise kq(q) = 4*q, kg(g) = g,
+// which keeps every k-step on four consecutive k (a step wholly past the end
+// of K is skipped).  After the MFMAs lane (r, g) holds, for column r of each
+// 16-column tile j, the eight consecutive rows 32h + 8g + t, t = 2v + e, in
+// acc[2h + e][j][v].
 __device__ __forceinline__ int a_row(int i, int arow) { return 32 * (i >> 1) + 2 * arow + (i & 1); }
-__device__ __forceinline__ int k_of(int q, int g) { return 8 * (q >> 1) + 2 * g + (q & 1); }
+template <int MODE> __device__ __forceinline__ int kq_of(int q);
+template <int MODE> __device__ __forceinline__ int kg_of(int g);
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;
 constexpr int BUF_WORD3 = 0x00020000;   // raw (untyped) buffer access on CDNA
@@ -117,6 +121,11 @@ __device__ __forceinline__ uint32_t lane_off(bool ok, uint32_t v) { return ok ? 
 // index, so that a pair lies wholly inside an operand or wholly outside it.
 constexpr int SINGLE = LOAD_SINGLE, PAIR_M = LOAD_PAIR_M, PAIR_K = LOAD_PAIR_K;
 
+template <int MODE> __device__ __forceinline__ int kq_of(int q) {
+  return MODE == PAIR_K ? 8 * (q >> 1) + (q & 1) : 4 * q;
+}
+template <int MODE> __device__ __forceinline__ int kg_of(int g) { return MODE == PAIR_K ? 2 * g : g; }
+
 template <typename T>
 struct SegCtx {
   const T *aw;          // A at the wave's first row
@@ -126,7 +135,7 @@ struct SegCtx {
   int mrem, nrem;       // rows of the wave's slice / columns of the block inside the operand
   int32_t sr, sk;       // element strides of A along a row step and a k step
   uint32_t a_lane;      // byte offset of the lane's (row 2*arow, k 2*g) in the slice
-  int row2, g2;         // 2*arow, 2*g
+  int row2, gk;         // 2*arow and the lane's k offset kg(g)
 };
 
 // A fragments needed after k-step q of a stage are loaded for the stage that
@@ -138,8 +147,8 @@ __device__ __forceinline__ void load_a(const SegCtx<T> &c, int k0, int q, T (&fa
   const __amdgpu_buffer_rsrc_t rs = rsrc(c.a_xc ? c.aw + (int64_t)k0 * c.lda : c.aw + k0);
   constexpr uint32_t SZ = sizeof(T);
   if (MODE == PAIR_M) {
-    const int qk = 8 * (q >> 1) + (q & 1);
-    const bool kok = c.g2 < krem - qk;
+    const int qk = kq_of<MODE>(q);
+    const bool kok = c.gk < krem - qk;
 #pragma unroll
     for (int h = 0; h < MI / 2; ++h) {
       const int ri = 32 * h;
@@ -150,8 +159,8 @@ __device__ __forceinline__ void load_a(const SegCtx<T> &c, int k0, int q, T (&fa
     }
   } else if (MODE == PAIR_K) {
     if (q & 1) {
-      const int qk = 8 * (q >> 1);
-      const bool kok = c.g2 < krem - qk;
+      const int qk = kq_of<MODE>(q - 1);
+      const bool kok = c.gk < krem - qk;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int ri = 32 * (i >> 1) + (i & 1);
@@ -162,8 +171,8 @@ __device__ __forceinline__ void load_a(const SegCtx<T> &c, int k0, int q, T (&fa
       }
     }
   } else {
-    const int qk = 8 * (q >> 1) + (q & 1);
-    const bool kok = c.g2 < krem - qk;
+    const int qk = kq_of<MODE>(q);
+    const bool kok = c.gk < krem - qk;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int ri = 32 * (i >> 1) + (i & 1);
@@ -252,10 +261,13 @@ __device__ __forceinline__ void store_b(const BMap &m, const T (&rb)[EPT], T *Bs
 }
 
 template <typename T, int MODE>
-__device__ __forceinline__ void run_segment(const SegCtx<T> &c, int tid, int arow, int g, int r, int wn,
+__device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int g, int r, int wn,
                                             T (*Bs)[KBK * LDS_B], typename Mfma<T>::v4 (&acc)[MI][NJ]) {
   const int nst = (c.K + KBK - 1) / KBK;
   if (nst <= 0) return;
+  c.gk = kg_of<MODE>(g);
+  c.a_lane = (uint32_t)(c.row2 * c.sr + c.gk * c.sk) * (uint32_t)sizeof(T);
+  const int klast = c.K - (nst - 1) * KBK;   // valid k of the last stage
   const BMap bm = b_map<MODE, T>(c.b_xc, c.ldb, tid);
   T fa[MI][4];
   T rb[EPT];
@@ -276,7 +288,8 @@ __device__ __forceinline__ void run_segment(const SegCtx<T> &c, int tid, int aro
     const T *Bb = Bs[st & 1];
 #pragma unroll
     for (int q = 0; q < KBK / 4; ++q) {
-      const T *br = Bb + k_of(q, g) * LDS_B + wn + r;
+      if (!MORE && kq_of<MODE>(q) >= klast) continue;   // every k of this step is past K
+      const T *br = Bb + (kq_of<MODE>(q) + kg_of<MODE>(g)) * LDS_B + wn + r;
       T b[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) b[j] = br[16 * j];
@@ -365,8 +378,7 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
     c.sr = c.a_xc ? 1 : c.lda;
     c.sk = c.a_xc ? c.lda : 1;
     c.row2 = 2 * arow;
-    c.g2 = 2 * g;
-    c.a_lane = (uint32_t)(c.row2 * c.sr + c.g2 * c.sk) * (uint32_t)sizeof(T);
+    c.a_lane = 0;   // set per load mode in run_segment
   };
   if (nseg > 0) { SegCtx<T> c; setup(t.seg[0], c); run_segment<T, MODE0>(c, tid, arow, g, r, wn, Bs, acc); }
   if (nseg > 1) { SegCtx<T> c; setup(t.seg[1], c); run_segment<T, SINGLE>(c, tid, arow, g, r, wn, Bs, acc); }

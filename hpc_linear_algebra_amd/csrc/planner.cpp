@@ -31,6 +31,7 @@ namespace tlr {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+static int64_t even_up(int64_t x) { return x + (x & 1); }
 
 static void split_dim(int64_t n, int64_t b, std::vector<int64_t> &s, std::vector<int64_t> &o) {
   s.clear();
@@ -154,6 +155,16 @@ static int64_t height(const Plan &p, int i0, int i1) {
 }
 
 // Exact workspace bytes of one rectangle in one order (every buffer 256-B aligned).
+// Coupling block S_k (kappa x beta) in the workspace: column-major S for the
+// right order, S^T for the left, each with its leading dimension rounded up to
+// even, so that the right or left product reads it with pair loads.
+static int64_t s_ld(int64_t kappa, int64_t beta, int order) {
+  return even_up(order == TLR_ORDER_RIGHT ? kappa : beta);
+}
+static int64_t s_elems(int64_t kappa, int64_t beta, int order) {
+  return s_ld(kappa, beta, order) * (order == TLR_ORDER_RIGHT ? beta : kappa);
+}
+
 static size_t rect_ws(const Plan &p, const Sums &s, int i0, int i1, int j0, int j1, int order) {
   const size_t es = p.es;
   size_t tot = 0;
@@ -165,7 +176,7 @@ static size_t rect_ws(const Plan &p, const Sums &s, int i0, int i1, int j0, int 
   }
   for (int k = 0; k < s.qk; ++k) {
     int64_t M = s.kap(k, i0, i1), N = s.bet(k, j0, j1);
-    if (M > 0 && N > 0) tot += align_up((size_t)M * N * es, WS_ALIGN);
+    if (M > 0 && N > 0) tot += align_up((size_t)s_elems(M, N, order) * es, WS_ALIGN);
   }
   if (order == TLR_ORDER_RIGHT) {
     for (int i = i0; i < i1; ++i) {
@@ -443,7 +454,14 @@ static DevOperand opnd(uint8_t base, int64_t off, int64_t ld, int trans) {
   o.ld = (int32_t)ld;
   o.base = base;
   o.trans = (uint8_t)trans;
-  o.pad = 0;
+  o.flags = 0;
+  return o;
+}
+
+// a workspace operand allocated with whole ld-strided vectors: padded when ld
+// exceeds its extent along the contiguous index
+static DevOperand padded(DevOperand o, int64_t extent) {
+  if (o.ld > extent) o.flags |= OPND_PADDED;
   return o;
 }
 
@@ -615,14 +633,23 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
   for (int k = 0; k < qk; ++k) {
     SM[k] = s.kap(k, i0, i1);
     SN[k] = s.bet(k, j0, j1);
-    if (SM[k] > 0 && SN[k] > 0) Soff[k] = take((size_t)SM[k] * SN[k] * es);
+    if (SM[k] > 0 && SN[k] > 0) Soff[k] = take((size_t)s_elems(SM[k], SN[k], R.order) * es);
   }
   TaskList l1, l2, l3;
   for (int k = 0; k < qk; ++k) {
     if (Soff[k] < 0) continue;
-    DevTask d = new_task(SM[k], SN[k], BASE_WS, Soff[k], SM[k], -1, false);
-    add_seg(d, opnd(A.inner_base, A.ic(i0, k) * b, b, 1), opnd(B.outer_base, B.oc(k, j0) * b, b, 0), A.cs[k]);
-    l1.t.push_back(d);
+    const int64_t ls = s_ld(SM[k], SN[k], R.order);
+    if (R.order == TLR_ORDER_RIGHT) {
+      // S_k = V_{I,k}^T W_{k,J}
+      DevTask d = new_task(SM[k], SN[k], BASE_WS, Soff[k], ls, -1, false);
+      add_seg(d, opnd(A.inner_base, A.ic(i0, k) * b, b, 1), opnd(B.outer_base, B.oc(k, j0) * b, b, 0), A.cs[k]);
+      l1.t.push_back(d);
+    } else {
+      // S_k^T = W_{k,J}^T V_{I,k}
+      DevTask d = new_task(SN[k], SM[k], BASE_WS, Soff[k], ls, -1, false);
+      add_seg(d, opnd(B.outer_base, B.oc(k, j0) * b, b, 1), opnd(A.inner_base, A.ic(i0, k) * b, b, 0), A.cs[k]);
+      l1.t.push_back(d);
+    }
     l1.useful.push_back(2.0 * SM[k] * (double)SN[k] * A.cs[k]);
   }
 
@@ -667,7 +694,8 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
         } else {
           int32_t r = B.r(k, j);
           if (r > 0)
-            add_seg(d, opnd(B.inner_base, B.ic(k, j) * b, b, 0), opnd(BASE_WS, Soff[k] + boff * SM[k], SM[k], 1), r);
+            add_seg(d, opnd(B.inner_base, B.ic(k, j) * b, b, 0),
+                    padded(opnd(BASE_WS, Soff[k] + boff * s_ld(SM[k], SN[k], R.order), s_ld(SM[k], SN[k], R.order), 1), SM[k]), r);
           u = 2.0 * p.ns[j] * (double)SM[k] * r;   // r == 0 writes a zero block
           boff += r;
         }
@@ -739,7 +767,9 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
           int32_t r = A.r(i, k);
           if (r > 0) {
             int64_t ao = s.kap(k, i0, i);
-            add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), opnd(BASE_WS, Soff[k] + ao, SM[k], 0), r);
+            // rows ao.. of S_k, read from S_k^T: N (beta) contiguous
+            const int64_t ls = s_ld(SM[k], SN[k], R.order);
+            add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), padded(opnd(BASE_WS, Soff[k] + ao * ls, ls, 1), SN[k]), r);
           }
           u = 2.0 * A.rs[i] * (double)SN[k] * r;
         }
@@ -829,6 +859,11 @@ static bool operand_ok(const DevOperand &o, int64_t rows, int64_t cols, bool is_
   int64_t a = first_contig ? rows : cols, c = first_contig ? cols : rows;
   (void)is_a;
   int64_t last = o.off + (a - 1) + (c - 1) * (int64_t)o.ld;
+  // a padded operand claims whole ld-strided vectors (and the pair loads use it)
+  if (o.flags & OPND_PADDED) {
+    if (o.ld <= a) return false;
+    last = o.off + c * (int64_t)o.ld - 1;
+  }
   return last < z.n[o.base];
 }
 

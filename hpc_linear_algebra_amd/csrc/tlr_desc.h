@@ -33,8 +33,13 @@ struct DevOperand {      // 16 bytes
   int32_t ld;
   uint8_t base;
   uint8_t trans;
-  uint16_t pad;
+  uint16_t flags;        // OperandFlags
 };
+
+// OPND_PADDED: ld exceeds the extent along the contiguous index and the buffer
+// holds every ld-strided vector whole, so the element one past that extent is
+// addressable (its value is unspecified).
+enum OperandFlags : uint16_t { OPND_PADDED = 1 };
 
 struct DevSeg {          // 40 bytes
   DevOperand a;
@@ -62,19 +67,22 @@ enum TaskFlags : uint8_t { TASK_VEC = 1 };
 // two adjacent elements per instruction: along M (PAIR_M, A M-contiguous) or
 // along K (PAIR_K, A K-contiguous) for A, and along the contiguous index for B.
 // A task qualifies for a pair mode when, for both operands of that segment,
-// the element offset and the leading dimension are even and the extent along
-// each paired index is even; the buffer bases must be aligned to a pair
-// (checked when the plan runs).
+// the element offset and the leading dimension are even (the buffer bases must
+// be aligned to a pair, checked when the plan runs) and every pair either lies
+// inside the operand or outside it, or straddles the end of an M or N extent
+// into a padded operand: the extra element then only feeds a row or column of
+// the output that is never stored.  Along K both elements of a pair must be
+// real, since the extra one would multiply the other operand's zero.
 enum LoadMode : int { LOAD_SINGLE = 0, LOAD_PAIR_M = 1, LOAD_PAIR_K = 2, NUM_LOAD_MODES = 3 };
 
 inline int task_load_mode(const DevTask &t) {
   if (t.nseg < 1) return LOAD_SINGLE;
   const DevSeg &s = t.seg[0];
-  const bool b_even = (s.b.off % 2) == 0 && (s.b.ld % 2) == 0 &&
-                      (s.b.trans == 1 ? (t.N % 2) == 0 : (s.K % 2) == 0);
-  const bool a_even = (s.a.off % 2) == 0 && (s.a.ld % 2) == 0;
-  if (!a_even || !b_even) return LOAD_SINGLE;
-  if (s.a.trans == 0) return (t.M % 2) == 0 ? LOAD_PAIR_M : LOAD_SINGLE;
+  const bool b_ok = (s.b.off % 2) == 0 && (s.b.ld % 2) == 0 &&
+                    (s.b.trans == 1 ? (t.N % 2) == 0 || (s.b.flags & OPND_PADDED) : (s.K % 2) == 0);
+  const bool a_ok = (s.a.off % 2) == 0 && (s.a.ld % 2) == 0;
+  if (!a_ok || !b_ok) return LOAD_SINGLE;
+  if (s.a.trans == 0) return (t.M % 2) == 0 || (s.a.flags & OPND_PADDED) ? LOAD_PAIR_M : LOAD_SINGLE;
   return (s.K % 2) == 0 ? LOAD_PAIR_K : LOAD_SINGLE;
 }
 

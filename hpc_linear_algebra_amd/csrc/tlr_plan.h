@@ -96,6 +96,11 @@ struct Plan {
   std::vector<void *> join_events;   // hipEvent_t, one per group
   std::vector<void *> dep_events;    // hipEvent_t, one per launch (recorded only when awaited)
   void *fork_event = nullptr;
+  // load-mode sub-launches of one launch run concurrently: two auxiliary
+  // streams per group, and per launch with several non-empty sub-tables one
+  // fork event and two join events (null otherwise)
+  std::vector<void *> aux_streams;   // hipStream_t, 2 per group
+  std::vector<void *> mode_events;   // hipEvent_t, 3 per launch
   int prof_max = 0, prof_count = 0;
   std::vector<void *> prof_events;   // 2 per launch per execute + 2 per execute (whole)
   ~Plan();
