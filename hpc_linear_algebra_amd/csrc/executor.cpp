@@ -306,7 +306,7 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
   t.c_base = BASE_C;
   t.final_ = 1;
   t.nseg = 1;
-  t.flags = ldc % 4 == 0 ? TASK_VEC : 0;
+  t.flags = ldc % (16 / (dt == TLR_F64 ? 8 : 4)) == 0 ? TASK_VEC : 0;
   t.seg[0].a.off = 0;
   t.seg[0].a.ld = (int32_t)lda;
   t.seg[0].a.base = BASE_A_OUTER;

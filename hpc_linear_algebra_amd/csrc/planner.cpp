@@ -1083,12 +1083,13 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   p->launches.clear();
   for (size_t g = 0; g < p->groups.size(); ++g)
     for (int r : p->groups[g].rects) emit_rect(*p, s, r);
-  // output columns that start on a 4-element boundary allow 4-row vector stores
+  // output columns that start on a 16-byte boundary allow 16-byte C accesses
+  const int64_t vec_el = 16 / p->es;
   for (DevTask &d : p->tasks) {
-    bool v = d.c_off % 4 == 0;
-    if (d.ctab < 0) v = v && d.ldc % 4 == 0;
+    bool v = d.c_off % vec_el == 0;
+    if (d.ctab < 0) v = v && d.ldc % vec_el == 0;
     else
-      for (int n = 0; n < d.N && v; ++n) v = p->coltab[d.ctab + n] % 4 == 0;
+      for (int n = 0; n < d.N && v; ++n) v = p->coltab[d.ctab + n] % vec_el == 0;
     d.flags = v ? TASK_VEC : 0;
   }
   // pipelining: the second stream starts once the first rectangle's stage 2

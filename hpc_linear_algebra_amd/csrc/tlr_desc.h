@@ -56,7 +56,7 @@ struct DevTask {         // 112 bytes
   uint8_t c_base;
   uint8_t final_;        // 1: alpha/beta update of C
   uint8_t nseg;
-  uint8_t flags;         // TASK_VEC: every output column starts 4-element aligned
+  uint8_t flags;         // TASK_VEC: every output column starts 16-byte aligned
   DevSeg seg[2];
 };
 
