@@ -276,7 +276,8 @@ def main():
                           "roof": round(roof, 2), "unit": "TFLOP/s", "frac": round(value / roof, 4),
                           "arith_intensity": round(ai, 2)},
         "stages_ms": {"stage1": round(stage_ms[0] / nexec, 4), "stage2": round(stage_ms[1] / nexec, 4),
-                      "stage3": round(stage_ms[2] / nexec, 4), "execute": round(stage_ms[3] / nexec, 4)},
+                      "stage3": round(stage_ms[2] / nexec, 4), "side": round(stage_ms[4] / nexec, 4),
+                      "execute": round(stage_ms[3] / nexec, 4)},
         "dense_reference": dense,
         "cpu_baseline": cpu,
     }

@@ -34,6 +34,9 @@ void plan_release_device(Plan *p) {
   destroy_events(p->dep_events);
   destroy_events(p->prof_events);
   destroy_events(p->mode_events);
+  destroy_events(p->side_events);
+  destroy_events(p->side_join);
+  p->forks_at.clear();
   for (void *s : p->aux_streams)
     if (s) (void)hipStreamDestroy(static_cast<hipStream_t>(s));
   p->aux_streams.clear();
@@ -87,8 +90,27 @@ tlr_status plan_bind(Plan *p, void *dev, size_t bytes, void *stream) {
     }
     split = split || parts > 1;
   }
-  if (split)
-    for (size_t i = 0; i < 2 * p->groups.size(); ++i) {
+  bool side = false;
+  p->forks_at.assign(p->launches.size(), {});
+  for (size_t l = 0; l < p->launches.size(); ++l) {
+    const Launch &L = p->launches[l];
+    hipEvent_t se = nullptr;
+    if (L.stage == STAGE_SIDE) {
+      HIP_TRY(hipEventCreateWithFlags(&se, hipEventDisableTiming));
+      p->forks_at[L.fork_at >= 0 ? (size_t)L.fork_at : l].push_back((int)l);
+      side = true;
+    }
+    p->side_events.push_back(se);
+  }
+  for (size_t g = 0; g < p->groups.size(); ++g) {
+    hipEvent_t je = nullptr;
+    bool any = false;
+    for (int l : p->groups[g].launches) any = any || p->launches[l].stage == STAGE_SIDE;
+    if (any) HIP_TRY(hipEventCreateWithFlags(&je, hipEventDisableTiming));
+    p->side_join.push_back(je);
+  }
+  if (split || side)
+    for (size_t i = 0; i < AUX_PER_GROUP * p->groups.size(); ++i) {
       hipStream_t as;
       HIP_TRY(hipStreamCreateWithFlags(&as, hipStreamNonBlocking));   // ordered by events only
       p->aux_streams.push_back(as);
@@ -114,7 +136,7 @@ tlr_status plan_profile(Plan *p, int max_exec) {
 }
 
 tlr_status plan_profile_read(Plan *p, double *stage_ms, double *launch_ms, int32_t *execs) {
-  for (int s = 0; s < 4; ++s) stage_ms[s] = 0;
+  for (int s = 0; s < 5; ++s) stage_ms[s] = 0;
   if (launch_ms)
     for (size_t l = 0; l < p->launches.size(); ++l) launch_ms[l] = 0;
   const size_t nl = p->launches.size();
@@ -128,7 +150,8 @@ tlr_status plan_profile_read(Plan *p, double *stage_ms, double *launch_ms, int32
       if (l == nl) {
         stage_ms[3] += ms;
       } else {
-        stage_ms[p->launches[l].stage - 1] += ms;
+        const int st = p->launches[l].stage;
+        stage_ms[st == STAGE_SIDE ? 4 : st - 1] += ms;
         if (launch_ms) launch_ms[l] += ms;
       }
     }
@@ -199,6 +222,12 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
     int si = p->groups[g].stream % n_streams;
     return streams ? static_cast<hipStream_t>(streams[si]) : nullptr;
   };
+  auto aux = [&](int g, int i) { return static_cast<hipStream_t>(p->aux_streams[AUX_PER_GROUP * g + i]); };
+  // the stream a launch runs on (its first load-mode part, for a split launch)
+  auto launch_stream = [&](int l) -> hipStream_t {
+    const Launch &L = p->launches[l];
+    return L.stage == STAGE_SIDE ? aux(L.group, AUX_PER_GROUP - 1) : stream_of(L.group);
+  };
   const bool prof = p->prof_count < p->prof_max;
   const size_t nl = p->launches.size();
   const size_t per = 2 * (nl + 1);
@@ -221,9 +250,28 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
     hipStream_t sg = stream_of((int)g);
     for (int l : p->groups[g].launches) {
       const Launch &L = p->launches[l];
+      const hipStream_t sl = launch_stream(l);
       if (L.wait_launch >= 0) {
-        hipStream_t sw = stream_of(p->launches[L.wait_launch].group);
-        if (sw != sg) HIP_TRY(hipStreamWaitEvent(sg, static_cast<hipEvent_t>(p->dep_events[L.wait_launch]), 0));
+        hipStream_t sw = launch_stream(L.wait_launch);
+        if (sw != sl) HIP_TRY(hipStreamWaitEvent(sl, static_cast<hipEvent_t>(p->dep_events[L.wait_launch]), 0));
+      }
+      // side launches fork here: after everything enqueued on the group's
+      // stream so far (earlier rectangles of the arena included), before l
+      for (int d : p->forks_at[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->side_events[d]), sg));
+      if (L.stage == STAGE_SIDE) {
+        HIP_TRY(hipStreamWaitEvent(sl, static_cast<hipEvent_t>(p->side_events[l]), 0));
+        if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sl));
+        // load-mode parts one after another on the side stream
+        for (int m = 0; m < NUM_LOAD_MODES; ++m) {
+          if (pairs_ok ? L.mode_tiles[m] == 0 : m > 0) continue;
+          const int mode = pairs_ok ? m : LOAD_SINGLE;
+          const int64_t off = pairs_ok ? L.mode_off[m] : 0, n = pairs_ok ? L.mode_tiles[m] : L.n_tiles;
+          int e = launch_grouped(p->dt, L.stage, mode, tasks, tiles + L.tile_off + off, n, ctab, bases, alpha, beta, sl);
+          if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
+        }
+        if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sl));
+        if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sl));
+        continue;
       }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
       if (pairs_ok) {
@@ -237,7 +285,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
           if (L.mode_tiles[m] == 0) continue;
           hipStream_t sm = sg;
           if (part > 0) {
-            sm = static_cast<hipStream_t>(p->aux_streams[2 * L.group + part - 1]);
+            sm = aux(L.group, part - 1);
             HIP_TRY(hipStreamWaitEvent(sm, fork, 0));
           }
           int e = launch_grouped(p->dt, L.stage, m, tasks, tiles + L.tile_off + L.mode_off[m], L.mode_tiles[m],
@@ -257,6 +305,11 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
       }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));
       if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sg));
+    }
+    if (p->side_join[g]) {   // every side launch of the group ends before the group does
+      hipEvent_t je = static_cast<hipEvent_t>(p->side_join[g]);
+      HIP_TRY(hipEventRecord(je, aux((int)g, AUX_PER_GROUP - 1)));
+      HIP_TRY(hipStreamWaitEvent(sg, je, 0));
     }
   }
   for (size_t g = 0; g < p->groups.size(); ++g) {

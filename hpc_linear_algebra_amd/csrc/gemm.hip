@@ -527,8 +527,10 @@ void launch_grouped_t(int stage, int mode, unsigned n, hipStream_t s, const DevT
     launch_grouped_s<T, 1>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
   else if (stage == 2)
     launch_grouped_s<T, 2>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
-  else
+  else if (stage == 3)
     launch_grouped_s<T, 3>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else
+    launch_grouped_s<T, STAGE_SIDE>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
 }
 
 template <typename T>

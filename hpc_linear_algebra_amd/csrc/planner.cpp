@@ -509,13 +509,15 @@ static double task_exec_flops(const DevTask &d) {
 // Lists are padded with idle entries to a common length, so every sub-table
 // is a multiple of NUM_XCD entries and the XCD of an entry does not depend on
 // which sub-tables precede it.
-static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
-  if (tl.t.empty()) return;
+// Appends one launch of `tl` (nothing when empty) and returns its index, or -1.
+static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
+  if (tl.t.empty()) return -1;
   Launch L;
   L.stage = stage;
   L.group = group;
   L.rect = rect;
   L.wait_launch = -1;
+  L.fork_at = -1;
   L.n_tasks = (int64_t)tl.t.size();
   L.useful_flops = 0;
   L.executed_flops = 0;
@@ -560,6 +562,24 @@ static void emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.n_tiles = (int64_t)p.tiles.size() - L.tile_off;
   p.launches.push_back(L);
   p.groups[group].launches.push_back((int)p.launches.size() - 1);
+  return (int)p.launches.size() - 1;
+}
+
+// Launches of one rectangle: the coupling (stage 1), then the diagonal-term
+// products that read only inputs on the side stream (forked before stage 1, so
+// they run beside stages 1 and 2), the right/left product (stage 2) and the
+// final update (stage 3), which waits for the side launch.
+static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &side, TaskList &l2,
+                        TaskList &l3) {
+  const int a = emit_launch(p, 1, group, rect, l1);
+  const int d = emit_launch(p, STAGE_SIDE, group, rect, side);
+  const int b = emit_launch(p, 2, group, rect, l2);
+  const int c = emit_launch(p, 3, group, rect, l3);
+  if (d < 0) return;
+  // fork before the first launch of the group's stream that follows in this
+  // rectangle, or at the group's end when there is none
+  p.launches[d].fork_at = a >= 0 ? a : (b >= 0 ? b : c);
+  if (c >= 0) p.launches[c].wait_launch = d;
 }
 
 static void emit_rect(Plan &p, const Sums &s, int rect) {
@@ -635,7 +655,7 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
     SN[k] = s.bet(k, j0, j1);
     if (SM[k] > 0 && SN[k] > 0) Soff[k] = take((size_t)s_elems(SM[k], SN[k], R.order) * es);
   }
-  TaskList l1, l2, l3;
+  TaskList l1, ls, l2, l3;
   for (int k = 0; k < qk; ++k) {
     if (Soff[k] < 0) continue;
     const int64_t ls = s_ld(SM[k], SN[k], R.order);
@@ -659,15 +679,15 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
       if (s.rho[i] > 0) Toff[i] = take((size_t)WJ * s.rho[i] * es);
       if (A.diag && s.bet(i, j0, j1) > 0) Xoff[i] = take((size_t)A.rs[i] * s.bet(i, j0, j1) * es);
     }
-    // X_i = op(D_A,ii) W_{i,J}
+    // X_i = op(D_A,ii) W_{i,J} (inputs only: side launch)
     if (A.diag)
       for (int i = i0; i < i1; ++i) {
         int64_t bi = s.bet(i, j0, j1);
         if (bi == 0) continue;
         DevTask d = new_task(A.rs[i], bi, BASE_WS, Xoff[i], A.rs[i], -1, false);
         add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans), opnd(B.outer_base, B.oc(i, j0) * b, b, 0), A.rs[i]);
-        l1.t.push_back(d);
-        l1.useful.push_back(2.0 * A.rs[i] * (double)A.rs[i] * bi);
+        ls.t.push_back(d);
+        ls.useful.push_back(2.0 * A.rs[i] * (double)A.rs[i] * bi);
       }
     // column maps: coupling row (i, a) of contraction tile k -> column p_i(k)+a of T_i^T
     std::vector<int64_t> ctab(qk, -1);
@@ -685,22 +705,22 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
       int64_t boff = 0;   // column offset of block j inside S_k
       for (int j = j0; j < j1; ++j) {
         DevTask d = new_task(p.ns[j], SM[k], BASE_WS, cJ(j), 0, ctab[k], false);
-        double u = 0;
         if (B.diag && k == j) {
-          // T_i[j-block rows, j-block cols] = V_ij^T D_B,jj, stored transposed: D^T V
+          // T_i[j-block rows, j-block cols] = V_ij^T D_B,jj, stored transposed:
+          // D^T V (inputs only: side launch)
           add_seg(d, opnd(B.diag_base, (int64_t)j * b * b, b, B.diag_trans ? 0 : 1),
                   opnd(A.inner_base, A.ic(i0, j) * b, b, 0), p.ns[j]);
-          u = 2.0 * p.ns[j] * (double)p.ns[j] * SM[k];
-        } else {
-          int32_t r = B.r(k, j);
-          if (r > 0)
-            add_seg(d, opnd(B.inner_base, B.ic(k, j) * b, b, 0),
-                    padded(opnd(BASE_WS, Soff[k] + boff * s_ld(SM[k], SN[k], R.order), s_ld(SM[k], SN[k], R.order), 1), SM[k]), r);
-          u = 2.0 * p.ns[j] * (double)SM[k] * r;   // r == 0 writes a zero block
-          boff += r;
+          ls.t.push_back(d);
+          ls.useful.push_back(2.0 * p.ns[j] * (double)p.ns[j] * SM[k]);
+          continue;
         }
+        const int32_t r = B.r(k, j);
+        if (r > 0)
+          add_seg(d, opnd(B.inner_base, B.ic(k, j) * b, b, 0),
+                  padded(opnd(BASE_WS, Soff[k] + boff * s_ld(SM[k], SN[k], R.order), s_ld(SM[k], SN[k], R.order), 1), SM[k]), r);
+        boff += r;
         l2.t.push_back(d);
-        l2.useful.push_back(u);
+        l2.useful.push_back(2.0 * p.ns[j] * (double)SM[k] * r);   // r == 0 writes a zero block
       }
     }
     for (int i = i0; i < i1; ++i) {
@@ -734,15 +754,15 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
       if (s.gam[j] > 0) Yoff[j] = take((size_t)WI * s.gam[j] * es);
       if (B.diag && s.kap(j, i0, i1) > 0) Xoff[j] = take((size_t)s.kap(j, i0, i1) * p.ns[j] * es);
     }
-    // X'_j = V_{I,j}^T op(D_B,jj)
+    // X'_j = V_{I,j}^T op(D_B,jj) (inputs only: side launch)
     if (B.diag)
       for (int j = j0; j < j1; ++j) {
         int64_t kj = s.kap(j, i0, i1);
         if (kj == 0) continue;
         DevTask d = new_task(kj, p.ns[j], BASE_WS, Xoff[j], kj, -1, false);
         add_seg(d, opnd(A.inner_base, A.ic(i0, j) * b, b, 1), opnd(B.diag_base, (int64_t)j * b * b, b, B.diag_trans), p.ns[j]);
-        l1.t.push_back(d);
-        l1.useful.push_back(2.0 * kj * (double)p.ns[j] * p.ns[j]);
+        ls.t.push_back(d);
+        ls.useful.push_back(2.0 * kj * (double)p.ns[j] * p.ns[j]);
       }
     // column maps: coupling column (j, a) of contraction tile k -> column p'_j(k)+a of Y_j
     std::vector<int64_t> ytab(qk, -1);
@@ -759,22 +779,22 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
       for (int k = 0; k < qk; ++k) {
         if (SN[k] == 0) continue;
         DevTask d = new_task(A.rs[i], SN[k], BASE_WS, rI(i), 0, ytab[k], false);
-        double u = 0;
         if (A.diag && k == i) {
+          // Y_j[i rows, k = i block] = op(D_A,ii) W_ij (inputs only: side launch)
           add_seg(d, opnd(A.diag_base, (int64_t)i * b * b, b, A.diag_trans), opnd(B.outer_base, B.oc(i, j0) * b, b, 0), A.rs[i]);
-          u = 2.0 * A.rs[i] * (double)A.rs[i] * SN[k];
-        } else {
-          int32_t r = A.r(i, k);
-          if (r > 0) {
-            int64_t ao = s.kap(k, i0, i);
-            // rows ao.. of S_k, read from S_k^T: N (beta) contiguous
-            const int64_t ls = s_ld(SM[k], SN[k], R.order);
-            add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), padded(opnd(BASE_WS, Soff[k] + ao * ls, ls, 1), SN[k]), r);
-          }
-          u = 2.0 * A.rs[i] * (double)SN[k] * r;
+          ls.t.push_back(d);
+          ls.useful.push_back(2.0 * A.rs[i] * (double)A.rs[i] * SN[k]);
+          continue;
+        }
+        const int32_t r = A.r(i, k);
+        if (r > 0) {
+          const int64_t ao = s.kap(k, i0, i);
+          // rows ao.. of S_k, read from S_k^T: N (beta) contiguous
+          const int64_t lt = s_ld(SM[k], SN[k], R.order);
+          add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), padded(opnd(BASE_WS, Soff[k] + ao * lt, lt, 1), SN[k]), r);
         }
         l2.t.push_back(d);
-        l2.useful.push_back(u);
+        l2.useful.push_back(2.0 * A.rs[i] * (double)SN[k] * r);
       }
     }
     for (int j = j0; j < j1; ++j) {
@@ -802,9 +822,7 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
       }
     }
   }
-  emit_launch(p, 1, R.group, rect, l1);
-  emit_launch(p, 2, R.group, rect, l2);
-  emit_launch(p, 3, R.group, rect, l3);
+  emit_stages(p, R.group, rect, l1, ls, l2, l3);
 }
 
 static double compressed_elems(const View &v) {
@@ -954,7 +972,14 @@ static tlr_status validate(const Plan &p, bool deep) {
         rect_hi = (int64_t)((G.arena_off + G.arena_bytes) / (size_t)p.es);
         std::fill(ws.begin() + rect_lo, ws.begin() + rect_hi, 0);
       }
+      // workspace marks: the writer's stage.  A stage reads what earlier
+      // stages of its rectangle wrote; the side launch runs beside stages 1
+      // and 2, so only the final update may read it, and it reads no workspace
       const uint8_t me = (uint8_t)L.stage;
+      auto readable = [&](uint8_t w) {
+        if (w == 0 || me == STAGE_SIDE) return false;
+        return w == STAGE_SIDE ? me == 3 : w < me;
+      };
       // collect distinct tasks of the launch
       std::vector<int32_t> tl;
       for (int64_t e = L.tile_off; e < L.tile_off + L.n_tiles; ++e)
@@ -968,10 +993,10 @@ static tlr_status validate(const Plan &p, bool deep) {
             const DevOperand &o = w == 0 ? d.seg[s].a : d.seg[s].b;
             if (o.base != BASE_WS) continue;
             bool ok = w == 0 ? for_elems(o, d.M, d.seg[s].K, [&](int64_t e) {
-                                 return e >= rect_lo && e < rect_hi && ws[e] != 0 && ws[e] < me;
+                                 return e >= rect_lo && e < rect_hi && readable(ws[e]);
                                })
                              : for_elems(o, d.seg[s].K, d.N, [&](int64_t e) {
-                                 return e >= rect_lo && e < rect_hi && ws[e] != 0 && ws[e] < me;
+                                 return e >= rect_lo && e < rect_hi && readable(ws[e]);
                                });
             if (!ok) return fail(TLR_ERR_INVALID_ARG, "internal: workspace read before it is written (task " + std::to_string(ti) + ")");
           }

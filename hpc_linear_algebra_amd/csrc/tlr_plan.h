@@ -15,6 +15,7 @@ constexpr int BM = 128;            // workgroup block of every grouped launch
 constexpr int BN = 128;
 constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
 constexpr int NUM_XCD = 8;         // MI355X: workgroups go round-robin over 8 XCDs
+constexpr int AUX_PER_GROUP = 3;   // auxiliary streams of a group: two for load modes, one side lane
 
 // One operand after op: tile (i,j) of op(X) is Outer_ij Inner_ij^T, or the
 // dense diagonal (transposed when op = T).
@@ -39,11 +40,19 @@ struct Rect {
   double useful_flops;
 };
 
+// Stage 4 holds the products of the diagonal terms that read only the inputs
+// (X = D W or X' = V^T D, and the D W / D^T V blocks of the terminal
+// matrices).  It runs on the group's side stream, forked from the group's
+// stream just before `fork_at` is enqueued, beside stages 1 and 2; the final
+// update waits for it.
+constexpr int STAGE_SIDE = 4;
+
 struct Launch {
-  int stage;         // 1, 2, 3
+  int stage;         // 1, 2, 3, or STAGE_SIDE
   int group;
   int rect;
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
+  int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
   int64_t tile_off;  // first DevTile of the launch in the tile table
   int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)
   // the table is the concatenation of one sub-table per load mode (each a
@@ -98,9 +107,14 @@ struct Plan {
   void *fork_event = nullptr;
   // load-mode sub-launches of one launch run concurrently: two auxiliary
   // streams per group, and per launch with several non-empty sub-tables one
-  // fork event and two join events (null otherwise)
-  std::vector<void *> aux_streams;   // hipStream_t, 2 per group
+  // fork event and two join events (null otherwise); a third auxiliary stream
+  // per group carries its side launches, forked by side_events[l] (null
+  // unless l is a side launch) and joined at the group's end by side_join
+  std::vector<void *> aux_streams;   // hipStream_t, AUX_PER_GROUP per group
   std::vector<void *> mode_events;   // hipEvent_t, 3 per launch
+  std::vector<void *> side_events;   // hipEvent_t, 1 per launch
+  std::vector<void *> side_join;     // hipEvent_t, 1 per group
+  std::vector<std::vector<int>> forks_at;   // per launch: the side launches forked just before it
   int prof_max = 0, prof_count = 0;
   std::vector<void *> prof_events;   // 2 per launch per execute + 2 per execute (whole)
   ~Plan();

@@ -221,7 +221,7 @@ def tlr_plan_profile(p: Plan, max_executes: int):
 
 
 def tlr_plan_profile_read(p: Plan, launches: int):
-    st_ms = (c_double * 4)()
+    st_ms = (c_double * 5)()
     l_ms = (c_double * max(1, launches))()
     ex = c_int32()
     _check(lib().tlr_plan_profile_read(p.h, st_ms, l_ms, ctypes.byref(ex)), "tlr_plan_profile_read")

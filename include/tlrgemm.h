@@ -198,7 +198,11 @@ tlr_status tlr_plan_stage_shapes(const tlr_plan *p, int32_t rect, int32_t stage,
 
 /*
  * tlr_plan_launch: launch `idx` (0 <= idx < launches) of one execute.
- *   out_i32[0..3] = stage (1, 2 or 3), tasks, workgroups, group.
+ *   out_i32[0..3] = stage, tasks, workgroups, group.  Stages: 1 coupling,
+ *   2 right/left product, 3 final update, 4 the diagonal-term products that
+ *   read only the inputs (X = op(D_A) W or X' = V^T op(D_B), and the op(D_A) W
+ *   or op(D_B)^T V blocks of the terminal matrices; the "easy terms" of "TLR
+ *   Matrix Multiplication"), run on a side stream beside stages 1 and 2.
  *   out_f64[0..1] = useful flops, executed flops of the launch.
  */
 tlr_status tlr_plan_launch(const tlr_plan *p, int32_t idx, int32_t *out_i32, double *out_f64);
@@ -244,8 +248,10 @@ tlr_status tlr_gemm_execute(tlr_plan *p, double alpha,
  * `max_executes` executes (0 switches recording off).  Creates the events on
  * the current device.  Errors: TLR_ERR_HIP.
  * tlr_plan_profile_read: after the caller has synchronised, sum the recorded
- * kernel time per stage: stage_ms[0..2] = stages 1..3, stage_ms[3] = the whole
- * execute (first launch start to last launch end on streams[0]);
+ * kernel time per stage into stage_ms[5]: stage_ms[0..2] = stages 1..3,
+ * stage_ms[3] = the whole execute (first launch start to last launch end on
+ * streams[0]), stage_ms[4] = stage 4 (the side launches, which overlap stages
+ * 1 and 2);
  * launch_ms (may be NULL) receives the per-launch sums, `launches` entries.
  * *executes = executes recorded.  Resets the record.
  */

@@ -226,3 +226,34 @@ def test_empty_and_degenerate():
     R = np.zeros((3, 3), dtype=np.int32)
     p = T.tlr_gemm_analyze("f64", "N", T.Shape(12, 12, 4, R, True), "N", T.Shape(12, 12, 4, R, True), ldc=12)
     assert T.tlr_plan_info(p)["useful_flops"] == 3 * 2 * 4 ** 3
+
+
+@pytest.mark.parametrize("order", [T.TLR_PLAN_FORCE_RIGHT, T.TLR_PLAN_FORCE_LEFT])
+def test_side_launch_holds_the_diagonal_terms(order):
+    # with dense diagonal tiles the input-only diagonal products form a side
+    # launch (stage 4) between the coupling and the right/left product of each
+    # rectangle; its useful flops are exactly those products'
+    rng = np.random.default_rng(31)
+    n, b = 640, 64
+    sz = tile_sizes(n, b)
+    q = len(sz)
+    RA, RB = _rand_ranks(rng, q, b, True, 1, 12), _rand_ranks(rng, q, b, True, 1, 12)
+    A, B = T.Shape(n, n, b, RA, True), T.Shape(n, n, b, RB, True)
+    p = T.tlr_gemm_analyze("f64", "N", A, "N", B, ldc=n, flags=order | T.TLR_PLAN_VALIDATE)
+    info = T.tlr_plan_info(p)
+    L = [T.tlr_plan_launch(p, l) for l in range(info["launches"])]
+    assert [x["stage"] for x in L] == [1, 4, 2, 3]
+    if order == T.TLR_PLAN_FORCE_RIGHT:
+        # X_i = D_A,ii W_{i,:} and the D_B,jj^T V_{:,j} blocks of T
+        want = sum(2 * b * b * int(RB[i, :].sum()) for i in range(q)) + \
+            sum(2 * b * b * int(RA[:, j].sum()) for j in range(q))
+    else:
+        # X'_j = V_{:,j}^T D_B,jj and the D_A,ii W_{i,:} blocks of Y
+        want = sum(2 * b * b * int(RA[:, j].sum()) for j in range(q)) + \
+            sum(2 * b * b * int(RB[i, :].sum()) for i in range(q))
+    assert L[1]["useful_flops"] == want
+    assert sum(x["useful_flops"] for x in L) == info["useful_flops"]
+    # no diagonal: no side launch
+    A0, B0 = T.Shape(n, n, b, RA, False), T.Shape(n, n, b, RB, False)
+    p0 = T.tlr_gemm_analyze("f64", "N", A0, "N", B0, ldc=n, flags=order)
+    assert [T.tlr_plan_launch(p0, l)["stage"] for l in range(T.tlr_plan_info(p0)["launches"])] == [1, 2, 3]
