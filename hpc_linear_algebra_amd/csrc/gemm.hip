@@ -8,15 +8,15 @@
 // Layout of the descriptors: tlr_desc.h.  Each stage gets its own kernel symbol
 // so that profilers report the stages separately.
 //
-// Work split: four wave64s, 2 x 2, each owning a 64 x 64 quarter of the block
-// as 4 x 4 MFMA tiles of 16 x 16 (v_mfma_f64_16x16x4_f64 /
+// Work split: four wave64s stacked along M, each owning a 32 x 128 strip of
+// the block as 2 x 8 MFMA tiles of 16 x 16 (v_mfma_f64_16x16x4_f64 /
 // v_mfma_f32_16x16x4_f32).  K advances in stages of 16.  The A operand goes
 // from global memory straight into registers in MFMA operand order (each wave
-// loads its own 64 rows; no LDS round trip), refilled for the next stage as the
-// current stage's MFMAs release each register.  The B operand, shared by the
-// two waves of a column, is staged through a double-buffered LDS tile whose
-// global loads are in flight during the previous stage.  Registers are sized
-// for two workgroups per CU (two waves per SIMD).
+// loads its own 32 rows; no LDS round trip), refilled for the next stage as the
+// current stage's MFMAs release each register.  The B operand, shared by all
+// four waves, is staged through a three-buffer LDS ring, its global loads one
+// stage ahead of the LDS store and the LDS fragments one k-step ahead of the
+// MFMAs.  Registers are sized for two workgroups per CU (two waves per SIMD).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,7 +35,7 @@ namespace {
 constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 17;
 constexpr int LDS_B = KBN + KPAD;
 constexpr int NT = 256;               // threads per workgroup: four wave64s
-constexpr int WM = 32, WN = 128;      // per-wave block: four waves stacked along M
+constexpr int WM = 32;               // rows per wave: four waves stacked along M, 128 columns each
 constexpr int MI = 2, NJ = 8;         // 16 x 16 MFMA tiles per wave
 constexpr int EPT = KBN * KBK / NT;   // B elements per thread per stage
 
@@ -266,6 +266,19 @@ __device__ __forceinline__ void store_b(const BMap &m, const T (&rb)[EPT], T *Bs
   }
 }
 
+// One K segment.  Pipeline of a stage st (16 k, four k-steps q):
+//   k-step q:  LDS fragments of step q+1 are read while step q's MFMAs run
+//              (fragments double-buffered in registers), and A for stage
+//              st+1 is loaded into the registers step q just released;
+//   after q=1: the B tile of stage st+1 (loaded from global memory one
+//              stage earlier) goes to LDS buffer (st+1)%3, one barrier, and
+//              the global loads of stage st+2's B tile are issued;
+//   k-step 3:  reads stage st+1's first fragments from the new buffer.
+// Three LDS buffers make one barrier per stage enough: buffer (st+1)%3 was
+// last read in stage st-2, before every wave passed stage st-1's barrier.
+// The barrier sits mid-stage, with two k-steps of MFMAs (and their operands)
+// still to issue behind it, so a wave that waits there loses no fragment
+// latency.  B loads past the end of K come back as zeros and are never used.
 template <typename T, int MODE>
 __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int g, int r, int wn,
                                             T (*Bs)[KBK * LDS_B], typename Mfma<T>::v4 (&acc)[MI][NJ]) {
@@ -277,38 +290,50 @@ __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int 
   const BMap bm = b_map<MODE, T>(c.b_xc, c.ldb, tid);
   T fa[MI][4];
   T rb[EPT];
+  T bf[2][NJ];
+  auto read_b = [&](const T *Bb, int q, T (&b)[NJ]) {
+    const T *br = Bb + (kq_of<MODE>(q) + kg_of<MODE>(g)) * LDS_B + wn + r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[j] = br[16 * j];
+  };
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_a<T, MODE>(c, 0, q, fa);
   load_b<T, MODE>(c, bm, 0, rb);
-  __syncthreads();   // the previous segment's last reads of buffer 0 are done
+  __syncthreads();   // the previous segment's last reads of every buffer are done
   store_b<MODE>(bm, rb, Bs[0]);
+  load_b<T, MODE>(c, bm, KBK, rb);   // stage 1 (zeros when there is none)
   __syncthreads();
-  // One K stage: MFMAs on LDS buffer st & 1 and on fa; with MORE the next
-  // stage's loads are issued as their registers free up.  The last stage is
-  // peeled so that the loop body holds no conditional loads (a load under a
-  // branch makes the compiler wait for every outstanding load at the join).
+  read_b(Bs[0], 0, bf[0]);
+  // The last stage is peeled so that the loop body holds no conditional loads
+  // (a load under a branch makes the compiler wait for every outstanding load
+  // at the join).
+  int cur = 0;   // LDS buffer of stage st: st % 3
   auto stage = [&](int st, auto more_tag) {
     constexpr bool MORE = decltype(more_tag)::value;
     const int k1 = (st + 1) * KBK;
-    if (MORE) load_b<T, MODE>(c, bm, k1, rb);
-    const T *Bb = Bs[st & 1];
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    const T *Bb = Bs[cur];
 #pragma unroll
     for (int q = 0; q < KBK / 4; ++q) {
       if (!MORE && kq_of<MODE>(q) >= klast) continue;   // every k of this step is past K
-      const T *br = Bb + (kq_of<MODE>(q) + kg_of<MODE>(g)) * LDS_B + wn + r;
-      T b[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) b[j] = br[16 * j];
+      T(&b)[NJ] = bf[q & 1];
+      if (q + 1 < KBK / 4) {
+        if (MORE || kq_of<MODE>(q + 1) < klast) read_b(Bb, q + 1, bf[(q + 1) & 1]);
+      } else if (MORE) {
+        read_b(Bs[nxt], 0, bf[0]);
+      }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(fa[i][q], b[j], acc[i][j]);
       if (MORE) load_a<T, MODE>(c, k1, q, fa);
+      if (MORE && q == 1) {
+        store_b<MODE>(bm, rb, Bs[nxt]);
+        __syncthreads();
+        load_b<T, MODE>(c, bm, k1 + KBK, rb);
+      }
     }
-    if (MORE) {
-      store_b<MODE>(bm, rb, Bs[(st + 1) & 1]);
-      __syncthreads();
-    }
+    cur = nxt;
   };
   for (int st = 0; st + 1 < nst; ++st) stage(st, std::true_type{});
   stage(nst - 1, std::false_type{});
@@ -318,7 +343,7 @@ template <typename T, int MODE0>
 __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, const int64_t *coltab,
                                            const Bases &bases, T alpha, T beta, T cscale) {
   typedef typename Mfma<T>::v4 v4;
-  __shared__ T Bs[2][KBK * LDS_B];
+  __shared__ T Bs[3][KBK * LDS_B];
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave: readfirstlane tells the compiler
   // so, which keeps operand addresses and buffer resources in scalar registers
@@ -416,14 +441,26 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
   if (nseg > 0) { SegCtx<T> c; setup(t.seg[0], c); run_segment<T, MODE0>(c, tid, arow, g, r, wn, Bs, acc); }
   if (nseg > 1) { SegCtx<T> c; setup(t.seg[1], c); run_segment<T, SINGLE>(c, tid, arow, g, r, wn, Bs, acc); }
 
-  // epilogue: one 16-byte unit per lane, column and u (when the column start is
-  // 16-byte aligned)
+  // Epilogue: one 16-byte unit per lane, column and u (when the column start is
+  // 16-byte aligned).  Every column offset is read before the first store:
+  // the memory counter that a wait for a column-map load uses also counts the
+  // stores issued before it, so a map lookup between stores would wait for
+  // all of them to complete.
+  int64_t ocol[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn + 16 * j + r;
+    ocol[j] = n >= N ? 0 : (t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n]);
+  }
+  // The stores keep their per-unit checks even for a slice wholly inside the
+  // task: a branch-free run of 32 back-to-back stores per wave measured slower,
+  // since the burst holds up the co-resident workgroup's operand loads in the
+  // CU's shared memory pipeline.
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn + 16 * j + r;
     if (n >= N) continue;
-    const int64_t col = t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n];
-    T *cp = C + col;
+    T *cp = C + ocol[j];
 #pragma unroll
     for (int h = 0; h < MI / 2; ++h) {
 #pragma unroll

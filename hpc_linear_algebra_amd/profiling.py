@@ -47,10 +47,11 @@ def trace_stats(dirs, command: str) -> str:
                     groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     tot_all = sum(sum(v) for v in groups.values()) or 1.0
     out = [f"Command: `{command}`", "",
-           "| kernel | workgroups | calls | total ms | avg us | min us | max us | % |",
-           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+           "| kernel | workgroups | calls | total ms | avg us | median us | min us | max us | % |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for (k, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        out.append(f"| {k} | {wg} | {len(v)} | {sum(v)/1e3:.3f} | {sum(v)/len(v):.1f} | {min(v):.1f} | "
+        med = sorted(v)[len(v) // 2]
+        out.append(f"| {k} | {wg} | {len(v)} | {sum(v)/1e3:.3f} | {sum(v)/len(v):.1f} | {med:.1f} | {min(v):.1f} | "
                    f"{max(v):.1f} | {100*sum(v)/tot_all:.1f} |")
     return "\n".join(out) + "\n"
 
