@@ -32,12 +32,19 @@ namespace {
 // LDS rows of the B tile hold 145 elements: an odd stride sends the 16 k-rows
 // that one K-contiguous store touches to 16 different banks, and a 16-element
 // fragment read still covers each bank once.
-constexpr int KBM = 128, KBN = 128, KBK = 16, KPAD = 17;
-constexpr int LDS_B = KBN + KPAD;
+constexpr int KBM = 128, KBK = 16, KPAD = 17;
 constexpr int NT = 256;               // threads per workgroup: four wave64s
 constexpr int WM = 32;               // rows per wave: four waves stacked along M, 128 columns each
-constexpr int MI = 2, NJ = 8;         // 16 x 16 MFMA tiles per wave
-constexpr int EPT = KBN * KBK / NT;   // B elements per thread per stage
+constexpr int MI = 2;                 // 16-row MFMA tiles per wave
+// Block width: NJ 16-column MFMA tiles per wave (NJ = 8: 128 x 128 blocks,
+// NJ = 4: 128 x 64 blocks with half the accumulators, for launches whose
+// tasks are too few or too short to fill the chip with 128 x 128 blocks).
+template <int NJ> struct Blk {
+  static constexpr int KBN = 16 * NJ;             // block columns
+  static constexpr int LDS_B = KBN + KPAD;        // LDS row stride of the B tile (odd)
+  static constexpr int EPT = KBN * KBK / NT;      // B elements per thread per stage
+  static constexpr int WAVES_PER_EU = NJ == 8 ? 2 : 3;
+};
 
 // Lane layout of the 16x16x4 MFMAs (measured on gfx950): lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16]; accumulator element v of lane l is
@@ -199,13 +206,14 @@ struct BMap {
   int32_t lds, lds_step, lds2;
 };
 
-template <int MODE, typename T>
+template <int MODE, int NJ, typename T>
 __device__ __forceinline__ BMap b_map(bool xc, int32_t ld, int tid) {
+  constexpr int KBN = Blk<NJ>::KBN, LDS_B = Blk<NJ>::LDS_B;
   BMap m;
   int32_t lin, st;
   if (MODE == SINGLE) {
     if (xc) {   // lanes walk n
-      m.x = tid & 127; m.dx = 0; m.k = tid >> 7; m.dk = NT / 128;
+      m.x = tid % KBN; m.dx = 0; m.k = tid / KBN; m.dk = NT / KBN;
       lin = m.x + m.k * ld; st = m.dk * ld;
     } else {    // lanes walk k
       m.k = tid & 15; m.dk = 0; m.x = tid >> 4; m.dx = NT / 16;
@@ -213,8 +221,8 @@ __device__ __forceinline__ BMap b_map(bool xc, int32_t ld, int tid) {
     }
     m.lds2 = 0;
   } else {
-    if (xc) {   // pairs along n: 64 pairs cover a k-row
-      m.x = 2 * (tid & 63); m.dx = 0; m.k = tid >> 6; m.dk = NT / 64;
+    if (xc) {   // pairs along n: KBN / 2 pairs cover a k-row
+      m.x = 2 * (tid % (KBN / 2)); m.dx = 0; m.k = tid / (KBN / 2); m.dk = NT / (KBN / 2);
       lin = m.x + m.k * ld; st = m.dk * ld;
       m.lds2 = 1;
     } else {    // pairs along k: 8 pairs cover a column
@@ -230,7 +238,7 @@ __device__ __forceinline__ BMap b_map(bool xc, int32_t ld, int tid) {
   return m;
 }
 
-template <typename T, int MODE>
+template <typename T, int MODE, int NJ, int EPT = Blk<NJ>::EPT>
 __device__ __forceinline__ void load_b(const SegCtx<T> &c, const BMap &m, int k0, T (&rb)[EPT]) {
   const int krem = c.K - k0;
   const __amdgpu_buffer_rsrc_t rs = rsrc(c.b_xc ? c.b + (int64_t)k0 * c.ldb : c.b + k0);
@@ -251,7 +259,7 @@ __device__ __forceinline__ void load_b(const SegCtx<T> &c, const BMap &m, int k0
   }
 }
 
-template <int MODE, typename T>
+template <int MODE, int NJ, typename T, int EPT = Blk<NJ>::EPT>
 __device__ __forceinline__ void store_b(const BMap &m, const T (&rb)[EPT], T *Bs) {
   if (MODE == SINGLE) {
 #pragma unroll
@@ -279,15 +287,16 @@ __device__ __forceinline__ void store_b(const BMap &m, const T (&rb)[EPT], T *Bs
 // The barrier sits mid-stage, with two k-steps of MFMAs (and their operands)
 // still to issue behind it, so a wave that waits there loses no fragment
 // latency.  B loads past the end of K come back as zeros and are never used.
-template <typename T, int MODE>
+template <typename T, int MODE, int NJ>
 __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int g, int r, int wn,
-                                            T (*Bs)[KBK * LDS_B], typename Mfma<T>::v4 (&acc)[MI][NJ]) {
+                                            T (*Bs)[KBK * Blk<NJ>::LDS_B], typename Mfma<T>::v4 (&acc)[MI][NJ]) {
+  constexpr int LDS_B = Blk<NJ>::LDS_B, EPT = Blk<NJ>::EPT;
   const int nst = (c.K + KBK - 1) / KBK;
   if (nst <= 0) return;
   c.gk = kg_of<MODE>(g);
   c.a_lane = (uint32_t)(c.row2 * c.sr + c.gk * c.sk) * (uint32_t)sizeof(T);
   const int klast = c.K - (nst - 1) * KBK;   // valid k of the last stage
-  const BMap bm = b_map<MODE, T>(c.b_xc, c.ldb, tid);
+  const BMap bm = b_map<MODE, NJ, T>(c.b_xc, c.ldb, tid);
   T fa[MI][4];
   T rb[EPT];
   T bf[2][NJ];
@@ -298,10 +307,10 @@ __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int 
   };
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_a<T, MODE>(c, 0, q, fa);
-  load_b<T, MODE>(c, bm, 0, rb);
+  load_b<T, MODE, NJ>(c, bm, 0, rb);
   __syncthreads();   // the previous segment's last reads of every buffer are done
-  store_b<MODE>(bm, rb, Bs[0]);
-  load_b<T, MODE>(c, bm, KBK, rb);   // stage 1 (zeros when there is none)
+  store_b<MODE, NJ>(bm, rb, Bs[0]);
+  load_b<T, MODE, NJ>(c, bm, KBK, rb);   // stage 1 (zeros when there is none)
   __syncthreads();
   read_b(Bs[0], 0, bf[0]);
   // The last stage is peeled so that the loop body holds no conditional loads
@@ -328,9 +337,9 @@ __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int 
         for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(fa[i][q], b[j], acc[i][j]);
       if (MORE) load_a<T, MODE>(c, k1, q, fa);
       if (MORE && q == 1) {
-        store_b<MODE>(bm, rb, Bs[nxt]);
+        store_b<MODE, NJ>(bm, rb, Bs[nxt]);
         __syncthreads();
-        load_b<T, MODE>(c, bm, k1 + KBK, rb);
+        load_b<T, MODE, NJ>(c, bm, k1 + KBK, rb);
       }
     }
     cur = nxt;
@@ -339,11 +348,11 @@ __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int 
   stage(nst - 1, std::false_type{});
 }
 
-template <typename T, int MODE0>
+template <typename T, int MODE0, int NJ>
 __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, const int64_t *coltab,
                                            const Bases &bases, T alpha, T beta, T cscale) {
   typedef typename Mfma<T>::v4 v4;
-  __shared__ T Bs[3][KBK * LDS_B];
+  __shared__ T Bs[3][KBK * Blk<NJ>::LDS_B];
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave: readfirstlane tells the compiler
   // so, which keeps operand addresses and buffer resources in scalar registers
@@ -438,8 +447,8 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
     c.row2 = 2 * arow;
     c.a_lane = 0;   // set per load mode in run_segment
   };
-  if (nseg > 0) { SegCtx<T> c; setup(t.seg[0], c); run_segment<T, MODE0>(c, tid, arow, g, r, wn, Bs, acc); }
-  if (nseg > 1) { SegCtx<T> c; setup(t.seg[1], c); run_segment<T, SINGLE>(c, tid, arow, g, r, wn, Bs, acc); }
+  if (nseg > 0) { SegCtx<T> c; setup(t.seg[0], c); run_segment<T, MODE0, NJ>(c, tid, arow, g, r, wn, Bs, acc); }
+  if (nseg > 1) { SegCtx<T> c; setup(t.seg[1], c); run_segment<T, SINGLE, NJ>(c, tid, arow, g, r, wn, Bs, acc); }
 
   // Epilogue: one 16-byte unit per lane, column and u (when the column start is
   // 16-byte aligned).  Every column offset is read before the first store:
@@ -492,15 +501,15 @@ __device__ __forceinline__ void gemm_block(const DevTask &t, int m0, int n0, con
 // MODE: load mode of the first segment of every task in the table (the
 // table is split by mode on the host); a second segment, the small diagonal
 // term of a tile, always runs in single-element mode.
-template <typename T, int STAGE, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int STAGE, int MODE, int NJ>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Blk<NJ>::WAVES_PER_EU)))
 void grouped_gemm_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
                          const int64_t *__restrict__ coltab, Bases bases, T alpha, T beta, T cscale) {
   const DevTile e = tiles[blockIdx.x];
   if (e.task < 0) return;
   const DevTask &t = tasks[e.task];
   const bool fin = t.final_ != 0;
-  gemm_block<T, MODE>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0), fin ? cscale : T(0));
+  gemm_block<T, MODE, NJ>(t, e.m0, e.n0, coltab, bases, fin ? alpha : T(1), fin ? beta : T(0), fin ? cscale : T(0));
 }
 
 // Single task given by value; blockIdx.x walks the output blocks so that each
@@ -519,7 +528,7 @@ void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int m
   const int in = logical - group * band * nt;
   const int mtile = first_m + in % rows;
   const int ntile = in / rows;
-  gemm_block<T, MODE>(t, mtile * KBM, ntile * KBN, nullptr, bases, alpha, beta, cscale);
+  gemm_block<T, MODE, 8>(t, mtile * KBM, ntile * Blk<8>::KBN, nullptr, bases, alpha, beta, cscale);
 }
 
 template <typename T>
@@ -543,31 +552,40 @@ T preload_scale(double alpha, double beta) {
   return (r == r && r < lim && r > -lim) ? T(r) : T(0);
 }
 
-template <typename T, int STAGE>
+template <typename T, int STAGE, int NJ>
 void launch_grouped_s(int mode, dim3 grid, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                       const int64_t *coltab, const Bases &bases, T a, T b, T c) {
   const dim3 block(NT);
   if (mode == LOAD_PAIR_M)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_M>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_M, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
   else if (mode == LOAD_PAIR_K)
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_K>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_PAIR_K, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_SINGLE>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, STAGE, LOAD_SINGLE, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+}
+
+template <typename T, int NJ>
+void launch_grouped_w(int stage, int mode, dim3 grid, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                      const int64_t *coltab, const Bases &bases, T a, T b, T c) {
+  if (stage == 1)
+    launch_grouped_s<T, 1, NJ>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (stage == 2)
+    launch_grouped_s<T, 2, NJ>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (stage == 3)
+    launch_grouped_s<T, 3, NJ>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  else
+    launch_grouped_s<T, STAGE_SIDE, NJ>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
 }
 
 template <typename T>
-void launch_grouped_t(int stage, int mode, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
-                      const int64_t *coltab, const Bases &bases, double alpha, double beta) {
+void launch_grouped_t(int stage, int mode, int bn, unsigned n, hipStream_t s, const DevTask *tasks,
+                      const DevTile *tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
   const dim3 grid(n);
-  if (stage == 1)
-    launch_grouped_s<T, 1>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
-  else if (stage == 2)
-    launch_grouped_s<T, 2>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
-  else if (stage == 3)
-    launch_grouped_s<T, 3>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+  if (bn == Blk<4>::KBN)
+    launch_grouped_w<T, 4>(stage, mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
   else
-    launch_grouped_s<T, STAGE_SIDE>(mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
+    launch_grouped_w<T, 8>(stage, mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
 }
 
 template <typename T>
@@ -585,20 +603,22 @@ void launch_single_t(int mode, unsigned n, hipStream_t s, const DevTask &task, c
 
 }  // namespace
 
-int launch_grouped(tlr_dtype dt, int stage, int mode, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
-                   const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
+int launch_grouped(tlr_dtype dt, int stage, int mode, int bn, const DevTask *tasks, const DevTile *tiles,
+                   int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,
+                   void *stream) {
   if (n_tiles <= 0) return 0;
+  if (bn != Blk<4>::KBN && bn != Blk<8>::KBN) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64)
-    launch_grouped_t<double>(stage, mode, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+    launch_grouped_t<double>(stage, mode, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   else
-    launch_grouped_t<float>(stage, mode, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+    launch_grouped_t<float>(stage, mode, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
   return (int)hipGetLastError();
 }
 
 int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &bases, double alpha, double beta,
                   void *stream) {
-  const int mt = (task.M + KBM - 1) / KBM, nt = (task.N + KBN - 1) / KBN;
+  const int mt = (task.M + KBM - 1) / KBM, nt = (task.N + Blk<8>::KBN - 1) / Blk<8>::KBN;
   if (mt == 0 || nt == 0) return 0;
   const int64_t n = (int64_t)mt * nt;
   const int per = (int)((n + 7) / 8);

@@ -509,6 +509,19 @@ static double task_exec_flops(const DevTask &d) {
 // Lists are padded with idle entries to a common length, so every sub-table
 // is a multiple of NUM_XCD entries and the XCD of an entry does not depend on
 // which sub-tables precede it.
+// Block width of a launch.  128 x 128 blocks move the fewest operand bytes per
+// flop; 128 x 64 blocks (half the accumulators, three workgroups per CU) spread
+// a launch of few blocks over more CUs.  The final update stays wide; the
+// others go narrow when 128 x 128 blocks would give fewer than four workgroups
+// per CU (the coupling and diagonal-term GEMMs: few, with K = b).  Measured on
+// the store-bound right/left product, narrow blocks were slower.
+static int launch_bn(int stage, const TaskList &tl) {
+  if (stage == 3) return BN;
+  int64_t blocks = 0;
+  for (const DevTask &d : tl.t) blocks += ceil_div(d.M, BM) * ceil_div(d.N, BN);
+  return blocks < 4 * 256 ? BN_NARROW : BN;
+}
+
 // Appends one launch of `tl` (nothing when empty) and returns its index, or -1.
 static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   if (tl.t.empty()) return -1;
@@ -522,6 +535,9 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.useful_flops = 0;
   L.executed_flops = 0;
   const int32_t task0 = (int32_t)p.tasks.size();
+  L.task_off = task0;
+  L.bn = launch_bn(stage, tl);
+  const int bn = L.bn;
   struct TaskCost { int32_t t; int64_t per_block, blocks; int mode; };
   std::vector<TaskCost> order;
   for (size_t t = 0; t < tl.t.size(); ++t) {
@@ -530,7 +546,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
     L.executed_flops += task_exec_flops(d);
     int64_t K = 0;
     for (int s = 0; s < d.nseg; ++s) K += d.seg[s].K;
-    const int64_t blocks = ceil_div(d.M, BM) * ceil_div(d.N, BN);
+    const int64_t blocks = ceil_div(d.M, BM) * ceil_div(d.N, bn);
     // one block costs its K steps plus a fixed share for the C update
     order.push_back({(int32_t)t, K + 32, blocks, task_load_mode(d)});
     p.tasks.push_back(d);
@@ -547,7 +563,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
       load[x] += c.per_block * c.blocks;
       const DevTask &d = tl.t[c.t];
       for (int64_t m0 = 0; m0 < d.M; m0 += BM)
-        for (int64_t n0 = 0; n0 < d.N; n0 += BN)
+        for (int64_t n0 = 0; n0 < d.N; n0 += bn)
           xl[x].push_back(DevTile{task0 + c.t, (int32_t)m0, (int32_t)n0, 0});
     }
     size_t per = 0;
@@ -915,9 +931,13 @@ static tlr_status validate(const Plan &p, bool deep) {
       return fail(TLR_ERR_INVALID_ARG, "internal: output range outside its buffer (task " + std::to_string(t) + ")");
   }
   // workgroup tables: each block of each task exactly once
-  std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), 0);
-  for (size_t t = 0; t < p.tasks.size(); ++t)
-    want[t] = ceil_div(p.tasks[t].M, BM) * ceil_div(p.tasks[t].N, BN);
+  std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), -1);
+  for (const Launch &L : p.launches) {
+    if ((L.bn != BN && L.bn != BN_NARROW) || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
+      return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block width or task range");
+    for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t)
+      want[t] = ceil_div(p.tasks[t].M, BM) * ceil_div(p.tasks[t].N, L.bn);
+  }
   for (const Launch &L : p.launches) {
     if (L.tile_off < 0 || L.tile_off + L.n_tiles > (int64_t)p.tiles.size() || L.n_tiles % NUM_XCD)
       return fail(TLR_ERR_INVALID_ARG, "internal: launch table out of range");
@@ -940,7 +960,9 @@ static tlr_status validate(const Plan &p, bool deep) {
       while (mode + 1 < NUM_LOAD_MODES && e >= L.tile_off + L.mode_off[mode + 1]) ++mode;
       if (mode != LOAD_SINGLE && task_load_mode(d) != mode)
         return fail(TLR_ERR_INVALID_ARG, "internal: task in the table of a load mode it does not qualify for");
-      if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % BM || x.n0 % BN)
+      if (x.task < L.task_off || x.task >= L.task_off + L.n_tasks)
+        return fail(TLR_ERR_INVALID_ARG, "internal: workgroup entry of another launch's task");
+      if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % BM || x.n0 % L.bn)
         return fail(TLR_ERR_INVALID_ARG, "internal: bad block origin");
       seen[x.task]++;
     }

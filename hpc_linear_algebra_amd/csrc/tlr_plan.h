@@ -11,8 +11,9 @@
 
 namespace tlr {
 
-constexpr int BM = 128;            // workgroup block of every grouped launch
-constexpr int BN = 128;
+constexpr int BM = 128;            // workgroup block rows of every grouped launch
+constexpr int BN = 128;            // block columns: wide launches
+constexpr int BN_NARROW = 64;      // block columns: narrow launches (see launch_bn)
 constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
 constexpr int NUM_XCD = 8;         // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int AUX_PER_GROUP = 3;   // auxiliary streams of a group: two for load modes, one side lane
@@ -53,6 +54,8 @@ struct Launch {
   int rect;
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
+  int bn;            // block columns of the launch's workgroups (BN or BN_NARROW)
+  int64_t task_off;  // the launch's tasks are tasks[task_off, task_off + n_tasks)
   int64_t tile_off;  // first DevTile of the launch in the tile table
   int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)
   // the table is the concatenation of one sub-table per load mode (each a
@@ -139,7 +142,7 @@ tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n
                       double beta, void *C, int64_t ldc, void *stream);
 
 // Kernel launchers (gemm.hip).
-int launch_grouped(tlr_dtype dt, int stage, int mode, const DevTask *tasks, const DevTile *tiles,
+int launch_grouped(tlr_dtype dt, int stage, int mode, int bn, const DevTask *tasks, const DevTile *tiles,
                    int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,
                    void *stream);
 int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &bases, double alpha,
