@@ -29,7 +29,22 @@ sys.path.insert(0, ROOT)
 PEAK = {"f64": 78.6, "f32": 157.3}      # MI355X dense MFMA TFLOP/s (datasheet)
 HBM_PEAK_GBS = 8000.0
 METRIC = "TLR GEMM useful TFLOP/s + % of roofline, fp64 TLRxTLR->dense N=16384"
-WORKLOAD = 3
+DEFAULT_WORKLOAD = "3"
+
+
+def workload(name: str):
+    """Inputs of a bench workload: "1".."5" are the seeded workloads of
+    tlr_inputs.CONFIGS; "dense_tlr" is workload 2 with its operands swapped
+    (a dense 4096 x 4096 A times the TLR operand), the dense x TLR product."""
+    from tlr_inputs import CONFIGS, config_inputs
+    if name == "dense_tlr":
+        cfg = dict(CONFIGS[2])
+        T_op, Bd, C = config_inputs(2)
+        cfg["name"] = "dense_tlr_f64_n4096_b256_NN"
+        return cfg, Bd, T_op, C
+    cfg = CONFIGS[int(name)]
+    A, B, C = config_inputs(int(name))
+    return cfg, A, B, C
 
 
 def log(*a):
@@ -41,10 +56,11 @@ def kernel_hash() -> str:
     return kernel_source_hash()
 
 
-def traffic_from_profiles(stage: int):
+def traffic_from_profiles(stage: int, workload_name: str):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter runs, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "stage3_traffic.json")
+    counter runs of this workload, if they were taken on the current kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", f"stage{stage}_traffic_{workload_name}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -141,6 +157,9 @@ def cpu_baseline(cfg, A, B, C_in, useful_flops, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="1..5: the seeded workloads (3, the N=16384 TLR x TLR product, is the metric's); "
+                         "dense_tlr: workload 2 with the operands swapped")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -170,18 +189,22 @@ def main():
     import torch
     from hpc_linear_algebra_amd import tlrgemm as T
     from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_to_device
-    from tlr_inputs import CONFIGS, config_inputs
+    from tlr_inputs import TLRTiles
 
-    cfg = CONFIGS[WORKLOAD]
-    dtype, N = cfg["dtype"], cfg["N"]
     torch.cuda.set_device(0)
-    log(f"bench: generating workload {cfg['name']}")
-    A, B, C_in = config_inputs(WORKLOAD)
-    dA, dB = DeviceTLR(A), DeviceTLR(B)
-    Cd = dense_to_device(C_in)
+    log(f"bench: generating workload {args.workload}")
+    cfg, A, B, C_in = workload(args.workload)
+    dtype, N = cfg["dtype"], cfg["N"]
+    dense_a, dense_b = not isinstance(A, TLRTiles), not isinstance(B, TLRTiles)
+    dA = dense_to_device(A) if dense_a else DeviceTLR(A)
+    dB = dense_to_device(B) if dense_b else DeviceTLR(B)
+    dense_shape = A.shape if dense_a else (B.shape if dense_b else None)
+    tdt = torch.float64 if dtype == "f64" else torch.float32
+    Cd = dense_to_device(C_in) if C_in is not None else torch.zeros((N, N), dtype=tdt, device="cuda")
     n_streams = 2 if args.pipeline else 1
-    g = TLRGemm(dtype, cfg["opA"], dA, cfg["opB"], dB, ldc=N, budget=cfg["budget"] or 0, n_streams=n_streams,
-                flags=T.TLR_PLAN_PIPELINE if args.pipeline else 0)
+    g = TLRGemm(dtype, cfg["opA"], None if dense_a else dA, cfg["opB"], None if dense_b else dB, ldc=N,
+                dense_shape=dense_shape, ldb=N if (dense_a or dense_b) else 0, budget=cfg["budget"] or 0,
+                n_streams=n_streams, flags=T.TLR_PLAN_PIPELINE if args.pipeline else 0)
     info = g.info
     launches = g.launches()
     stream = torch.cuda.current_stream()
@@ -222,7 +245,7 @@ def main():
     ai = F / alg_bytes
     roof = min(peak, HBM_PEAK_GBS * 1e9 * ai / 1e12)
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"]),
+                "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"]),
                 "kernel": f"stage {L['stage']} launch (final update, segmented-K)" if L["stage"] == 3
                 else f"stage {L['stage']} launch",
                 "launch_ms": round(per_launch[dom], 4)}
@@ -230,8 +253,8 @@ def main():
     dense = None
     if not args.no_dense:
         log("bench: dense reference (rebuilt operands, same MFMA kernel)")
-        Ad = rebuild_dense_on_gpu(dA, A, dtype)
-        Bd = rebuild_dense_on_gpu(dB, B, dtype)
+        Ad = dA if dense_a else rebuild_dense_on_gpu(dA, A, dtype)
+        Bd = dB if dense_b else rebuild_dense_on_gpu(dB, B, dtype)
         Cw = torch.zeros((N, N), dtype=Ad.dtype, device="cuda")
         s = stream.cuda_stream
 
@@ -253,6 +276,10 @@ def main():
                  "parity": round(value / dense_tf, 4),
                  "note": "useful TFLOP/s of the TLR product / TFLOP/s of the library's dense MFMA GEMM on the "
                          "rebuilt N x N operands (dense time scaled by the executed-flop ratio)"}
+        if dense_a:
+            Ad = None
+        if dense_b:
+            Bd = None
         del Ad, Bd, Cw
         torch.cuda.empty_cache()
 
@@ -264,7 +291,8 @@ def main():
     order = ",".join("left" if T.tlr_plan_rect(g.plan, r)["order"] == T.TLR_ORDER_LEFT else "right"
                      for r in range(info["runs"]))
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
+        f"TLR GEMM useful TFLOP/s + % of roofline, {cfg['name']}", "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": cfg["name"], "N": N, "b": cfg["b"], "opA": cfg["opA"], "opB": cfg["opB"],

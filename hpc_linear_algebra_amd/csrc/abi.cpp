@@ -64,6 +64,7 @@ tlr_status tlr_gemm_workspace_bytes(tlr_dtype dt, tlr_op opA, const tlr_shape *A
     const int64_t ld_b = std::max<int64_t>(1, dense_rows);
     int64_t mrows = 0;
     if (A) mrows = opA == TLR_OP_N ? A->rows : A->cols;
+    else mrows = opA == TLR_OP_N ? dense_rows : dense_cols;   // dense A
     const int64_t ld_c = std::max<int64_t>(1, mrows);
     auto plan_at = [&](size_t budget, tlr::Plan &p) {
       return tlr::build_plan(dt, opA, A, opB, B, dense_rows, dense_cols, ld_b, ld_c, budget, n_streams, flags,
@@ -134,7 +135,7 @@ tlr_status tlr_plan_stage_shapes(const tlr_plan *h, int32_t rect, int32_t stage,
   auto WJ = [&]() { int64_t w = 0; for (int j = r.j0; j < r.j1; ++j) w += p.ns[j]; return w; };
   auto WI = [&]() { int64_t w = 0; for (int i = r.i0; i < r.i1; ++i) w += A.rs[i]; return w; };
   if (stage == 1) {
-    if (p.dense_b) return tlr::fail(TLR_ERR_UNSUPPORTED, "stage_shapes: no coupling stage with a dense B");
+    if (p.dense_b || p.dense_a) return tlr::fail(TLR_ERR_UNSUPPORTED, "stage_shapes: no coupling stage with a dense operand");
     for (int k = 0; k < A.qc; ++k) {
       int64_t M = 0, N = 0;
       for (int i = r.i0; i < r.i1; ++i) M += A.r(i, k);

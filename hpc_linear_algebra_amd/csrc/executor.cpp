@@ -174,13 +174,16 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
   if (n_streams < 1) return fail(TLR_ERR_INVALID_ARG, "execute: n_streams must be >= 1");
   if (ldc != p->ldc) return fail(TLR_ERR_INVALID_ARG, "execute: ldc differs from the analysed one");
   if (p->m > 0 && p->n > 0 && !C) return fail(TLR_ERR_INVALID_ARG, "execute: null C");
-  if (!A) return fail(TLR_ERR_INVALID_ARG, "execute: null A buffers");
-  if (p->A.diag && p->A.qr > 0 && !A->diag) return fail(TLR_ERR_INVALID_ARG, "execute: null A diagonal");
-  if (any_rank(p->A) && (!A->outer || !A->inner)) return fail(TLR_ERR_INVALID_ARG, "execute: null A factors");
-  if (p->dense_b) {
-    if (ldb != p->ldb) return fail(TLR_ERR_INVALID_ARG, "execute: ldb differs from the analysed one");
-    if (p->k > 0 && p->n > 0 && !B_dense) return fail(TLR_ERR_INVALID_ARG, "execute: null dense B");
-  } else {
+  if (!p->dense_a) {
+    if (!A) return fail(TLR_ERR_INVALID_ARG, "execute: null A buffers");
+    if (p->A.diag && p->A.qr > 0 && !A->diag) return fail(TLR_ERR_INVALID_ARG, "execute: null A diagonal");
+    if (any_rank(p->A) && (!A->outer || !A->inner)) return fail(TLR_ERR_INVALID_ARG, "execute: null A factors");
+  }
+  if (p->dense_a || p->dense_b) {   // the dense operand
+    if (ldb != p->ldb) return fail(TLR_ERR_INVALID_ARG, "execute: leading dimension of the dense operand differs from the analysed one");
+    if (p->m > 0 && p->n > 0 && p->k > 0 && !B_dense) return fail(TLR_ERR_INVALID_ARG, "execute: null dense operand");
+  }
+  if (!p->dense_b) {
     if (!B) return fail(TLR_ERR_INVALID_ARG, "execute: null B buffers");
     if (p->B.diag && p->B.qr > 0 && !B->diag) return fail(TLR_ERR_INVALID_ARG, "execute: null B diagonal");
     if (any_rank(p->B) && (!B->outer || !B->inner)) return fail(TLR_ERR_INVALID_ARG, "execute: null B factors");
@@ -201,9 +204,9 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
     return TLR_OK;
   }
   Bases bases;
-  bases.p[BASE_A_OUTER] = A->outer;
-  bases.p[BASE_A_INNER] = A->inner;
-  bases.p[BASE_A_DIAG] = A->diag;
+  bases.p[BASE_A_OUTER] = A ? A->outer : nullptr;
+  bases.p[BASE_A_INNER] = A ? A->inner : nullptr;
+  bases.p[BASE_A_DIAG] = A ? A->diag : nullptr;
   bases.p[BASE_B_OUTER] = B ? B->outer : nullptr;
   bases.p[BASE_B_INNER] = B ? B->inner : nullptr;
   bases.p[BASE_B_DIAG] = B ? B->diag : nullptr;

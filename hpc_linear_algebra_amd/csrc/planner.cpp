@@ -174,6 +174,11 @@ static size_t rect_ws(const Plan &p, const Sums &s, int i0, int i1, int j0, int 
       if (s.rho[i] > 0) tot += align_up((size_t)WJ * s.rho[i] * es, WS_ALIGN);
     return tot;
   }
+  if (p.dense_a) {   // Y_j only
+    for (int j = j0; j < j1; ++j)
+      if (s.gam[j] > 0) tot += align_up((size_t)WI * s.gam[j] * es, WS_ALIGN);
+    return tot;
+  }
   for (int k = 0; k < s.qk; ++k) {
     int64_t M = s.kap(k, i0, i1), N = s.bet(k, j0, j1);
     if (M > 0 && N > 0) tot += align_up((size_t)s_elems(M, N, order) * es, WS_ALIGN);
@@ -212,6 +217,16 @@ static double rect_useful(const Plan &p, const Sums &s, int i0, int i1, int j0, 
     return F;
   }
   const View &B = p.B;
+  if (p.dense_a) {
+    // Y_j = op(A)[I, k-block] W_kj for every k; then Y_j Z_j^T, and op(A)[I, j-block] op(D_B,jj)
+    const double WI = (double)height(p, i0, i1);
+    for (int k = 0; k < s.qk; ++k) F += 2.0 * WI * A.cs[k] * s.bet(k, j0, j1);
+    for (int j = j0; j < j1; ++j) {
+      F += 2.0 * WI * (double)p.ns[j] * s.gam[j];
+      if (B.diag) F += 2.0 * WI * (double)p.ns[j] * p.ns[j];
+    }
+    return F;
+  }
   for (int k = 0; k < s.qk; ++k) F += 2.0 * s.kap(k, i0, i1) * s.bet(k, j0, j1) * A.cs[k];
   if (order == TLR_ORDER_RIGHT) {
     if (A.diag)
@@ -257,6 +272,7 @@ static double rect_useful(const Plan &p, const Sums &s, int i0, int i1, int j0, 
 
 static bool order_allowed(const Plan &p, int order) {
   if (p.dense_b) return order == TLR_ORDER_RIGHT;
+  if (p.dense_a) return order == TLR_ORDER_LEFT;
   if (p.flags & TLR_PLAN_FORCE_RIGHT) return order == TLR_ORDER_RIGHT;
   if (p.flags & TLR_PLAN_FORCE_LEFT) return order == TLR_ORDER_LEFT;
   return true;
@@ -664,6 +680,52 @@ static void emit_rect(Plan &p, const Sums &s, int rect) {
     return;
   }
 
+  if (p.dense_a) {
+    // dense A: the left order with the coupling replaced by the product itself
+    // (launch 1: Y_j[:, (k, a)] = op(A)[I rows, k-block] W_kj[:, a] through a
+    // column map), then Y_j Z_j^T plus op(A)[i rows, j-block] op(D_B,jj)
+    const int64_t lda = p.ldb;
+    auto a_block = [&](int64_t r0, int64_t c0) {   // op(A)[r0.., c0..] as an M x K operand
+      return p.opA == TLR_OP_N ? opnd(BASE_B_DENSE, r0 + c0 * lda, lda, 0) : opnd(BASE_B_DENSE, c0 + r0 * lda, lda, 1);
+    };
+    std::vector<int64_t> Yoff(s.qn, -1);
+    for (int j = j0; j < j1; ++j)
+      if (s.gam[j] > 0) Yoff[j] = take((size_t)WI * s.gam[j] * es);
+    TaskList l1, l3;
+    for (int k = 0; k < qk; ++k) {
+      const int64_t SN = s.bet(k, j0, j1);
+      if (SN == 0) continue;
+      const int64_t ctab = (int64_t)p.coltab.size();
+      for (int j = j0; j < j1; ++j) {
+        int64_t pkj = 0;
+        for (int kk = 0; kk < k; ++kk) pkj += B.r(kk, j);
+        for (int a = 0; a < B.r(k, j); ++a) p.coltab.push_back(Yoff[j] + (pkj + a) * WI);
+      }
+      DevTask d = new_task(WI, SN, BASE_WS, 0, 0, ctab, false);
+      add_seg(d, a_block(A.ro[i0], A.co[k]), opnd(B.outer_base, B.oc(k, j0) * b, b, 0), A.cs[k]);
+      l1.t.push_back(d);
+      l1.useful.push_back(2.0 * WI * (double)SN * A.cs[k]);
+    }
+    for (int j = j0; j < j1; ++j)
+      for (int i = i0; i < i1; ++i) {
+        DevTask d = new_task(A.rs[i], p.ns[j], BASE_C, A.ro[i] + p.no[j] * p.ldc, p.ldc, -1, true);
+        double u = 0;
+        if (s.gam[j] > 0) {
+          add_seg(d, opnd(BASE_WS, Yoff[j] + rI(i), WI, 0), opnd(B.inner_base, B.ic(0, j) * b, b, 1), s.gam[j]);
+          u += 2.0 * A.rs[i] * (double)p.ns[j] * s.gam[j];
+        }
+        if (B.diag) {
+          add_seg(d, a_block(A.ro[i], A.co[j]), opnd(B.diag_base, (int64_t)j * b * b, b, B.diag_trans), p.ns[j]);
+          u += 2.0 * A.rs[i] * (double)p.ns[j] * p.ns[j];
+        }
+        l3.t.push_back(d);
+        l3.useful.push_back(u);
+      }
+    emit_launch(p, 1, R.group, rect, l1);
+    emit_launch(p, 3, R.group, rect, l3);
+    return;
+  }
+
   // coupling blocks S_k (kap_k(I) x bet_k(J), column-major)
   std::vector<int64_t> Soff(qk, -1), SM(qk, 0), SN(qk, 0);
   for (int k = 0; k < qk; ++k) {
@@ -876,9 +938,9 @@ static BufSizes buffer_sizes(const Plan &p) {
   if (!p.dense_b) {
     z.n[BASE_B_OUTER] = z.n[BASE_B_INNER] = view_factor_elems(p.B);
     z.n[BASE_B_DIAG] = p.B.diag ? (int64_t)p.B.qr * p.B.b * p.B.b : 0;
-  } else if (p.dense_cols > 0 && p.dense_rows > 0) {
-    z.n[BASE_B_DENSE] = p.ldb * (p.dense_cols - 1) + p.dense_rows;
   }
+  if ((p.dense_b || p.dense_a) && p.dense_cols > 0 && p.dense_rows > 0)   // the dense operand, A or B
+    z.n[BASE_B_DENSE] = p.ldb * (p.dense_cols - 1) + p.dense_rows;
   z.n[BASE_WS] = (int64_t)(p.ws_bytes / (size_t)p.es);
   if (p.m > 0 && p.n > 0) z.n[BASE_C] = p.ldc * (p.n - 1) + p.m;
   return z;
@@ -1069,12 +1131,54 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   p->n_streams = n_streams;
   p->flags = flags;
   p->dense_b = (B == nullptr);
+  p->dense_a = (A == nullptr);
+  p->opA = opA;
   p->opB = opB;
-  tlr_status st = make_view(A, opA, BASE_A_OUTER, BASE_A_INNER, BASE_A_DIAG, "A", &p->A);
-  if (st != TLR_OK) return st;
-  p->m = A ? (opA == TLR_OP_N ? A->rows : A->cols) : 0;
-  p->k = A ? (opA == TLR_OP_N ? A->cols : A->rows) : 0;
-  if (p->dense_b) {
+  if (p->dense_a && p->dense_b) return fail(TLR_ERR_INVALID_ARG, "A and B cannot both be dense (one TLR operand needed)");
+  tlr_status st = TLR_OK;
+  if (p->dense_a) {
+    // dense A (stored dense_rows x dense_cols, leading dim ldb) times a TLR B
+    if (flags & TLR_PLAN_FORCE_RIGHT) return fail(TLR_ERR_UNSUPPORTED, "the right order needs a TLR A");
+    if (flags & TLR_PLAN_PIPELINE) return fail(TLR_ERR_UNSUPPORTED, "pipelining needs a TLR A");
+    if (dense_rows < 0 || dense_cols < 0) return fail(TLR_ERR_INVALID_ARG, "bad dense A dims");
+    st = make_view(B, opB, BASE_B_OUTER, BASE_B_INNER, BASE_B_DIAG, "B", &p->B);
+    if (st != TLR_OK) return st;
+    p->m = opA == TLR_OP_N ? dense_rows : dense_cols;
+    p->k = opA == TLR_OP_N ? dense_cols : dense_rows;
+    const int64_t kb = opB == TLR_OP_N ? B->rows : B->cols;
+    p->n = opB == TLR_OP_N ? B->cols : B->rows;
+    if (kb != p->k) return fail(TLR_ERR_INVALID_ARG, "op(A) columns != op(B) rows");
+    if (ldb < std::max<int64_t>(1, dense_rows)) return fail(TLR_ERR_INVALID_ARG, "lda < rows of A");
+    if (ldb >= (int64_t)1 << 21) return fail(TLR_ERR_INVALID_ARG, "lda must be below 2^21");
+    p->ldb = ldb;
+    p->dense_rows = dense_rows;
+    p->dense_cols = dense_cols;
+    // A as a view without ranks: row tiles of op(A) of B's tile size,
+    // contraction tiles those of op(B)'s rows
+    View &V = p->A;
+    V.b = B->b;
+    split_dim(p->m, B->b, V.rs, V.ro);
+    V.cs = p->B.rs;
+    V.co = p->B.ro;
+    V.qr = (int)V.rs.size();
+    V.qc = (int)V.cs.size();
+    V.R.assign((size_t)V.qr * V.qc, 0);
+    V.ocol.assign((size_t)V.qr * V.qc, 0);
+    V.icol.assign((size_t)V.qr * V.qc, 0);
+    V.diag = false;
+    V.outer_base = BASE_A_OUTER;
+    V.inner_base = BASE_A_INNER;
+    V.diag_base = BASE_A_DIAG;
+    p->ns = p->B.cs;
+    p->no = p->B.co;
+  } else {
+    st = make_view(A, opA, BASE_A_OUTER, BASE_A_INNER, BASE_A_DIAG, "A", &p->A);
+    if (st != TLR_OK) return st;
+    p->m = opA == TLR_OP_N ? A->rows : A->cols;
+    p->k = opA == TLR_OP_N ? A->cols : A->rows;
+  }
+  if (p->dense_a) {
+  } else if (p->dense_b) {
     if (flags & TLR_PLAN_FORCE_LEFT) return fail(TLR_ERR_UNSUPPORTED, "the left order needs a TLR B");
     if (dense_rows < 0 || dense_cols < 0) return fail(TLR_ERR_INVALID_ARG, "bad dense B dims");
     int64_t kb = opB == TLR_OP_N ? dense_rows : dense_cols;
@@ -1106,15 +1210,16 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   build_sums(*p, s);
   const int qm = s.qm, qn = s.qn;
   // whole-C accounting
-  p->flops_right = (qm && qn) ? rect_useful(*p, s, 0, qm, 0, qn, TLR_ORDER_RIGHT) : 0;
+  p->flops_right = p->dense_a ? -1 : ((qm && qn) ? rect_useful(*p, s, 0, qm, 0, qn, TLR_ORDER_RIGHT) : 0);
   p->flops_left = p->dense_b ? -1 : ((qm && qn) ? rect_useful(*p, s, 0, qm, 0, qn, TLR_ORDER_LEFT) : 0);
-  p->final_right = 0;
-  for (int i = 0; i < qm; ++i) p->final_right += 2.0 * p->A.rs[i] * (double)s.rho[i] * p->n;
+  p->final_right = p->dense_a ? -1 : 0;
+  if (!p->dense_a)
+    for (int i = 0; i < qm; ++i) p->final_right += 2.0 * p->A.rs[i] * (double)s.rho[i] * p->n;
   if (!p->dense_b) {
     p->final_left = 0;
     for (int j = 0; j < qn; ++j) p->final_left += 2.0 * p->ns[j] * (double)s.gam[j] * p->m;
   }
-  p->alg_bytes = (double)p->es * (compressed_elems(p->A) +
+  p->alg_bytes = (double)p->es * ((p->dense_a ? (double)dense_rows * dense_cols : compressed_elems(p->A)) +
                                   (p->dense_b ? (double)dense_rows * dense_cols : compressed_elems(p->B)) +
                                   (double)p->m * p->n);
 

@@ -79,6 +79,8 @@ struct Plan {
   tlr_dtype dt = TLR_F64;
   int es = 8;
   bool dense_b = false;
+  bool dense_a = false;        // dense A (and TLR B): the left order with no coupling stage
+  int opA = 0;
   View A, B;                  // B unused (except sizes) for a dense B
   int opB = 0;
   int64_t m = 0, n = 0, k = 0;

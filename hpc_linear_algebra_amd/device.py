@@ -59,16 +59,22 @@ def dense_from_device(t: torch.Tensor, rows: int, cols: int) -> np.ndarray:
 
 
 class TLRGemm:
-    """Analyse, allocate descriptor + workspace tensors, bind; then execute."""
+    """Analyse, allocate descriptor + workspace tensors, bind; then execute.
 
-    def __init__(self, dtype: str, opA: str, A: DeviceTLR, opB: str, B, ldc: int,
+    Either A or B may be a dense operand (None at construction, with its
+    stored dense_shape and leading dimension ldb; its device tensor is passed
+    in that position at call time)."""
+
+    def __init__(self, dtype: str, opA: str, A: Optional[DeviceTLR], opB: str, B, ldc: int,
                  dense_shape: Optional[tuple] = None, ldb: int = 0, budget: int = 0,
                  n_streams: int = 1, flags: int = 0, device="cuda"):
         self.dtype = dtype
+        self.dense_a = A is None
         self.dense = B is None
-        dr, dc = dense_shape if self.dense else (0, 0)
-        self.plan = T.tlr_gemm_analyze(dtype, opA, A.shape, opB, None if self.dense else B.shape,
-                                       dr, dc, ldb, ldc, budget, n_streams, flags)
+        dr, dc = dense_shape if (self.dense or self.dense_a) else (0, 0)
+        self.plan = T.tlr_gemm_analyze(dtype, opA, None if self.dense_a else A.shape, opB,
+                                       None if self.dense else B.shape, dr, dc, ldb, ldc, budget, n_streams,
+                                       flags)
         self.info = T.tlr_plan_info(self.plan)
         self.ldb, self.ldc = ldb, ldc
         self.desc = torch.empty(self.info["descriptor_bytes"], dtype=torch.uint8, device=device)
@@ -82,14 +88,17 @@ class TLRGemm:
     def launches(self):
         return [T.tlr_plan_launch(self.plan, l) for l in range(self.info["launches"])]
 
-    def __call__(self, alpha: float, A: DeviceTLR, B, beta: float, C: torch.Tensor,
+    def __call__(self, alpha: float, A, B, beta: float, C: torch.Tensor,
                  streams: Optional[Sequence[int]] = None):
         if streams is None:
             streams = [torch.cuda.current_stream().cuda_stream]
-        if self.dense:
-            Bb, Bd = None, B.data_ptr()
+        Ab, Bb, Dd = None, None, 0
+        if self.dense_a:
+            Dd, Bb = A.data_ptr(), B.buffers()
+        elif self.dense:
+            Ab, Dd = A.buffers(), B.data_ptr()
         else:
-            Bb, Bd = B.buffers(), 0
-        T.tlr_gemm_execute(self.plan, alpha, A.buffers(), Bb, Bd, self.ldb, beta, C.data_ptr(), self.ldc,
+            Ab, Bb = A.buffers(), B.buffers()
+        T.tlr_gemm_execute(self.plan, alpha, Ab, Bb, Dd, self.ldb, beta, C.data_ptr(), self.ldc,
                            self.ws.data_ptr(), self.ws.numel(), list(streams))
         return C

@@ -4,7 +4,7 @@ short markdown, for the committed profiles.
   python -m hpc_linear_algebra_amd.profiling stats DIR --command "..." > out.md
   python -m hpc_linear_algebra_amd.profiling pmc DIR [DIR ...] --command "..." > out.md
   python -m hpc_linear_algebra_amd.profiling traffic --fetch D --write D --copy-fetch D \
-         --copy-write D --kernel REGEX --out profiles/stage3_traffic.json
+         --copy-write D --kernel REGEX --out profiles/stage3_traffic_WORKLOAD.json
 
 DIR is a rocprofv3 output directory written with --output-format csv.
 """

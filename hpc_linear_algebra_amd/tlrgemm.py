@@ -143,23 +143,24 @@ class Plan:
             self.h = c_void_p(0)
 
 
-def tlr_gemm_analyze(dtype, opA, A: Shape, opB, B: Optional[Shape], dense_rows: int = 0,
+def tlr_gemm_analyze(dtype, opA, A: Optional[Shape], opB, B: Optional[Shape], dense_rows: int = 0,
                      dense_cols: int = 0, ldb: int = 0, ldc: int = 0, workspace_budget: int = 0,
                      n_streams: int = 1, flags: int = 0) -> Plan:
+    """A or B None: that operand is dense (stored dense_rows x dense_cols, leading dim ldb)."""
     L = lib()
     h = c_void_p()
-    st = L.tlr_gemm_analyze(_dt(dtype), _op(opA), ctypes.byref(A.c), _op(opB),
+    st = L.tlr_gemm_analyze(_dt(dtype), _op(opA), ctypes.byref(A.c) if A is not None else None, _op(opB),
                             ctypes.byref(B.c) if B is not None else None, dense_rows, dense_cols, ldb, ldc,
                             workspace_budget, n_streams, flags, ctypes.byref(h))
     _check(st, "tlr_gemm_analyze")
     return Plan(h.value, (A, B))
 
 
-def tlr_gemm_workspace_bytes(dtype, opA, A: Shape, opB, B: Optional[Shape], dense_rows: int = 0,
+def tlr_gemm_workspace_bytes(dtype, opA, A: Optional[Shape], opB, B: Optional[Shape], dense_rows: int = 0,
                              dense_cols: int = 0, n_streams: int = 1, flags: int = 0, runs: int = 1) -> int:
     L = lib()
     out = c_size_t()
-    st = L.tlr_gemm_workspace_bytes(_dt(dtype), _op(opA), ctypes.byref(A.c), _op(opB),
+    st = L.tlr_gemm_workspace_bytes(_dt(dtype), _op(opA), ctypes.byref(A.c) if A is not None else None, _op(opB),
                                     ctypes.byref(B.c) if B is not None else None, dense_rows, dense_cols,
                                     n_streams, flags, runs, ctypes.byref(out))
     _check(st, "tlr_gemm_workspace_bytes")
@@ -206,11 +207,13 @@ def buffers(diag: int = 0, outer: int = 0, inner: int = 0) -> tlr_buffers:
     return tlr_buffers(c_void_p(diag or None), c_void_p(outer or None), c_void_p(inner or None))
 
 
-def tlr_gemm_execute(p: Plan, alpha: float, A: tlr_buffers, B: Optional[tlr_buffers], B_dense: int,
+def tlr_gemm_execute(p: Plan, alpha: float, A: Optional[tlr_buffers], B: Optional[tlr_buffers], B_dense: int,
                      ldb: int, beta: float, C: int, ldc: int, workspace: int, workspace_bytes: int,
                      streams: Sequence[int]):
+    """B_dense / ldb: the dense operand (A's storage when A is None, else B's)."""
     arr = (c_void_p * max(1, len(streams)))(*[c_void_p(s or None) for s in streams])
-    st = lib().tlr_gemm_execute(p.h, alpha, ctypes.byref(A), ctypes.byref(B) if B is not None else None,
+    st = lib().tlr_gemm_execute(p.h, alpha, ctypes.byref(A) if A is not None else None,
+                                ctypes.byref(B) if B is not None else None,
                                 c_void_p(B_dense or None), ldb, beta, c_void_p(C or None), ldc,
                                 c_void_p(workspace or None), workspace_bytes, arr, max(1, len(streams)))
     _check(st, "tlr_gemm_execute")

@@ -124,10 +124,14 @@ typedef struct {
  * the workspace budget, grouped descriptors; reusable for every product with
  * the same rank structure).
  *   dt          element type of every buffer.
- *   opA, A      op and structure of A (required).
+ *   opA, A      op and structure of A; A == NULL selects a dense A of
+ *               dense_rows x dense_cols (stored, column-major, leading dim ldb):
+ *               the dense x TLR product, evaluated in the left order with
+ *               op(A) W in place of the coupling (at most one operand dense).
  *   opB, B      op and structure of B; B == NULL selects a dense B of
  *               dense_rows x dense_cols (stored, column-major, leading dim ldb).
- *   ldb         leading dimension of a dense B (ignored for a TLR B; < 2^21).
+ *   ldb         leading dimension of the dense operand (ignored when both are
+ *               TLR; < 2^21).
  *   ldc         leading dimension of C (>= m).
  *   workspace_budget  bytes of device workspace execute may use; 0 means no limit.
  *   n_streams   streams execute will be given (>= 1); boundary regions of C
@@ -143,8 +147,8 @@ typedef struct {
  *   plan_out    receives a new plan (free with tlr_plan_destroy).
  * Every plan is checked before it is returned: each operand and output range a
  * kernel task can touch must lie inside the buffer sizes the layout above
- * implies (factor buffers b * sum(r_ij) elements, diagonal q*b*b, dense B
- * ldb * cols, C ldc * n, workspace workspace_bytes); with TLR_PLAN_VALIDATE it
+ * implies (factor buffers b * sum(r_ij) elements, diagonal q*b*b, dense
+ * operand ldb * cols, C ldc * n, workspace workspace_bytes); with TLR_PLAN_VALIDATE it
  * also checks that writes inside one launch never overlap, that every
  * workspace element a launch reads was written earlier for the same output
  * rectangle, and that each element of C is written exactly once.
@@ -223,8 +227,10 @@ tlr_status tlr_plan_bind(tlr_plan *p, void *dev_desc, size_t bytes, void *stream
 
 /*
  * tlr_gemm_execute: C <- alpha op(A) op(B) + beta C with the bound plan.
- *   A, B        device buffers of the analysed operands (B NULL for a dense B).
- *   B_dense     dense B (when analysed with B == NULL), leading dim ldb.
+ *   A, B        device buffers of the analysed TLR operands (NULL for the
+ *               dense one).
+ *   B_dense     the dense operand (dense A or dense B as analysed), leading
+ *               dim ldb; NULL when both operands are TLR.
  *   C           m x n column-major, leading dim ldc (both as analysed).
  *   workspace   device buffer of at least workspace_bytes (256-byte aligned).
  *   streams     n_streams >= 1 streams; streams[0] is the caller's: the call is

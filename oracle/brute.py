@@ -81,11 +81,22 @@ def tile_loop(alpha: float, opA: str, A: TLRTiles, opB: str, B, beta: float,
 
     Returns (C as float64 array, flops performed).  ``B`` may be a dense array;
     then each op(B) tile is dense and a low-rank A tile is applied as
-    U (V^T B_kj).  C_in is not read when beta == 0."""
+    U (V^T B_kj).  ``A`` may be a dense array (with a TLR ``B``): its row panel
+    k-block is one dense tile per contraction tile (the contraction tiles are
+    op(B)'s row tiles) and a low-rank B tile is applied as (A_k W_kj) Z_kj^T.
+    C_in is not read when beta == 0."""
     if assoc not in ("right", "left"):
         raise ValueError(assoc)
     cnt = _Counter()
-    if opA == "N":
+    dense_A = not isinstance(A, TLRTiles)
+    if dense_A:
+        Ad = np.asarray(A, dtype=np.float64)
+        Ad = Ad if opA == "N" else Ad.T
+        mrows = [Ad.shape[0]] if Ad.shape[0] > 0 else []
+        ksz = B.row_sizes if opB == "N" else B.col_sizes
+        from .reference import offsets as _off
+        kao = _off(ksz)
+    elif opA == "N":
         mrows, ksz = A.row_sizes, A.col_sizes
     else:
         mrows, ksz = A.col_sizes, A.row_sizes
@@ -113,7 +124,7 @@ def tile_loop(alpha: float, opA: str, A: TLRTiles, opB: str, B, beta: float,
                         C[i][j][r][c] = beta * float(Cin[ro[i] + r, co[j] + c])
     for k in range(qk):
         for i in range(qm):
-            ta = _op_tile(A, opA, i, k)
+            ta = ("D", _mat(Ad[:, kao[k]:kao[k] + ksz[k]])) if dense_A else _op_tile(A, opA, i, k)
             for j in range(qn):
                 si, sk, sj = mrows[i], ksz[k], ncols[j]
                 if dense_B:

@@ -170,6 +170,22 @@ def useful_flops_dense_b(RA, ms, ks, ncols: int, dA: bool, I=None) -> int:
     return F
 
 
+def useful_flops_dense_a(RB, ks, ns, mrows: int, dB: bool, J=None) -> int:
+    """Useful flops of a dense op(A) with ``mrows`` rows times op(B) (TLR): per
+    (k, j) either A_k D_kk (k = j) or (A_k W_kj) Z_kj^T."""
+    RB = np.asarray(RB)
+    J = range(RB.shape[1]) if J is None else J
+    F = 0
+    for k in range(RB.shape[0]):
+        for j in J:
+            if dB and k == j:
+                F += 2 * mrows * ks[k] * ns[j]
+            else:
+                rb = int(RB[k, j])
+                F += 2 * mrows * ks[k] * rb + 2 * mrows * rb * ns[j]
+    return F
+
+
 def workspace_elements(RA, RB, ms, ks, ns, dA: bool, dB: bool, order: str,
                        I: Sequence[int], J: Sequence[int]) -> Dict[str, int]:
     """Element counts of the intermediates one rectangle needs:

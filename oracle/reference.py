@@ -58,12 +58,15 @@ def _op(M: np.ndarray, op: str) -> np.ndarray:
     raise ValueError(op)
 
 
-def gemm_reference(alpha: float, opA: str, A: TLRTiles, opB: str, B,
+def gemm_reference(alpha: float, opA: str, A, opB: str, B,
                    beta: float, C_in: Optional[np.ndarray]) -> np.ndarray:
     """alpha op(A) op(B) + beta C_in in float64; C_in is never read when beta == 0.
 
-    ``B`` is a TLRTiles or a dense 2-D array (the TLR x dense product)."""
-    Ad = _op(reconstruct(A), opA)
+    ``A`` and ``B`` are each a TLRTiles or a dense 2-D array (the TLR x dense
+    and dense x TLR products, both within the pages' "one or both operands in
+    TLR format")."""
+    Ad = reconstruct(A) if isinstance(A, TLRTiles) else np.asarray(A, dtype=np.float64)
+    Ad = _op(Ad, opA)
     Bd = reconstruct(B) if isinstance(B, TLRTiles) else np.asarray(B, dtype=np.float64)
     Bd = _op(Bd, opB)
     if Ad.shape[1] != Bd.shape[0]:
@@ -106,7 +109,11 @@ def gemm_reference_block(alpha: float, opA: str, A: TLRTiles, opB: str, B,
                          rows: Tuple[int, int], cols: Tuple[int, int]) -> np.ndarray:
     """Block C[rows[0]:rows[1], cols[0]:cols[1]] of the same product, built from
     the row panel of op(A) and the column panel of op(B) only."""
-    Ap = _op_row_panel(A, opA, rows[0], rows[1])
+    if isinstance(A, TLRTiles):
+        Ap = _op_row_panel(A, opA, rows[0], rows[1])
+    else:
+        Ad = np.asarray(A)
+        Ap = (Ad[rows[0]:rows[1], :] if opA == "N" else Ad[:, rows[0]:rows[1]].T).astype(np.float64)
     if isinstance(B, TLRTiles):
         Bp = _op_col_panel(B, opB, cols[0], cols[1])
     else:

@@ -34,28 +34,41 @@ def op_dims(t, op):
     return (t.rows, t.cols) if op == "N" else (t.cols, t.rows)
 
 
-def run_tlr(A: TLRTiles, B, opA: str, opB: str, alpha: float, beta: float, C_in,
-            budget: int = 0, n_streams: int = 1, flags: int = 0, ld_pad: int = 0, return_plan=False):
-    """C = alpha op(A) op(B) + beta C_in on the GPU; C_in None -> NaN-filled C."""
+def run_tlr(A, B, opA: str, opB: str, alpha: float, beta: float, C_in,
+            budget: int = 0, n_streams: int = 1, flags: int = 0, ld_pad: int = 0, return_plan=False,
+            dtype: str = None):
+    """C = alpha op(A) op(B) + beta C_in on the GPU; C_in None -> NaN-filled C.
+    Either A or B may be a dense array (the other a TLRTiles)."""
     import torch
     from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_from_device, dense_to_device
-    dtype = A.dtype
-    m = op_dims(A, opA)[0]
+    dense_a = not isinstance(A, TLRTiles)
     dense = not isinstance(B, TLRTiles)
+    dtype = dtype or (B.dtype if dense_a else A.dtype)
+    npd = np.float64 if dtype == "f64" else np.float32
+    if dense_a:
+        m = A.shape[0] if opA == "N" else A.shape[1]
+    else:
+        m = op_dims(A, opA)[0]
     if dense:
         n = B.shape[1] if opB == "N" else B.shape[0]
     else:
         n = op_dims(B, opB)[1]
     ldc = max(1, m + ld_pad)
-    npd = np.float64 if dtype == "f64" else np.float32
     Cstart = np.full((m, n), np.nan, dtype=npd) if C_in is None else np.asarray(C_in, dtype=npd)
-    dA = DeviceTLR(A)
-    if dense:
+    if dense_a:
+        lda = max(1, A.shape[0] + ld_pad)
+        dA = dense_to_device(np.asarray(A, dtype=npd), ld=lda)
+        dB = DeviceTLR(B)
+        g = TLRGemm(dtype, opA, None, opB, dB, ldc=ldc, dense_shape=A.shape, ldb=lda, budget=budget,
+                    n_streams=n_streams, flags=flags)
+    elif dense:
+        dA = DeviceTLR(A)
         ldb = max(1, B.shape[0] + ld_pad)
         dB = dense_to_device(np.asarray(B, dtype=npd), ld=ldb)
         g = TLRGemm(dtype, opA, dA, opB, None, ldc=ldc, dense_shape=B.shape, ldb=ldb, budget=budget,
                     n_streams=n_streams, flags=flags)
     else:
+        dA = DeviceTLR(A)
         dB = DeviceTLR(B)
         g = TLRGemm(dtype, opA, dA, opB, dB, ldc=ldc, budget=budget, n_streams=n_streams, flags=flags)
     Cd = dense_to_device(Cstart, ld=ldc)
@@ -73,8 +86,9 @@ def check_tlr(A, B, opA, opB, alpha, beta, C_in, **kw):
     got = run_tlr(A, B, opA, opB, alpha, beta, C_in, **kw)
     ref = reference.gemm_reference(alpha, opA, A, opB, B, beta, C_in)
     err = reference.rel_fro(got, ref)
+    dtype = kw.get("dtype") or (A.dtype if isinstance(A, TLRTiles) else B.dtype)
     assert np.all(np.isfinite(got)), "non-finite output"
-    assert err <= TOL[A.dtype], f"relative Frobenius error {err:.3e} > {TOL[A.dtype]:.0e}"
+    assert err <= TOL[dtype], f"relative Frobenius error {err:.3e} > {TOL[dtype]:.0e}"
     return err
 
 

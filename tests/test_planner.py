@@ -257,3 +257,60 @@ def test_side_launch_holds_the_diagonal_terms(order):
     A0, B0 = T.Shape(n, n, b, RA, False), T.Shape(n, n, b, RB, False)
     p0 = T.tlr_gemm_analyze("f64", "N", A0, "N", B0, ldc=n, flags=order)
     assert [T.tlr_plan_launch(p0, l)["stage"] for l in range(T.tlr_plan_info(p0)["launches"])] == [1, 2, 3]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_dense_a_plans(seed):
+    # dense A x TLR B: the left order without a coupling stage; useful flops
+    # equal the oracle's rank arithmetic exactly, and every plan (budgets,
+    # streams, ops, ragged grids) passes the exhaustive descriptor check
+    rng = np.random.default_rng(40 + seed)
+    b = (16, 24, 32, 7)[seed]
+    n = 5 * b - (0, 3, 0, 2)[seed]
+    sz = tile_sizes(n, b)
+    q = len(sz)
+    diag = seed % 2 == 0
+    RB = _rand_ranks(rng, q, b, diag, 0, min(b, 9))
+    for r in range(q):
+        for c in range(q):
+            RB[r, c] = min(RB[r, c], sz[r], sz[c])
+    B = T.Shape(n, n, b, RB, diag)
+    for opA, opB in (("N", "N"), ("T", "N"), ("N", "T"), ("T", "T")):
+        m = n + 5
+        dr, dc = (m, n) if opA == "N" else (n, m)
+        p = T.tlr_gemm_analyze("f64", opA, None, opB, B, dr, dc, ldb=dr + 1, ldc=m, flags=T.TLR_PLAN_VALIDATE)
+        info = T.tlr_plan_info(p)
+        oB = pa.op_ranks(RB, opB)
+        assert info["useful_flops"] == pa.useful_flops_dense_a(oB, sz, sz, m, diag)
+        assert info["flops_right"] == -1 and info["final_flops_right"] == -1
+        assert [T.tlr_plan_launch(p, l)["stage"] for l in range(info["launches"])] == [1, 3]
+        assert all(T.tlr_plan_rect(p, r)["order"] == T.TLR_ORDER_LEFT for r in range(info["runs"]))
+        full = info["workspace_bytes"]
+        for frac, ns in ((0.3, 1), (0.3, 3), (1.0, 3)):
+            try:
+                p2 = T.tlr_gemm_analyze("f64", opA, None, opB, B, dr, dc, ldb=dr, ldc=m,
+                                        workspace_budget=int(full * frac), n_streams=ns, flags=T.TLR_PLAN_VALIDATE)
+            except T.TLRError as e:
+                assert e.status == T.TLR_ERR_WORKSPACE
+                continue
+            i2 = T.tlr_plan_info(p2)
+            assert i2["useful_flops"] == info["useful_flops"]
+            assert i2["workspace_bytes"] <= max(int(full * frac), full if frac == 1.0 else 0)
+
+
+def test_dense_a_errors():
+    rng = np.random.default_rng(9)
+    RB = _rand_ranks(rng, 3, 8, True, 0, 4)
+    B = T.Shape(24, 24, 8, RB, True)
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_analyze("f64", "N", None, "N", None, 10, 24, ldb=10, ldc=10)
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_analyze("f64", "N", None, "N", B, 10, 23, ldb=10, ldc=10)      # k mismatch
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_analyze("f64", "N", None, "N", B, 10, 24, ldb=9, ldc=10)       # lda < rows
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_analyze("f64", "N", None, "N", B, 10, 24, ldb=10, ldc=10, flags=T.TLR_PLAN_FORCE_RIGHT)
+    assert e.value.status == T.TLR_ERR_UNSUPPORTED
