@@ -118,6 +118,25 @@ def rebuild_dense_on_gpu(dev, t, dtype):
     return out
 
 
+def padded_copy(t, rmax: int):
+    """The TLR operand with every off-diagonal tile's factors padded with zero
+    columns to rank min(rmax, tile sizes): the one-rank storage of the
+    batched per-k comparator."""
+    import copy
+    import numpy as np
+    p = copy.copy(t)
+    p.U, p.V = dict(t.U), dict(t.V)
+    p.ranks = np.array(t.ranks, copy=True)
+    for key in list(p.U):
+        u, v = p.U[key], p.V[key]
+        want = min(rmax, u.shape[0], v.shape[0])
+        if want > u.shape[1]:
+            p.U[key] = np.concatenate([u, np.zeros((u.shape[0], want - u.shape[1]), u.dtype)], axis=1)
+            p.V[key] = np.concatenate([v, np.zeros((v.shape[0], want - v.shape[1]), v.dtype)], axis=1)
+            p.ranks[key] = want
+    return p
+
+
 def cpu_baseline(cfg, A, B, C_in, useful_flops, budget_s=15.0):
     """The CPU oracle, timed on a bounded sample of output tiles."""
     import numpy as np
@@ -167,6 +186,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pipeline", type=int, default=0,
                     help="1: rectangles alternate between two workspace arenas on two streams")
+    ap.add_argument("--comparator", action="store_true",
+                    help="also time the per-contraction-tile loop (one pass over C per k) on operands padded to "
+                         "one rank: the batched-GEMM comparator the three-stage product is set against")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -283,6 +305,32 @@ def main():
         del Ad, Bd, Cw
         torch.cuda.empty_cache()
 
+    comparator = None
+    if args.comparator and not (dense_a or dense_b):
+        rmax = int(max(np.max(A.ranks), np.max(B.ranks)))
+        log(f"bench: per-k comparator, ranks padded to {rmax}")
+        Ap, Bp = padded_copy(A, rmax), padded_copy(B, rmax)
+        dAp, dBp = DeviceTLR(Ap), DeviceTLR(Bp)
+        gk = TLRGemm(dtype, cfg["opA"], dAp, cfg["opB"], dBp, ldc=N, flags=T.TLR_PLAN_PER_K)
+        for _ in range(2):
+            gk(cfg["alpha"], dAp, dBp, cfg["beta"], Cd, [stream.cuda_stream])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            gk(cfg["alpha"], dAp, dBp, cfg["beta"], Cd, [stream.cuda_stream])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kms = e0.elapsed_time(e1) / reps
+        comparator = {"ms": round(kms, 3), "speedup": round(kms / ms, 3), "padded_rank": rmax,
+                      "passes_over_C": gk.info["runs"], "executed_flops": gk.info["useful_flops"],
+                      "note": "per contraction tile k: batched couplings, right products and updates of every "
+                              "output tile at one common rank, C read and written once per k; speedup = its "
+                              "time / the three-stage product's"}
+        del gk, dAp, dBp, Ap, Bp
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         log("bench: CPU oracle baseline on a bounded sample")
@@ -309,6 +357,8 @@ def main():
         "dense_reference": dense,
         "cpu_baseline": cpu,
     }
+    if comparator is not None:
+        out["per_k_comparator"] = comparator
     print(json.dumps(out), flush=True)
 
 

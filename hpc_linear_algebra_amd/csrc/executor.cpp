@@ -269,7 +269,8 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
           if (pairs_ok ? L.mode_tiles[m] == 0 : m > 0) continue;
           const int mode = pairs_ok ? m : LOAD_SINGLE;
           const int64_t off = pairs_ok ? L.mode_off[m] : 0, n = pairs_ok ? L.mode_tiles[m] : L.n_tiles;
-          int e = launch_grouped(p->dt, L.stage, mode, L.bn, tasks, tiles + L.tile_off + off, n, ctab, bases, alpha, beta, sl);
+          int e = launch_grouped(p->dt, L.stage, mode, L.bn, tasks, tiles + L.tile_off + off, n, ctab, bases, alpha,
+                                 L.beta_one ? 1.0 : beta, sl);
           if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
         }
         if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sl));
@@ -292,7 +293,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
             HIP_TRY(hipStreamWaitEvent(sm, fork, 0));
           }
           int e = launch_grouped(p->dt, L.stage, m, L.bn, tasks, tiles + L.tile_off + L.mode_off[m], L.mode_tiles[m],
-                                 ctab, bases, alpha, beta, sm);
+                                 ctab, bases, alpha, L.beta_one ? 1.0 : beta, sm);
           if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
           if (part > 0) {
             hipEvent_t join = static_cast<hipEvent_t>(p->mode_events[3 * l + part]);
@@ -303,7 +304,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
         }
       } else {
         int e = launch_grouped(p->dt, L.stage, LOAD_SINGLE, L.bn, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases,
-                               alpha, beta, sg);
+                               alpha, L.beta_one ? 1.0 : beta, sg);
         if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
       }
       if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));

@@ -547,6 +547,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.rect = rect;
   L.wait_launch = -1;
   L.fork_at = -1;
+  L.beta_one = false;
   L.n_tasks = (int64_t)tl.t.size();
   L.useful_flops = 0;
   L.executed_flops = 0;
@@ -1037,6 +1038,7 @@ static tlr_status validate(const Plan &p, bool deep) {
   std::vector<uint8_t> ws((size_t)z.n[BASE_WS], 0);
   std::vector<uint64_t> cbits((size_t)((z.n[BASE_C] + 63) / 64), 0);
   int64_t cwrites = 0;
+  const bool per_k = (p.flags & TLR_PLAN_PER_K) != 0;
   auto for_elems = [&](const DevOperand &o, int64_t rows, int64_t cols, auto &&fn) {
     const bool fc = o.trans == 0;
     const int64_t a = fc ? rows : cols, c = fc ? cols : rows;
@@ -1055,6 +1057,9 @@ static tlr_status validate(const Plan &p, bool deep) {
         rect_lo = (int64_t)(G.arena_off / (size_t)p.es);
         rect_hi = (int64_t)((G.arena_off + G.arena_bytes) / (size_t)p.es);
         std::fill(ws.begin() + rect_lo, ws.begin() + rect_hi, 0);
+        // the per-k loop: every rectangle is one more pass over C; the first
+        // writes each element once, a later one each at most once
+        if (per_k && L.rect > 0) std::fill(cbits.begin(), cbits.end(), 0);
       }
       // workspace marks: the writer's stage.  A stage reads what earlier
       // stages of its rectangle wrote; the side launch runs beside stages 1
@@ -1099,7 +1104,7 @@ static tlr_status validate(const Plan &p, bool deep) {
               if (word & bit) return fail(TLR_ERR_INVALID_ARG, "internal: element of C written twice");
               if (e % p.ldc >= p.m) return fail(TLR_ERR_INVALID_ARG, "internal: write into C's padding");
               word |= bit;
-              cwrites++;
+              if (!per_k || L.rect == 0) cwrites++;
             } else {
               return fail(TLR_ERR_INVALID_ARG, "internal: task writes an input buffer");
             }
@@ -1112,6 +1117,131 @@ static tlr_status validate(const Plan &p, bool deep) {
   return TLR_OK;
 }
 
+// The per-contraction-tile loop ("Many small GEMMs"): for each k, launch 1
+// forms the couplings S_ij = V_ik^T W_kj (and, at dense diagonal tiles,
+// X_j = op(D_A,kk) W_kj and Y_i = V_ik^T op(D_B,kk)), launch 2 the right
+// products T_ij = S_ij Z_kj^T, and launch 3 adds U_ik T_ij (or X_j Z_kj^T,
+// U_ik Y_i, op(D_A,kk) op(D_B,kk)) into every output tile, with the caller's
+// beta in the first pass and beta = 1 after: one pass over C per k.  Each k
+// is one rectangle over all of C reusing the workspace of the previous one.
+static tlr_status build_per_k(Plan &p, const Sums &s) {
+  const View &A = p.A, &B = p.B;
+  const int qm = s.qm, qk = s.qk, qn = s.qn;
+  const int64_t es = p.es, b = A.b;
+  p.rects.clear();
+  p.groups.clear();
+  if (qm == 0 || qn == 0) return TLR_OK;
+  // workspace of one pass (every buffer 256-B aligned, slots at even offsets)
+  struct Slots { std::vector<int64_t> S, T, X, Y; size_t bytes = 0; };
+  auto slots = [&](int k, Slots &o) {
+    o.S.assign((size_t)qm * qn, -1);
+    o.T.assign((size_t)qm * qn, -1);
+    o.X.assign(qn, -1);
+    o.Y.assign(qm, -1);
+    int64_t cur = 0;
+    auto take = [&](int64_t elems) { int64_t off = cur; cur += even_up(elems); return off; };
+    for (int i = 0; i < qm; ++i)
+      for (int j = 0; j < qn; ++j) {
+        const bool ad = A.diag && i == k, bd = B.diag && k == j;
+        if (!ad && !bd && A.r(i, k) > 0 && B.r(k, j) > 0) {
+          o.S[(size_t)i + (size_t)j * qm] = take((int64_t)A.r(i, k) * B.r(k, j));
+          o.T[(size_t)i + (size_t)j * qm] = take((int64_t)A.r(i, k) * p.ns[j]);
+        }
+      }
+    for (int j = 0; j < qn; ++j)
+      if (A.diag && k < qm && !(B.diag && k == j) && B.r(k, j) > 0) o.X[j] = take(A.rs[k] * (int64_t)B.r(k, j));
+    for (int i = 0; i < qm; ++i)
+      if (B.diag && k < qn && !(A.diag && i == k) && A.r(i, k) > 0) o.Y[i] = take((int64_t)A.r(i, k) * p.ns[k]);
+    o.bytes = align_up((size_t)cur * (size_t)es, WS_ALIGN);
+  };
+  size_t need = 0;
+  for (int k = 0; k < qk; ++k) { Slots o; slots(k, o); need = std::max(need, o.bytes); }
+  if (p.budget && need > p.budget)
+    return fail(TLR_ERR_WORKSPACE, "the per-k loop needs " + std::to_string(need) + " B of workspace");
+  Group G;
+  G.stream = 0;
+  G.arena_off = 0;
+  G.arena_bytes = need;
+  p.groups.push_back(G);
+  p.ws_bytes = need;
+  for (int k = 0; k < qk; ++k) {
+    Slots o;
+    slots(k, o);
+    const int rect = (int)p.rects.size();
+    p.rects.push_back(Rect{0, qm, 0, qn, TLR_ORDER_RIGHT, 0, o.bytes, 0});
+    p.groups[0].rects.push_back(rect);
+    TaskList l1, l2, l3;
+    const int64_t sk = A.cs[k];
+    for (int i = 0; i < qm; ++i)
+      for (int j = 0; j < qn; ++j) {
+        const size_t ij = (size_t)i + (size_t)j * qm;
+        if (o.S[ij] < 0) continue;
+        const int32_t ra = A.r(i, k), rb = B.r(k, j);
+        DevTask d = new_task(ra, rb, BASE_WS, o.S[ij], ra, -1, false);
+        add_seg(d, opnd(A.inner_base, A.ic(i, k) * b, b, 1), opnd(B.outer_base, B.oc(k, j) * b, b, 0), sk);
+        l1.t.push_back(d);
+        l1.useful.push_back(2.0 * ra * (double)rb * sk);
+        DevTask e = new_task(ra, p.ns[j], BASE_WS, o.T[ij], ra, -1, false);
+        add_seg(e, opnd(BASE_WS, o.S[ij], ra, 0), opnd(B.inner_base, B.ic(k, j) * b, b, 1), rb);
+        l2.t.push_back(e);
+        l2.useful.push_back(2.0 * ra * (double)p.ns[j] * rb);
+      }
+    for (int j = 0; j < qn; ++j)
+      if (o.X[j] >= 0) {
+        DevTask d = new_task(A.rs[k], B.r(k, j), BASE_WS, o.X[j], A.rs[k], -1, false);
+        add_seg(d, opnd(A.diag_base, (int64_t)k * b * b, b, A.diag_trans), opnd(B.outer_base, B.oc(k, j) * b, b, 0), sk);
+        l1.t.push_back(d);
+        l1.useful.push_back(2.0 * A.rs[k] * (double)B.r(k, j) * sk);
+      }
+    for (int i = 0; i < qm; ++i)
+      if (o.Y[i] >= 0) {
+        DevTask d = new_task(A.r(i, k), p.ns[k], BASE_WS, o.Y[i], A.r(i, k), -1, false);
+        add_seg(d, opnd(A.inner_base, A.ic(i, k) * b, b, 1), opnd(B.diag_base, (int64_t)k * b * b, b, B.diag_trans), sk);
+        l1.t.push_back(d);
+        l1.useful.push_back(2.0 * A.r(i, k) * (double)p.ns[k] * sk);
+      }
+    for (int j = 0; j < qn; ++j)
+      for (int i = 0; i < qm; ++i) {
+        DevTask d = new_task(A.rs[i], p.ns[j], BASE_C, A.ro[i] + p.no[j] * p.ldc, p.ldc, -1, true);
+        const size_t ij = (size_t)i + (size_t)j * qm;
+        const bool ad = A.diag && i == k, bd = B.diag && k == j;
+        double u = 0;
+        if (ad && bd) {
+          add_seg(d, opnd(A.diag_base, (int64_t)k * b * b, b, A.diag_trans), opnd(B.diag_base, (int64_t)k * b * b, b, B.diag_trans), sk);
+          u = 2.0 * A.rs[i] * (double)p.ns[j] * sk;
+        } else if (ad) {
+          if (o.X[j] >= 0) {
+            add_seg(d, opnd(BASE_WS, o.X[j], A.rs[k], 0), opnd(B.inner_base, B.ic(k, j) * b, b, 1), B.r(k, j));
+            u = 2.0 * A.rs[i] * (double)p.ns[j] * B.r(k, j);
+          }
+        } else if (bd) {
+          if (o.Y[i] >= 0) {
+            add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), opnd(BASE_WS, o.Y[i], A.r(i, k), 0), A.r(i, k));
+            u = 2.0 * A.rs[i] * (double)p.ns[j] * A.r(i, k);
+          }
+        } else if (o.S[ij] >= 0) {
+          add_seg(d, opnd(A.outer_base, A.oc(i, k) * b, b, 0), opnd(BASE_WS, o.T[ij], A.r(i, k), 0), A.r(i, k));
+          u = 2.0 * A.rs[i] * (double)p.ns[j] * A.r(i, k);
+        }
+        // a later pass skips tiles without a term; the first pass writes every
+        // tile (beta C alone where there is none)
+        if (d.nseg == 0 && k > 0) continue;
+        l3.t.push_back(d);
+        l3.useful.push_back(u);
+      }
+    double F = 0;
+    for (double x : l1.useful) F += x;
+    for (double x : l2.useful) F += x;
+    for (double x : l3.useful) F += x;
+    p.rects[rect].useful_flops = F;
+    emit_launch(p, 1, 0, rect, l1);
+    emit_launch(p, 2, 0, rect, l2);
+    const int c = emit_launch(p, 3, 0, rect, l3);
+    if (c >= 0 && k > 0) p.launches[c].beta_one = true;
+  }
+  return TLR_OK;
+}
+
 tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, const tlr_shape *B,
                       int64_t dense_rows, int64_t dense_cols, int64_t ldb, int64_t ldc, size_t budget,
                       int n_streams, uint32_t flags, bool build_descriptors, Plan *p) {
@@ -1121,7 +1251,8 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   if (n_streams < 1) return fail(TLR_ERR_INVALID_ARG, "n_streams must be >= 1");
   if ((flags & TLR_PLAN_FORCE_RIGHT) && (flags & TLR_PLAN_FORCE_LEFT))
     return fail(TLR_ERR_INVALID_ARG, "cannot force both orders");
-  if (flags & ~(TLR_PLAN_FORCE_RIGHT | TLR_PLAN_FORCE_LEFT | TLR_PLAN_NO_REGIONS | TLR_PLAN_VALIDATE | TLR_PLAN_PIPELINE))
+  if (flags & ~(TLR_PLAN_FORCE_RIGHT | TLR_PLAN_FORCE_LEFT | TLR_PLAN_NO_REGIONS | TLR_PLAN_VALIDATE | TLR_PLAN_PIPELINE |
+                TLR_PLAN_PER_K))
     return fail(TLR_ERR_INVALID_ARG, "unknown flag bits");
   if ((flags & TLR_PLAN_PIPELINE) && n_streams < 2)
     return fail(TLR_ERR_INVALID_ARG, "pipelining needs n_streams >= 2");
@@ -1223,18 +1354,33 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
                                   (p->dense_b ? (double)dense_rows * dense_cols : compressed_elems(p->B)) +
                                   (double)p->m * p->n);
 
-  st = schedule(*p, s);
-  if (st != TLR_OK) return st;
+  const bool per_k = (flags & TLR_PLAN_PER_K) != 0;
+  if (per_k) {
+    if (p->dense_a || p->dense_b) return fail(TLR_ERR_UNSUPPORTED, "the per-k loop needs two TLR operands");
+    if (flags & (TLR_PLAN_PIPELINE | TLR_PLAN_FORCE_LEFT))
+      return fail(TLR_ERR_UNSUPPORTED, "the per-k loop takes neither pipelining nor the left order");
+    p->tasks.clear();
+    p->tiles.clear();
+    p->coltab.clear();
+    p->launches.clear();
+    st = build_per_k(*p, s);
+    if (st != TLR_OK) return st;
+  } else {
+    st = schedule(*p, s);
+    if (st != TLR_OK) return st;
+  }
   p->useful_flops = 0;
   for (auto &r : p->rects) p->useful_flops += r.useful_flops;
   if (!build_descriptors) return TLR_OK;
 
-  p->tasks.clear();
-  p->tiles.clear();
-  p->coltab.clear();
-  p->launches.clear();
-  for (size_t g = 0; g < p->groups.size(); ++g)
-    for (int r : p->groups[g].rects) emit_rect(*p, s, r);
+  if (!per_k) {
+    p->tasks.clear();
+    p->tiles.clear();
+    p->coltab.clear();
+    p->launches.clear();
+    for (size_t g = 0; g < p->groups.size(); ++g)
+      for (int r : p->groups[g].rects) emit_rect(*p, s, r);
+  }
   // output columns that start on a 16-byte boundary allow 16-byte C accesses
   const int64_t vec_el = 16 / p->es;
   for (DevTask &d : p->tasks) {

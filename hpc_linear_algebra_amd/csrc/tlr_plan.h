@@ -55,6 +55,7 @@ struct Launch {
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
   int bn;            // block columns of the launch's workgroups (BN or BN_NARROW)
+  bool beta_one;     // a later pass of the per-k loop over C: its updates use beta = 1
   int64_t task_off;  // the launch's tasks are tasks[task_off, task_off + n_tasks)
   int64_t tile_off;  // first DevTile of the launch in the tile table
   int64_t n_tiles;   // workgroups launched (padded to a multiple of NUM_XCD)

@@ -22,6 +22,7 @@ TLR_OP_N, TLR_OP_T = 0, 1
 TLR_ORDER_RIGHT, TLR_ORDER_LEFT = 0, 1
 TLR_PLAN_FORCE_RIGHT, TLR_PLAN_FORCE_LEFT, TLR_PLAN_NO_REGIONS, TLR_PLAN_VALIDATE = 0x1, 0x2, 0x4, 0x8
 TLR_PLAN_PIPELINE = 0x10
+TLR_PLAN_PER_K = 0x20
 
 EXPORTED = [
     "tlr_gemm_analyze", "tlr_gemm_workspace_bytes", "tlr_plan_info", "tlr_plan_rect",

@@ -79,6 +79,12 @@ typedef enum { TLR_ORDER_RIGHT = 0, TLR_ORDER_LEFT = 1 } tlr_order;
 #define TLR_PLAN_VALIDATE    0x8u  /* also run the exhaustive descriptor self-check (slow; for tests) */
 #define TLR_PLAN_PIPELINE    0x10u /* two arenas on two streams: stages 1-2 of one rectangle run beside
                                       stage 3 of the previous one (needs n_streams >= 2) */
+#define TLR_PLAN_PER_K       0x20u /* the per-contraction-tile loop instead ("Many small GEMMs"): for
+                                      each k, the coupling V_ik^T W_kj, the right product S Z_kj^T
+                                      and the update C_ij += U_ik T of every output tile, one pass
+                                      over C per k (TLR x TLR only; a comparator: with operands
+                                      padded to one rank it is the batched-GEMM baseline the page
+                                      compares against) */
 
 /* Structure of one stored TLR operand (host data; no device pointers). */
 typedef struct {

@@ -314,3 +314,30 @@ def test_dense_a_errors():
     with pytest.raises(T.TLRError) as e:
         T.tlr_gemm_analyze("f64", "N", None, "N", B, 10, 24, ldb=10, ldc=10, flags=T.TLR_PLAN_FORCE_RIGHT)
     assert e.value.status == T.TLR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_per_k_plans(seed):
+    # the per-contraction-tile loop (comparator): its flop count equals the
+    # brute-force tile loop's own multiply-add count, one rectangle (pass over
+    # C) per contraction tile, and the exhaustive check passes (the first pass
+    # writes C once, later passes each element at most once)
+    from oracle import brute
+    from tlr_inputs import random_tlr
+    rng = np.random.default_rng(70 + seed)
+    n, b = ((9, 3), (10, 4), (7, 2), (12, 5), (8, 4))[seed]
+    diag = seed != 3
+    A = random_tlr(rng, n, n, b, rank_lo=0, has_diag=diag, scale=1.0)
+    B = random_tlr(rng, n, n, b, rank_lo=0, has_diag=diag, scale=1.0)
+    for opA, opB in (("N", "N"), ("T", "N"), ("N", "T"), ("T", "T")):
+        sa, sb = T.Shape(n, n, b, A.ranks, diag), T.Shape(n, n, b, B.ranks, diag)
+        p = T.tlr_gemm_analyze("f64", opA, sa, opB, sb, ldc=n + 1, flags=T.TLR_PLAN_PER_K | T.TLR_PLAN_VALIDATE)
+        info = T.tlr_plan_info(p)
+        _, flops = brute.tile_loop(1.0, opA, A, opB, B, 0.0, None, "right")
+        assert info["useful_flops"] == flops
+        assert info["runs"] == len(tile_sizes(n, b))
+        stages = [T.tlr_plan_launch(p, l)["stage"] for l in range(info["launches"])]
+        assert set(stages) <= {1, 2, 3} and stages.count(3) == info["runs"]
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_analyze("f64", "N", sa, "N", None, n, n, ldb=n, ldc=n, flags=T.TLR_PLAN_PER_K)
+    assert e.value.status == T.TLR_ERR_UNSUPPORTED
