@@ -213,9 +213,15 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
   bases.p[BASE_B_DENSE] = B_dense;
   bases.p[BASE_WS] = ws;
   bases.p[BASE_C] = C;
-  // the pair load modes assume every buffer aligned to a pair of elements;
-  // otherwise each launch runs its whole table in single-element mode
-  const bool pairs_ok = bases_pair_aligned(bases, p->es);
+  // the 16-bit kernel moves whole 16-byte vectors; the pair load modes of the
+  // 32/64-bit kernel assume every buffer aligned to a pair of elements,
+  // otherwise each launch runs its whole table in single-element mode (the
+  // 16-bit kernel takes one launch per table, whatever the mode split)
+  if (p->es == 2)
+    for (const void *x : bases.p)
+      if (reinterpret_cast<uintptr_t>(x) % 16 != 0)
+        return fail(TLR_ERR_INVALID_ARG, "execute: 16-bit buffers must be 16-byte aligned");
+  const bool pairs_ok = p->es != 2 && bases_pair_aligned(bases, p->es);
   const char *dd = static_cast<const char *>(p->dev_desc);
   const DevTask *tasks = reinterpret_cast<const DevTask *>(dd + p->task_bytes_off);
   const DevTile *tiles = reinterpret_cast<const DevTile *>(dd + p->tile_bytes_off);
@@ -334,6 +340,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
 tlr_status dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n, int64_t k, double alpha,
                       const void *A, int64_t lda, const void *B, int64_t ldb, double beta, void *C, int64_t ldc,
                       void *stream) {
+  if (dt == TLR_F16 || dt == TLR_BF16) return fail(TLR_ERR_UNSUPPORTED, "dense: 16-bit types run only inside the TLR product");
   if (dt != TLR_F32 && dt != TLR_F64) return fail(TLR_ERR_INVALID_ARG, "dense: bad dtype");
   if ((opA != TLR_OP_N && opA != TLR_OP_T) || (opB != TLR_OP_N && opB != TLR_OP_T))
     return fail(TLR_ERR_INVALID_ARG, "dense: bad op");

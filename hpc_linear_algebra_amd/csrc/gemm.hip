@@ -606,6 +606,8 @@ void launch_single_t(int mode, unsigned n, hipStream_t s, const DevTask &task, c
 int launch_grouped(tlr_dtype dt, int stage, int mode, int bn, const DevTask *tasks, const DevTile *tiles,
                    int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,
                    void *stream) {
+  if (dt == TLR_F16 || dt == TLR_BF16)
+    return launch_grouped16(dt, stage, bn, tasks, tiles, n_tiles, coltab, bases, alpha, beta, stream);
   if (n_tiles <= 0) return 0;
   if (bn != Blk<4>::KBN && bn != Blk<8>::KBN) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -631,6 +633,7 @@ int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &base
 }
 
 int launch_scale(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta, void *stream) {
+  if (dt == TLR_F16 || dt == TLR_BF16) return launch_scale16(dt, C, m, n, ldc, beta, stream);
   if (m <= 0 || n <= 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t total = m * n;

@@ -1,0 +1,361 @@
+// Grouped, segmented-K MFMA GEMM for gfx950 (CDNA4), IEEE half and bfloat16.
+//
+// The same task tables as the 32/64-bit kernel (tlr_desc.h): each workgroup
+// reads one entry (task, m0, n0) and computes a 128 x BN block of that task's
+// output (BN = 128 or 64, chosen per launch), accumulating over the task's K
+// segments in float with v_mfma_f32_16x16x32_{f16,bf16}, then writes
+// C = alpha*acc + beta*C (final update) or C = acc (workspace intermediates),
+// rounded once to the 16-bit type.
+//
+// Every extent, offset and leading dimension is a multiple of 8 (the host
+// enforces it: stored ranks rounded up to a multiple of 8), so operands move
+// in 16-byte vectors of 8 elements along their contiguous index and a vector
+// lies wholly inside or wholly outside its operand.
+//
+// The 16-bit matrix cores take, per lane, 8 consecutive k of one row of A and
+// of one column of B.  Both operands therefore pass through LDS stored
+// K-contiguous: [row][k] for A, [column][k] for B, rows of 64 k padded to 72
+// elements (144 bytes: consecutive rows start four banks apart).  A stage
+// (64 k) is cut into 8 x 8 units, one per thread (threads 0..127: the A tile,
+// 128..255: the B tile); a thread loads its unit as eight 16-byte vectors.  An
+// operand that is K-contiguous in memory gives eight row pieces that go to LDS
+// as they are; an M- (or N-) contiguous one gives eight k-columns of 8 rows,
+// transposed in registers (v_perm_b32) before the eight 16-byte LDS stores.
+//
+// Work split: four wave64s in a 2 x 2 grid, each owning a 64 x BN/2 strip of
+// the block as 4 x (BN/32) MFMA tiles of 16 x 16.  LDS holds two stages; the
+// global loads of stage s+1 are in flight while stage s's MFMAs run, and one
+// barrier per stage separates the LDS stores from the next reads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "tlr_plan.h"
+
+namespace tlr {
+
+namespace {
+
+constexpr int BM16 = 128;        // block rows
+constexpr int KS = 64;           // k per stage
+constexpr int LROW = 72;         // LDS row stride in elements (64 k + 8)
+constexpr int NT16 = 256;        // four wave64s
+
+template <int NJ> struct Blk16 {
+  static constexpr int BN = 32 * NJ;   // block columns: two waves along N, NJ 16-column tiles each
+};
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// H: _Float16 or __bf16.  mma: one 16 x 16 x 32 product; lane l supplies
+// A[l % 16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l % 16] (any fixed
+// assignment of the 32 k to lanes gives the same sum, provided A and B use
+// the same one), and holds D[4*(l/16) + v][l % 16] in element v afterwards.
+template <typename H> struct M16;
+template <> struct M16<_Float16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f4 mma(u4 a, u4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+};
+template <> struct M16<__bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f4 mma(u4 a, u4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+};
+
+constexpr uint32_t OOB16 = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc16(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// LDS row of block row m in the A tile.  After the MFMAs, lane (r, g) of
+// tile i = 2h + p holds rows 4g .. 4g+3 of that tile; the A rows are placed so
+// that those are block rows 64w + 32h + 8g + 4p + v: the lane then holds the 8
+// consecutive rows 64w + 32h + 8g .. +7 of each column, one 16-byte unit of C.
+// In bits: m = [w h | g g | p | v v] sits at LDS row [w h | p | g g | v v].
+__device__ __forceinline__ int a_lds_row(int m) { return (m & ~0x1C) | ((m & 0x4) << 2) | ((m & 0x18) >> 1); }
+
+// 8 x 8 transpose of 16-bit elements: x[e] holds (s = e, c = 0..7); y[c]
+// holds (s = 0..7, c).  Dword w of a vector holds elements 2w (low half) and
+// 2w+1 (high half).
+__device__ __forceinline__ void transpose8(const u4 (&x)[8], u4 (&y)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of (lo, hi)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) y[c][w] = __builtin_amdgcn_perm(x[2 * w + 1][c >> 1], x[2 * w][c >> 1], sel);
+  }
+}
+
+// One operand tile of a stage as seen by one loading thread: unit (rg, kg) =
+// rows 8rg .. 8rg+7 (of the A tile, or columns of the B tile) and k
+// 8kg .. 8kg+7.  With kc (K-contiguous) vector e is row 8rg+e at k 8kg;
+// otherwise it is k 8kg+e at rows 8rg .. 8rg+7.  The uniform part e*ld of the
+// address goes into the instruction's scalar offset.
+struct Unit {
+  const uint16_t *base;   // operand at (row 0 of the block, k 0)
+  int64_t kstep;          // elements per stage along k
+  uint32_t lane;          // byte offset of the thread's vector 0
+  uint32_t ldb;           // leading dimension in bytes
+  int s0, s_lim, c0, c_lim;   // strided / contiguous index of vector 0 and their limits
+  bool kc;
+};
+
+__device__ __forceinline__ void load_unit(const Unit &u, int st, int krem, u4 (&x)[8]) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc16(u.base + (int64_t)st * u.kstep);
+  // k limit of this stage: contiguous index for kc, strided otherwise
+  const int s_lim = u.kc ? u.s_lim : krem, c_lim = u.kc ? krem : u.c_lim;
+  const bool cok = u.c0 < c_lim;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bool ok = cok && u.s0 + e < s_lim;
+    x[e] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? u.lane : OOB16, e * u.ldb, 0));
+  }
+}
+
+// LDS stores of a unit: row (of the tile) 8rg + e gets k 8kg .. 8kg+7.
+template <bool IS_A>
+__device__ __forceinline__ void store_unit(uint16_t *tile, int rg, int kg, bool kc, const u4 (&x)[8]) {
+  u4 y[8];
+  if (!kc) transpose8(x, y);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = IS_A ? a_lds_row(8 * rg + e) : 8 * rg + e;
+    *reinterpret_cast<u4 *>(tile + row * LROW + 8 * kg) = kc ? x[e] : y[e];
+  }
+}
+
+template <typename H> __device__ __forceinline__ float to_f(uint16_t v) {
+  return (float)__builtin_bit_cast(H, v);
+}
+template <typename H> __device__ __forceinline__ uint16_t from_f(float v) {
+  return __builtin_bit_cast(uint16_t, (H)v);
+}
+
+template <typename H, int NJ>
+__device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, const int64_t *coltab,
+                                             const Bases &bases, float alpha, float beta, float cscale) {
+  constexpr int BN = Blk16<NJ>::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM16 * LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LROW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = t.M, N = t.N;
+
+  uint16_t *C = static_cast<uint16_t *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
+  const bool fin = t.final_ != 0;
+  const bool preload = fin && cscale != 0.0f;
+  const bool rd = fin && beta != 0.0f && !preload;
+
+  // output columns of the lane (every column offset a multiple of 8 elements)
+  int64_t ocol[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * 16 * NJ + 16 * j + r;
+    ocol[j] = n >= N ? 0 : (t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n]);
+  }
+  f4 acc[4][NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * 16 * NJ + 16 * j + r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      acc[2 * h][j] = f4{0, 0, 0, 0};
+      acc[2 * h + 1][j] = f4{0, 0, 0, 0};
+      const int m = m0 + 64 * wm + 32 * h + 8 * g;
+      if (preload && n < N && m < M) {
+        const u4 x = *reinterpret_cast<const u4 *>(C + ocol[j] + m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[2 * h + (e >> 2)][j][e & 3] = cscale * to_f<H>((uint16_t)(x[e >> 1] >> (16 * (e & 1))));
+      }
+    }
+  }
+
+  // loading role: threads 0..127 the A tile (16 x 8 units), 128..255 the B tile
+  const bool loads_a = wave < 2;
+  const int uidx = loads_a ? tid : tid - 128;
+  const int kg = uidx & 7, rg = uidx >> 3;
+  const bool has_unit = loads_a || rg < BN / 8;
+
+  for (int sidx = 0; sidx < t.nseg; ++sidx) {
+    const DevSeg &d = t.seg[sidx];
+    const int K = d.K;
+    if (K <= 0) continue;
+    const int nst = (K + KS - 1) / KS;
+    // operand of this thread's unit
+    Unit u;
+    {
+      const DevOperand &o = loads_a ? d.a : d.b;
+      const uint16_t *p = static_cast<const uint16_t *>(bases.p[o.base]) + o.off;
+      const int64_t ld = o.ld;
+      // A: trans 1 = K-contiguous; B: trans 0 = K-contiguous
+      u.kc = loads_a ? o.trans == 1 : o.trans == 0;
+      const int first = loads_a ? m0 : n0;
+      const int rem = loads_a ? M - m0 : N - n0;
+      u.base = u.kc ? p + (int64_t)first * ld : p + first;
+      u.kstep = u.kc ? KS : (int64_t)KS * ld;
+      u.ldb = (uint32_t)(ld * 2);
+      const int srow = u.kc ? 8 * rg : 8 * kg, ccol = u.kc ? 8 * kg : 8 * rg;
+      u.lane = (uint32_t)((int64_t)srow * ld + ccol) * 2u;
+      u.s0 = srow;
+      u.c0 = ccol;
+      u.s_lim = u.kc ? rem : 0;   // the k limit is filled in per stage
+      u.c_lim = u.kc ? 0 : rem;
+    }
+    u4 x[8];
+    if (has_unit) {
+      load_unit(u, 0, K, x);
+      if (loads_a) store_unit<true>(As[0], rg, kg, u.kc, x);
+      else store_unit<false>(Bs[0], rg, kg, u.kc, x);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      const bool more = st + 1 < nst;
+      if (more && has_unit) load_unit(u, st + 1, K - (st + 1) * KS, x);
+      const uint16_t *a_t = As[st & 1];
+      const uint16_t *b_t = Bs[st & 1];
+      const int krem = K - st * KS;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks == 1 && krem <= 32) break;   // every k of the second step is past K
+        u4 af[4], bf[NJ];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const u4 *>(a_t + (64 * wm + 16 * i + r) * LROW + 32 * ks + 8 * g);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          bf[j] = *reinterpret_cast<const u4 *>(b_t + (wn * 16 * NJ + 16 * j + r) * LROW + 32 * ks + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
+      }
+      if (more && has_unit) {
+        if (loads_a) store_unit<true>(As[(st + 1) & 1], rg, kg, u.kc, x);
+        else store_unit<false>(Bs[(st + 1) & 1], rg, kg, u.kc, x);
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane (r, g) holds rows 64wm + 32h + 8g .. +7 of each of its columns
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * 16 * NJ + 16 * j + r;
+    if (n >= N) continue;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + 64 * wm + 32 * h + 8 * g;
+      if (m >= M) continue;
+      u4 *q = reinterpret_cast<u4 *>(C + ocol[j] + m);
+      u4 old = u4{0, 0, 0, 0};
+      if (rd) old = *q;
+      u4 y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float v0 = acc[2 * h + (w >> 1)][j][2 * (w & 1)];
+        float v1 = acc[2 * h + (w >> 1)][j][2 * (w & 1) + 1];
+        if (fin) {
+          v0 *= alpha;
+          v1 *= alpha;
+          if (rd) {
+            v0 += beta * to_f<H>((uint16_t)(old[w] & 0xffffu));
+            v1 += beta * to_f<H>((uint16_t)(old[w] >> 16));
+          }
+        }
+        y[w] = (uint32_t)from_f<H>(v0) | ((uint32_t)from_f<H>(v1) << 16);
+      }
+      *q = y;
+    }
+  }
+}
+
+template <typename H, int STAGE, int NJ>
+__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_gemm16_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
+                           const int64_t *__restrict__ coltab, Bases bases, float alpha, float beta, float cscale) {
+  const DevTile e = tiles[blockIdx.x];
+  if (e.task < 0) return;
+  const DevTask &t = tasks[e.task];
+  const bool fin = t.final_ != 0;
+  gemm_block16<H, NJ>(t, e.m0, e.n0, coltab, bases, fin ? alpha : 1.0f, fin ? beta : 0.0f, fin ? cscale : 0.0f);
+}
+
+template <typename H>
+__global__ void scale16_kernel(uint16_t *C, int64_t m, int64_t n, int64_t ldc, float beta) {
+  const int64_t total = m * n;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = idx / m, r = idx - c * m;
+    uint16_t *p = C + r + c * ldc;
+    *p = beta == 0.0f ? from_f<H>(0.0f) : from_f<H>(beta * to_f<H>(*p));
+  }
+}
+
+float preload_scale16(double alpha, double beta) {
+  if (beta == 0.0 || alpha == 0.0) return 0.0f;
+  const double r = beta / alpha;
+  return (r == r && r < 1e30 && r > -1e30) ? (float)r : 0.0f;
+}
+
+template <typename H, int NJ>
+void launch16_w(int stage, dim3 grid, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                const int64_t *coltab, const Bases &bases, float a, float b, float c) {
+  const dim3 block(NT16);
+  if (stage == 1)
+    hipLaunchKernelGGL((grouped_gemm16_kernel<H, 1, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (stage == 2)
+    hipLaunchKernelGGL((grouped_gemm16_kernel<H, 2, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (stage == 3)
+    hipLaunchKernelGGL((grouped_gemm16_kernel<H, 3, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a, b, c);
+  else
+    hipLaunchKernelGGL((grouped_gemm16_kernel<H, STAGE_SIDE, NJ>), grid, block, 0, s, tasks, tiles, coltab, bases, a,
+                       b, c);
+}
+
+template <typename H>
+void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                const int64_t *coltab, const Bases &bases, double alpha, double beta) {
+  const float a = (float)alpha, b = (float)beta, c = preload_scale16(alpha, beta);
+  if (bn == Blk16<2>::BN)
+    launch16_w<H, 2>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
+  else
+    launch16_w<H, 4>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
+}
+
+}  // namespace
+
+int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
+                     const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
+  if (n_tiles <= 0) return 0;
+  if (bn != Blk16<2>::BN && bn != Blk16<4>::BN) return (int)hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == TLR_F16)
+    launch16_t<_Float16>(stage, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+  else
+    launch16_t<__bf16>(stage, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);
+  return (int)hipGetLastError();
+}
+
+int launch_scale16(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta, void *stream) {
+  if (m <= 0 || n <= 0) return 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = m * n;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  if (dt == TLR_F16)
+    hipLaunchKernelGGL(scale16_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t *>(C), m, n,
+                       ldc, (float)beta);
+  else
+    hipLaunchKernelGGL(scale16_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t *>(C), m, n, ldc,
+                       (float)beta);
+  return (int)hipGetLastError();
+}
+
+}  // namespace tlr

@@ -1242,10 +1242,51 @@ static tlr_status build_per_k(Plan &p, const Sums &s) {
   return TLR_OK;
 }
 
+// 16-bit types: the kernel moves operands in 16-byte vectors of 8 elements
+// along each operand's contiguous index, so every extent, offset and leading
+// dimension it meets must be a multiple of 8.  The stored ranks (rounded up to
+// a multiple of 8 by the caller, "Packing for the contraction"), the tile
+// size, the matrix dimensions and the leading dimensions being multiples of 8
+// makes every rank sum, tile size and workspace offset one.
+static tlr_status check_16bit(const Plan &p) {
+  auto m8 = [](int64_t x) { return x % 8 == 0; };
+  const char *why = nullptr;
+  if (!m8(p.m) || !m8(p.n) || !m8(p.k)) why = "16-bit types: every matrix dimension must be a multiple of 8";
+  else if (!m8(p.ldc)) why = "16-bit types: ldc must be a multiple of 8";
+  else if ((p.dense_a || p.dense_b) && (!m8(p.ldb) || !m8(p.dense_rows) || !m8(p.dense_cols)))
+    why = "16-bit types: the dense operand's dimensions and leading dimension must be multiples of 8";
+  if (why) return fail(TLR_ERR_INVALID_ARG, why);
+  for (const View *v : {&p.A, &p.B}) {
+    if ((v == &p.A && p.dense_a) || (v == &p.B && p.dense_b)) continue;
+    if (!m8(v->b)) return fail(TLR_ERR_INVALID_ARG, "16-bit types: the tile size must be a multiple of 8");
+    for (int32_t r : v->R)
+      if (!m8(r)) return fail(TLR_ERR_RANK, "16-bit types: every stored rank must be a multiple of 8");
+  }
+  return TLR_OK;
+}
+
+// The same condition on the built descriptors (a safety net: it follows from
+// check_16bit, and the kernel relies on it for in-bounds vector accesses).
+static tlr_status check_16bit_tasks(const Plan &p) {
+  auto m8 = [](int64_t x) { return x % 8 == 0; };
+  for (const DevTask &t : p.tasks) {
+    bool ok = m8(t.M) && m8(t.N) && m8(t.c_off) && (t.ctab >= 0 || m8(t.ldc));
+    if (t.ctab >= 0)
+      for (int n = 0; n < t.N && ok; ++n) ok = m8(p.coltab[t.ctab + n]);
+    for (int g = 0; g < t.nseg && ok; ++g) {
+      const DevSeg &d = t.seg[g];
+      ok = m8(d.K) && m8(d.a.off) && m8(d.a.ld) && m8(d.b.off) && m8(d.b.ld);
+    }
+    if (!ok) return fail(TLR_ERR_INVALID_ARG, "internal: a 16-bit task is not 8-element aligned");
+  }
+  return TLR_OK;
+}
+
 tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, const tlr_shape *B,
                       int64_t dense_rows, int64_t dense_cols, int64_t ldb, int64_t ldc, size_t budget,
                       int n_streams, uint32_t flags, bool build_descriptors, Plan *p) {
-  if (dt != TLR_F32 && dt != TLR_F64) return fail(TLR_ERR_INVALID_ARG, "dtype must be TLR_F32 or TLR_F64");
+  if (dt != TLR_F32 && dt != TLR_F64 && dt != TLR_F16 && dt != TLR_BF16)
+    return fail(TLR_ERR_INVALID_ARG, "dtype must be TLR_F32, TLR_F64, TLR_F16 or TLR_BF16");
   if ((opA != TLR_OP_N && opA != TLR_OP_T) || (opB != TLR_OP_N && opB != TLR_OP_T))
     return fail(TLR_ERR_INVALID_ARG, "op must be TLR_OP_N or TLR_OP_T");
   if (n_streams < 1) return fail(TLR_ERR_INVALID_ARG, "n_streams must be >= 1");
@@ -1257,7 +1298,7 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   if ((flags & TLR_PLAN_PIPELINE) && n_streams < 2)
     return fail(TLR_ERR_INVALID_ARG, "pipelining needs n_streams >= 2");
   p->dt = dt;
-  p->es = dt == TLR_F64 ? 8 : 4;
+  p->es = dt == TLR_F64 ? 8 : (dt == TLR_F32 ? 4 : 2);
   p->budget = budget;
   p->n_streams = n_streams;
   p->flags = flags;
@@ -1336,6 +1377,10 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
   if (p->m > std::numeric_limits<int32_t>::max() || p->n > std::numeric_limits<int32_t>::max())
     return fail(TLR_ERR_INVALID_ARG, "C dimensions too large");
   p->ldc = ldc;
+  if (p->es == 2) {
+    st = check_16bit(*p);
+    if (st != TLR_OK) return st;
+  }
 
   Sums s;
   build_sums(*p, s);
@@ -1398,6 +1443,10 @@ tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB, 
     for (int l : p->groups[0].launches)
       if (p->launches[l].rect == p->groups[0].rects[0] && p->launches[l].stage < 3) dep = l;
     p->launches[p->groups[1].launches[0]].wait_launch = dep;
+  }
+  if (p->es == 2) {
+    st = check_16bit_tasks(*p);
+    if (st != TLR_OK) return st;
   }
   p->executed_flops = 0;
   for (auto &L : p->launches) p->executed_flops += L.executed_flops;

@@ -152,6 +152,11 @@ int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &base
                   double beta, void *stream);
 int launch_scale(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta,
                  void *stream);
+// 16-bit types (gemm16.hip); launch_grouped and launch_scale forward to these.
+int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, const DevTile *tiles,
+                     int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,
+                     void *stream);
+int launch_scale16(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta, void *stream);
 
 // Error reporting.
 void set_error(const std::string &msg);

@@ -16,13 +16,13 @@ from . import layout
 from . import tlrgemm as T
 from tlr_inputs import TLRTiles
 
-_TORCH = {"f64": torch.float64, "f32": torch.float32}
+_TORCH = {"f64": torch.float64, "f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def _dev(x: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
+def _dev(x: Optional[np.ndarray], device, dtype: str) -> Optional[torch.Tensor]:
     if x is None or x.size == 0:
         return None
-    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=_TORCH[dtype])
 
 
 def _ptr(t: Optional[torch.Tensor]) -> int:
@@ -30,32 +30,44 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
 
 
 class DeviceTLR:
-    """A TLR operand packed on the host and copied to the GPU."""
+    """A TLR operand packed on the host and copied to the GPU.  For the 16-bit
+    types the stored ranks are the logical ranks rounded up to a multiple of 8
+    (zero factor columns); ``logical_ranks`` keeps the originals."""
 
     def __init__(self, t: TLRTiles, device="cuda"):
+        self.logical_ranks = np.asarray(t.ranks, dtype=np.int32)
+        if t.dtype in layout.SIXTEEN_BIT:
+            t = layout.round_ranks(t, 8)
         pk = layout.pack(t)
         self.rows, self.cols, self.b = t.rows, t.cols, t.b
         self.dtype = t.dtype
         self.has_diag = t.has_diag
         self.ranks = np.asarray(t.ranks, dtype=np.int32)
         self.shape = T.Shape(t.rows, t.cols, t.b, self.ranks, t.has_diag)
-        self.outer = _dev(pk["outer"], device)
-        self.inner = _dev(pk["inner"], device)
-        self.diag = _dev(pk["diag"], device)
+        self.outer = _dev(pk["outer"], device, t.dtype)
+        self.inner = _dev(pk["inner"], device, t.dtype)
+        self.diag = _dev(pk["diag"], device, t.dtype)
 
     def buffers(self) -> T.tlr_buffers:
         return T.buffers(_ptr(self.diag), _ptr(self.outer), _ptr(self.inner))
 
 
-def dense_to_device(M: np.ndarray, device="cuda", ld: Optional[int] = None) -> torch.Tensor:
-    """Column-major device copy: tensor of shape (cols, ld)."""
+def dense_to_device(M: np.ndarray, device="cuda", ld: Optional[int] = None,
+                    dtype: Optional[str] = None) -> torch.Tensor:
+    """Column-major device copy: tensor of shape (cols, ld), of element type
+    ``dtype`` (default: the array's own)."""
     rows, cols = M.shape
     ld = rows if ld is None else ld
-    return torch.from_numpy(layout.to_colmajor(M, ld).reshape(cols, ld)).to(device)
+    t = torch.from_numpy(layout.to_colmajor(M, ld).reshape(cols, ld))
+    return t.to(device) if dtype is None else t.to(device=device, dtype=_TORCH[dtype])
 
 
 def dense_from_device(t: torch.Tensor, rows: int, cols: int) -> np.ndarray:
-    return t.detach().cpu().numpy()[:, :rows].T
+    """Host copy as a [row, col] array (16-bit values widened to float32)."""
+    t = t.detach()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        t = t.float()
+    return t.cpu().numpy()[:, :rows].T
 
 
 class TLRGemm:

@@ -21,7 +21,37 @@ from tlr_inputs import TLRTiles
 
 
 def _np(dtype: str):
+    # 16-bit element types are held in float32 host arrays (values on the
+    # 16-bit grid) and converted when copied to the device
     return np.float64 if dtype == "f64" else np.float32
+
+
+SIXTEEN_BIT = ("f16", "bf16")
+
+
+def round_ranks(t: TLRTiles, multiple: int = 8) -> TLRTiles:
+    """The operand with every stored rank rounded up to a multiple of
+    ``multiple`` by appending zero factor columns (section "Packing for the
+    contraction": on the 16-bit paths each stored rank is a multiple of 8, so
+    every factor column offset is a multiple of 16 bytes; the logical rank, and
+    the matrix, are unchanged).  A rank never exceeds its tile's smaller side,
+    so that side must itself be a multiple of ``multiple`` wherever a rank is
+    rounded."""
+    U, V = {}, {}
+    R = np.array(t.ranks, dtype=np.int32, copy=True)
+    rs, cs = t.row_sizes, t.col_sizes
+    for (i, j), u in t.U.items():
+        v = t.V[(i, j)]
+        r = u.shape[1]
+        want = -(-r // multiple) * multiple
+        if want > min(rs[i], cs[j]):
+            raise ValueError(f"tile ({i},{j}): rank {r} cannot be rounded up to {want}")
+        if want > r:
+            u = np.concatenate([u, np.zeros((u.shape[0], want - r), u.dtype)], axis=1)
+            v = np.concatenate([v, np.zeros((v.shape[0], want - r), v.dtype)], axis=1)
+        U[(i, j)], V[(i, j)] = u, v
+        R[i, j] = want
+    return TLRTiles(t.rows, t.cols, t.b, R, t.diag, U, V, t.dtype)
 
 
 def pack(t: TLRTiles) -> Dict[str, Optional[np.ndarray]]:

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtlrgemm.
 
 TLR_OK, TLR_ERR_INVALID_ARG, TLR_ERR_RANK, TLR_ERR_WORKSPACE = 0, -1, -2, -3
 TLR_ERR_UNSUPPORTED, TLR_ERR_HIP, TLR_ERR_NOT_BOUND = -4, -5, -6
-TLR_F32, TLR_F64 = 0, 1
+TLR_F32, TLR_F64, TLR_F16, TLR_BF16 = 0, 1, 2, 3
 TLR_OP_N, TLR_OP_T = 0, 1
 TLR_ORDER_RIGHT, TLR_ORDER_LEFT = 0, 1
 TLR_PLAN_FORCE_RIGHT, TLR_PLAN_FORCE_LEFT, TLR_PLAN_NO_REGIONS, TLR_PLAN_VALIDATE = 0x1, 0x2, 0x4, 0x8
@@ -118,6 +118,10 @@ def _dt(x) -> int:
         return TLR_F64
     if x in ("f32", TLR_F32, np.float32):
         return TLR_F32
+    if x in ("f16", TLR_F16, np.float16):
+        return TLR_F16
+    if x in ("bf16", TLR_BF16):
+        return TLR_BF16
     raise ValueError(f"bad dtype {x!r}")
 
 

@@ -32,8 +32,22 @@
  * moves.
  *
  * Dense matrices (C, a dense B) are column-major with a leading dimension.
- * All element types are float (TLR_F32) or double (TLR_F64), the same for
- * every buffer of one call.
+ * All element types are float (TLR_F32), double (TLR_F64), IEEE half (TLR_F16)
+ * or bfloat16 (TLR_BF16), the same for every buffer of one call.
+ *
+ * 16-bit types (the half-precision paths of the first page's evaluation, run
+ * on the 16-bit matrix cores with float accumulation).  Every stored rank is
+ * a multiple of 8: a tile of logical rank r is stored with its rank rounded up
+ * to the next multiple of 8, the extra factor columns zero, which leaves the
+ * product unchanged and keeps every factor column offset a multiple of 16
+ * bytes (section "Packing for the contraction").  The tile size b, the
+ * dimensions of A, B and C and the leading dimensions ldb and ldc are
+ * multiples of 8 too, and every buffer is 16-byte aligned; analysis rejects
+ * anything else with TLR_ERR_INVALID_ARG (TLR_ERR_RANK for a rank), execution
+ * rejects a misaligned buffer.  The products are accumulated in float; each
+ * workspace intermediate (the coupling blocks, the right or left products)
+ * and C are rounded to the 16-bit type once, when written, and alpha and beta
+ * are applied in float.
  *
  * Ownership: every device buffer (factors, diagonals, dense B, C, workspace,
  * descriptor buffer) belongs to the caller.  The library never allocates
@@ -68,7 +82,7 @@ typedef enum {
   TLR_ERR_NOT_BOUND = -6     /* execute before tlr_plan_bind */
 } tlr_status;
 
-typedef enum { TLR_F32 = 0, TLR_F64 = 1 } tlr_dtype;
+typedef enum { TLR_F32 = 0, TLR_F64 = 1, TLR_F16 = 2, TLR_BF16 = 3 } tlr_dtype;
 typedef enum { TLR_OP_N = 0, TLR_OP_T = 1 } tlr_op;
 typedef enum { TLR_ORDER_RIGHT = 0, TLR_ORDER_LEFT = 1 } tlr_order;
 
@@ -278,7 +292,8 @@ tlr_status tlr_plan_profile_read(tlr_plan *p, double *stage_ms, double *launch_m
  * dense-GEMM time scaled by the ratio of executed flops).
  *   op(A) is m x k, op(B) is k x n, C is m x n; lda/ldb/ldc >= rows of the
  *   stored matrices, lda and ldb < 2^21.  beta == 0 never reads C.  No workspace.
- * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_HIP.
+ *   TLR_F32 and TLR_F64 only.
+ * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_UNSUPPORTED (a 16-bit type), TLR_ERR_HIP.
  */
 tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64_t n,
                           int64_t k, double alpha, const void *A, int64_t lda,

@@ -10,7 +10,14 @@ import numpy as np
 from oracle import reference
 from tlr_inputs import TLRTiles
 
-TOL = {"f64": 1e-12, "f32": 1e-5}
+# fp64 / fp32: the stated bars.  16-bit types: 2u, u the unit roundoff (2^-11
+# half, 2^-8 bfloat16).  The 16-bit path rounds the coupling blocks, the right
+# or left products and C once each; a rounding is a relative error of at most
+# u, about u/sqrt(3) RMS, and for inputs with independent signs the three add
+# in quadrature to about u in relative Frobenius norm (an emulation in float64
+# of exactly those roundings measured 0.43u-0.74u on the test shapes).  The
+# float accumulation adds at most K * 2^-24 per element, far below u.
+TOL = {"f64": 1e-12, "f32": 1e-5, "f16": 2.0 * 2.0 ** -11, "bf16": 2.0 * 2.0 ** -8}
 
 
 def say(*a):
@@ -44,7 +51,7 @@ def run_tlr(A, B, opA: str, opB: str, alpha: float, beta: float, C_in,
     dense_a = not isinstance(A, TLRTiles)
     dense = not isinstance(B, TLRTiles)
     dtype = dtype or (B.dtype if dense_a else A.dtype)
-    npd = np.float64 if dtype == "f64" else np.float32
+    npd = np.float64 if dtype == "f64" else np.float32   # 16-bit values travel in float32 arrays
     if dense_a:
         m = A.shape[0] if opA == "N" else A.shape[1]
     else:
@@ -57,21 +64,21 @@ def run_tlr(A, B, opA: str, opB: str, alpha: float, beta: float, C_in,
     Cstart = np.full((m, n), np.nan, dtype=npd) if C_in is None else np.asarray(C_in, dtype=npd)
     if dense_a:
         lda = max(1, A.shape[0] + ld_pad)
-        dA = dense_to_device(np.asarray(A, dtype=npd), ld=lda)
+        dA = dense_to_device(np.asarray(A, dtype=npd), ld=lda, dtype=dtype)
         dB = DeviceTLR(B)
         g = TLRGemm(dtype, opA, None, opB, dB, ldc=ldc, dense_shape=A.shape, ldb=lda, budget=budget,
                     n_streams=n_streams, flags=flags)
     elif dense:
         dA = DeviceTLR(A)
         ldb = max(1, B.shape[0] + ld_pad)
-        dB = dense_to_device(np.asarray(B, dtype=npd), ld=ldb)
+        dB = dense_to_device(np.asarray(B, dtype=npd), ld=ldb, dtype=dtype)
         g = TLRGemm(dtype, opA, dA, opB, None, ldc=ldc, dense_shape=B.shape, ldb=ldb, budget=budget,
                     n_streams=n_streams, flags=flags)
     else:
         dA = DeviceTLR(A)
         dB = DeviceTLR(B)
         g = TLRGemm(dtype, opA, dA, opB, dB, ldc=ldc, budget=budget, n_streams=n_streams, flags=flags)
-    Cd = dense_to_device(Cstart, ld=ldc)
+    Cd = dense_to_device(Cstart, ld=ldc, dtype=dtype)
     side = [torch.cuda.Stream() for _ in range(n_streams - 1)]
     streams = [torch.cuda.current_stream().cuda_stream] + [s.cuda_stream for s in side]
     g(alpha, dA, dB, beta, Cd, streams)

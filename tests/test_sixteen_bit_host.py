@@ -1,0 +1,91 @@
+"""16-bit element types on the host: the analysis rules of the half and
+bfloat16 paths (stored ranks, tile size, dimensions and leading dimensions
+multiples of 8), the rank rounding of the packing ("Tile-Low-Rank GEMM:
+Designing Storage Around the Contraction", section "Packing for the
+contraction"), and the 16-bit value grids of the input generator.  No kernel
+is launched."""
+import numpy as np
+import pytest
+
+from hpc_linear_algebra_amd import layout
+from hpc_linear_algebra_amd import tlrgemm as T
+from oracle import reference
+from tlr_inputs import on_grid, random_tlr
+
+
+def _shape(n, b, R, diag=True):
+    return T.Shape(n, n, b, np.asarray(R, dtype=np.int32), diag)
+
+
+def _ranks(q, r):
+    R = np.full((q, q), r, dtype=np.int32)
+    np.fill_diagonal(R, 0)
+    return R
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_sixteen_bit_plans_validate(dt):
+    s = _shape(256, 64, _ranks(4, 16))
+    for flags in (T.TLR_PLAN_FORCE_RIGHT, T.TLR_PLAN_FORCE_LEFT, T.TLR_PLAN_PER_K):
+        p = T.tlr_gemm_analyze(dt, "N", s, "T", s, ldc=256, flags=flags | T.TLR_PLAN_VALIDATE)
+        info = T.tlr_plan_info(p)
+        assert info["dtype"] == T._dt(dt)
+        assert info["workspace_bytes"] % 256 == 0
+    # a dense operand, and a small budget (several rectangles)
+    T.tlr_gemm_analyze(dt, "N", s, "N", None, 256, 40, 256, 256, flags=T.TLR_PLAN_VALIDATE)
+    T.tlr_gemm_analyze(dt, "N", None, "N", s, 40, 256, 40, 40, flags=T.TLR_PLAN_VALIDATE)
+    T.tlr_gemm_analyze(dt, "N", s, "N", s, ldc=264, workspace_budget=1 << 16, flags=T.TLR_PLAN_VALIDATE)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_sixteen_bit_rules(dt):
+    ok = _shape(256, 64, _ranks(4, 16))
+    cases = [
+        (dict(A=_shape(256, 64, _ranks(4, 12))), T.TLR_ERR_RANK),        # rank not a multiple of 8
+        (dict(A=_shape(260, 65, _ranks(4, 16))), T.TLR_ERR_INVALID_ARG),  # dimensions / tile size
+        (dict(ldc=257), T.TLR_ERR_INVALID_ARG),                           # ldc
+    ]
+    for kw, status in cases:
+        A = kw.get("A", ok)
+        B = ok if A.c.rows == 256 else A
+        with pytest.raises(T.TLRError) as e:
+            T.tlr_gemm_analyze(dt, "N", A, "N", B, ldc=kw.get("ldc", A.c.rows))
+        assert e.value.status == status, T.tlr_last_error()
+    with pytest.raises(T.TLRError) as e:     # tile size not a multiple of 8 (dimensions are)
+        s = _shape(240, 60, _ranks(4, 8))
+        T.tlr_gemm_analyze(dt, "N", s, "N", s, ldc=240)
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    with pytest.raises(T.TLRError) as e:     # dense operand with 36 columns
+        T.tlr_gemm_analyze(dt, "N", ok, "N", None, 256, 36, 256, 256)
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    with pytest.raises(T.TLRError) as e:     # dense GEMM entry: 32/64-bit only
+        T.tlr_dense_gemm(dt, "N", "N", 8, 8, 8, 1.0, 0, 8, 0, 8, 0.0, 0, 8)
+    assert e.value.status == T.TLR_ERR_UNSUPPORTED
+
+
+def test_round_ranks_keeps_the_matrix():
+    rng = np.random.default_rng(3)
+    t = random_tlr(rng, 200, 200, 40, 1, 30, dtype="f16")
+    p = layout.round_ranks(t, 8)
+    assert np.all(p.ranks % 8 == 0) and np.all(p.ranks >= t.ranks) and np.all(p.ranks - t.ranks < 8)
+    assert np.array_equal(reference.reconstruct(p), reference.reconstruct(t))
+    with pytest.raises(ValueError):          # a 4-row tile cannot hold rank 8
+        layout.round_ranks(random_tlr(rng, 12, 12, 4, 1, 3), 8)
+
+
+def test_half_grid_is_numpy_half():
+    x = np.random.default_rng(1).standard_normal(10000) * 3
+    g = on_grid(x, "f16")
+    assert np.array_equal(g, x.astype(np.float32).astype(np.float16).astype(np.float32))
+
+
+def test_bfloat16_grid():
+    x = np.random.default_rng(2).standard_normal(20000) * 5
+    g = on_grid(x, "bf16")
+    bits = g.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)                       # upper 16 bits of a float32 only
+    f = x.astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(g - f) <= np.abs(f) * 2.0 ** -8)   # nearest: at most half a unit in the last place
+    # ties go to the even neighbour: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert on_grid(np.array([1 + 2.0 ** -8]), "bf16")[0] == 1.0
+    assert on_grid(np.array([1 + 3 * 2.0 ** -8]), "bf16")[0] == 1 + 2.0 ** -6

@@ -5,7 +5,7 @@ none of the product's arithmetic, so both the CPU oracle and the GPU path may
 import it.
 """
 from .gen import (TLRTiles, CONFIGS, config_inputs, config_ranks, random_tlr,
-                  tile_sizes, ranks_from_fn)
+                  tile_sizes, ranks_from_fn, on_grid)
 
 __all__ = ["TLRTiles", "CONFIGS", "config_inputs", "config_ranks", "random_tlr",
-           "tile_sizes", "ranks_from_fn"]
+           "tile_sizes", "ranks_from_fn", "on_grid"]

@@ -39,7 +39,8 @@ class TLRTiles:
     (row_sizes[i], r) and ``V[(i, j)]`` shape (col_sizes[j], r), so the tile
     equals U @ V.T.  ``diag[i]`` holds the dense tile (i, i) when the operand
     has a dense diagonal; ranks[i, i] is then 0.  Values are float64 or
-    float32 numpy arrays (``dtype`` 'f64' / 'f32').
+    float32 numpy arrays (``dtype`` 'f64' / 'f32'; for 'f16' / 'bf16' float32
+    arrays whose values are on the 16-bit type's grid).
     """
     rows: int
     cols: int
@@ -72,7 +73,27 @@ class TLRTiles:
 
 
 def _np_dtype(dtype: str):
-    return {"f64": np.float64, "f32": np.float32}[dtype]
+    """Host array type of an element type: 16-bit values are held in float32
+    arrays (numpy has no bfloat16), each value on the 16-bit type's grid."""
+    return {"f64": np.float64, "f32": np.float32, "f16": np.float32, "bf16": np.float32}[dtype]
+
+
+def on_grid(x: np.ndarray, dtype: str) -> np.ndarray:
+    """x in the host array type of ``dtype``, rounded to nearest-even onto that
+    type's values (for 16-bit types: half, or bfloat16 = the upper 16 bits of a
+    float32).  Input preparation only: drawn values become representable."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    f = np.asarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return f
+    if dtype == "f16":
+        return f.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = f.view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+        return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+    raise ValueError(dtype)
 
 
 def ranks_from_fn(qr: int, qc: int, fn: Callable[[int, int], int],
@@ -113,11 +134,10 @@ def fill_values(rng: np.random.Generator, rows: int, cols: int, b: int,
                 v = v * w
             U[(i, j)] = u
             V[(i, j)] = v
-    npd = _np_dtype(dtype)
     if dtype != "f64":
-        diag = None if diag is None else [d.astype(npd) for d in diag]
-        U = {k: x.astype(npd) for k, x in U.items()}
-        V = {k: x.astype(npd) for k, x in V.items()}
+        diag = None if diag is None else [on_grid(d, dtype) for d in diag]
+        U = {k: on_grid(x, dtype) for k, x in U.items()}
+        V = {k: on_grid(x, dtype) for k, x in V.items()}
     return TLRTiles(rows, cols, b, ranks.astype(np.int32), diag, U, V, dtype)
 
 
@@ -201,20 +221,22 @@ def config_ranks(c: int, stream: int) -> np.ndarray:
     raise KeyError(c)
 
 
-def config_inputs(c: int, with_c: bool = True):
+def config_inputs(c: int, with_c: bool = True, dtype: Optional[str] = None):
     """(A, B, C_in) of workload c.  B is a TLRTiles or, for the TLR x dense
     workload, a dense (N, N) array; C_in is None when beta == 0 (or when
-    ``with_c`` is False).  Dense arrays are indexed [row, col]."""
+    ``with_c`` is False).  Dense arrays are indexed [row, col].  ``dtype``
+    replaces the workload's element type (same draws, rounded to that type)."""
     cfg = CONFIGS[c]
-    N, b, dt = cfg["N"], cfg["b"], cfg["dtype"]
+    N, b = cfg["N"], cfg["b"]
+    dt = dtype or cfg["dtype"]
     RA = config_ranks(c, 0)
     A = fill_values(np.random.default_rng(1000 * c + 2), N, N, b, RA, True, dt, cfg["decay"])
     if cfg["kind"] == "tlr_dense":
-        B = np.random.default_rng(1000 * c + 3).standard_normal((N, N)).astype(_np_dtype(dt))
+        B = on_grid(np.random.default_rng(1000 * c + 3).standard_normal((N, N)), dt)
     else:
         RB = config_ranks(c, 1)
         B = fill_values(np.random.default_rng(1000 * c + 3), N, N, b, RB, True, dt, cfg["decay"])
     C = None
     if with_c and cfg["beta"] != 0.0:
-        C = np.random.default_rng(1000 * c + 4).standard_normal((N, N)).astype(_np_dtype(dt))
+        C = on_grid(np.random.default_rng(1000 * c + 4).standard_normal((N, N)), dt)
     return A, B, C
