@@ -26,37 +26,71 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"f64": 78.6, "f32": 157.3}      # MI355X dense MFMA TFLOP/s (datasheet)
+PEAK = {"f64": 78.6, "f32": 157.3, "f16": 2500.0, "bf16": 2500.0}   # MI355X dense MFMA TFLOP/s (datasheet)
+ES = {"f64": 8, "f32": 4, "f16": 2, "bf16": 2}
 HBM_PEAK_GBS = 8000.0
 METRIC = "TLR GEMM useful TFLOP/s + % of roofline, fp64 TLRxTLR->dense N=16384"
 DEFAULT_WORKLOAD = "3"
 
 
-def workload(name: str):
+def workload(name: str, dtype=None):
     """Inputs of a bench workload: "1".."5" are the seeded workloads of
     tlr_inputs.CONFIGS; "dense_tlr" is workload 2 with its operands swapped
-    (a dense 4096 x 4096 A times the TLR operand), the dense x TLR product."""
+    (a dense 4096 x 4096 A times the TLR operand), the dense x TLR product.
+    ``dtype`` replaces the element type (the same draws, rounded to it)."""
     from tlr_inputs import CONFIGS, config_inputs
     if name == "dense_tlr":
         cfg = dict(CONFIGS[2])
-        T_op, Bd, C = config_inputs(2)
+        T_op, Bd, C = config_inputs(2, dtype=dtype)
         cfg["name"] = "dense_tlr_f64_n4096_b256_NN"
-        return cfg, Bd, T_op, C
-    cfg = CONFIGS[int(name)]
-    A, B, C = config_inputs(int(name))
+        A, B = Bd, T_op
+    else:
+        cfg = dict(CONFIGS[int(name)])
+        A, B, C = config_inputs(int(name), dtype=dtype)
+    if dtype and dtype != cfg["dtype"]:
+        cfg["name"] = cfg["name"].replace("_" + cfg["dtype"] + "_", "_" + dtype + "_")
+        cfg["dtype"] = dtype
     return cfg, A, B, C
+
+
+def final_update_bytes(F3: float, N: int, b: int, es: int, beta: float) -> float:
+    """Algorithmic HBM bytes of a final-update launch over the whole N x N C
+    (square b x b tiles): C written once and read once when beta != 0, and the
+    two operand panels read once.  The launch's flops are F3 = 2 N b sum(rank
+    sums) in either association order, so the panels hold F3/(2b) (the N-long
+    side: the right products T or the left products Y) plus F3/(2N) (the
+    b-long side: U or Z) elements."""
+    return es * (N * N * (2.0 if beta != 0 else 1.0) + F3 / (2.0 * b) + F3 / (2.0 * N))
+
+
+def logical_flops(cfg, A, B, order: str) -> float:
+    """Useful flops of the product in the given order counted with the logical
+    ranks (16-bit operands store ranks rounded up to a multiple of 8; the
+    zero columns are storage, not work): the same analysis on a 32-bit plan of
+    the unrounded operands."""
+    import numpy as np
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from tlr_inputs import TLRTiles
+    shp = lambda t: None if not isinstance(t, TLRTiles) else T.Shape(t.rows, t.cols, t.b,
+                                                                      np.asarray(t.ranks, np.int32), t.has_diag)
+    dense = A if not isinstance(A, TLRTiles) else (B if not isinstance(B, TLRTiles) else None)
+    dr, dc = dense.shape if dense is not None else (0, 0)
+    flag = T.TLR_PLAN_FORCE_LEFT if order == "left" else T.TLR_PLAN_FORCE_RIGHT
+    p = T.tlr_gemm_analyze("f32", cfg["opA"], shp(A), cfg["opB"], shp(B), dr, dc, dr if dense is not None else 0,
+                           cfg["N"], flags=flag)
+    return T.tlr_plan_info(p)["useful_flops"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_hash(sixteen_bit: bool = False) -> str:
     from hpc_linear_algebra_amd.profiling import kernel_source_hash
-    return kernel_source_hash()
+    return kernel_source_hash(sixteen_bit)
 
 
-def traffic_from_profiles(stage: int, workload_name: str):
+def traffic_from_profiles(stage: int, workload_name: str, sixteen_bit: bool = False):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
     counter runs of this workload, if they were taken on the current kernel
     source."""
@@ -67,7 +101,7 @@ def traffic_from_profiles(stage: int, workload_name: str):
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("kernel_hash") != kernel_hash():
+    if d.get("kernel_hash") != kernel_hash(sixteen_bit):
         return None
     return d.get("bytes_per_launch")
 
@@ -137,6 +171,45 @@ def padded_copy(t, rmax: int):
     return p
 
 
+def dense_reference_16(cfg, A, B, dtype, value, stream):
+    """Same-chip dense reference of a 16-bit product: the N x N operands
+    rebuilt in float32 by the library's dense GEMM, rounded to the 16-bit
+    type, and multiplied by torch.matmul (hipBLASLt, 16-bit inputs, float
+    accumulation), which is the vendor's tuned 16-bit GEMM."""
+    import copy
+    import torch
+    from hpc_linear_algebra_amd.device import _TORCH, DeviceTLR, dense_to_device
+    from tlr_inputs import TLRTiles
+    N = cfg["N"]
+
+    def rebuilt(t):
+        if not isinstance(t, TLRTiles):
+            return dense_to_device(t, dtype=dtype)
+        t32 = copy.copy(t)
+        t32.dtype = "f32"
+        d = DeviceTLR(t32)
+        out = rebuild_dense_on_gpu(d, t32, "f32").to(_TORCH[dtype])
+        del d
+        return out
+    Ad, Bd = rebuilt(A), rebuilt(B)
+    torch.matmul(Ad, Bd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        Cw = torch.matmul(Ad, Bd)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / reps
+    dense_tf = 2.0 * N ** 3 / (dms * 1e-3) / 1e12
+    del Ad, Bd, Cw
+    torch.cuda.empty_cache()
+    return {"tflops": round(dense_tf, 3), "ms": round(dms, 3), "parity": round(value / dense_tf, 4),
+            "note": "useful TFLOP/s of the TLR product / TFLOP/s of torch.matmul (hipBLASLt) on the rebuilt "
+                    "N x N operands in the same 16-bit type"}
+
+
 def cpu_baseline(cfg, A, B, C_in, useful_flops, budget_s=15.0):
     """The CPU oracle, timed on a bounded sample of output tiles."""
     import numpy as np
@@ -179,6 +252,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="1..5: the seeded workloads (3, the N=16384 TLR x TLR product, is the metric's); "
                          "dense_tlr: workload 2 with the operands swapped")
+    ap.add_argument("--dtype", default=None, choices=["f64", "f32", "f16", "bf16"],
+                    help="element type in place of the workload's own (same draws, rounded to it)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -210,19 +285,20 @@ def main():
     import numpy as np
     import torch
     from hpc_linear_algebra_amd import tlrgemm as T
-    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_to_device
+    from hpc_linear_algebra_amd.device import _TORCH, DeviceTLR, TLRGemm, dense_to_device
     from tlr_inputs import TLRTiles
 
     torch.cuda.set_device(0)
     log(f"bench: generating workload {args.workload}")
-    cfg, A, B, C_in = workload(args.workload)
+    cfg, A, B, C_in = workload(args.workload, args.dtype)
     dtype, N = cfg["dtype"], cfg["N"]
+    sixteen = dtype in ("f16", "bf16")
     dense_a, dense_b = not isinstance(A, TLRTiles), not isinstance(B, TLRTiles)
-    dA = dense_to_device(A) if dense_a else DeviceTLR(A)
-    dB = dense_to_device(B) if dense_b else DeviceTLR(B)
+    dA = dense_to_device(A, dtype=dtype) if dense_a else DeviceTLR(A)
+    dB = dense_to_device(B, dtype=dtype) if dense_b else DeviceTLR(B)
     dense_shape = A.shape if dense_a else (B.shape if dense_b else None)
-    tdt = torch.float64 if dtype == "f64" else torch.float32
-    Cd = dense_to_device(C_in) if C_in is not None else torch.zeros((N, N), dtype=tdt, device="cuda")
+    tdt = _TORCH[dtype]
+    Cd = dense_to_device(C_in, dtype=dtype) if C_in is not None else torch.zeros((N, N), dtype=tdt, device="cuda")
     n_streams = 2 if args.pipeline else 1
     g = TLRGemm(dtype, cfg["opA"], None if dense_a else dA, cfg["opB"], None if dense_b else dB, ldc=N,
                 dense_shape=dense_shape, ldb=N if (dense_a or dense_b) else 0, budget=cfg["budget"] or 0,
@@ -252,7 +328,12 @@ def main():
     stage_ms, launch_ms, nexec = T.tlr_plan_profile_read(g.plan, info["launches"])
     T.tlr_plan_profile(g.plan, 0)
     assert nexec == args.steps
+    order = ",".join("left" if T.tlr_plan_rect(g.plan, r)["order"] == T.TLR_ORDER_LEFT else "right"
+                     for r in range(info["runs"]))
     F = info["useful_flops"]
+    F_stored = F
+    if sixteen and len(set(order.split(","))) == 1:
+        F = logical_flops(cfg, A, B, order.split(",")[0])
     value = F / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.3f} ms/step, {value:.2f} useful TFLOP/s (wall {wall*1e3/args.steps:.3f} ms/step)")
 
@@ -262,18 +343,30 @@ def main():
     L = launches[dom]
     achieved = L["useful_flops"] / (per_launch[dom] * 1e-3) / 1e12
     peak = PEAK[dtype]
-    es = 8 if dtype == "f64" else 4
+    es = ES[dtype]
     alg_bytes = info["algorithmic_bytes"] + (N * N * es if cfg["beta"] != 0 else 0)
     ai = F / alg_bytes
     roof = min(peak, HBM_PEAK_GBS * 1e9 * ai / 1e12)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"]),
-                "kernel": f"stage {L['stage']} launch (final update, segmented-K)" if L["stage"] == 3
-                else f"stage {L['stage']} launch",
-                "launch_ms": round(per_launch[dom], 4)}
+    kname = (f"stage {L['stage']} launch (final update, segmented-K)" if L["stage"] == 3
+             else f"stage {L['stage']} launch")
+    lbytes = final_update_bytes(L["useful_flops"], N, cfg["b"], es, cfg["beta"]) if L["stage"] == 3 else None
+    if lbytes is not None and lbytes / (HBM_PEAK_GBS * 1e9) > L["useful_flops"] / (peak * 1e12):
+        # the launch's bytes take longer at 8 TB/s than its flops at the MFMA peak
+        gbs = lbytes / (per_launch[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"], sixteen),
+                    "kernel": kname, "launch_ms": round(per_launch[dom], 4), "algorithmic_bytes": lbytes,
+                    "mfma_tflops": round(achieved, 3)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"], sixteen),
+                    "kernel": kname, "launch_ms": round(per_launch[dom], 4)}
 
     dense = None
-    if not args.no_dense:
+    if not args.no_dense and sixteen:
+        log("bench: dense reference (rebuilt operands, torch.matmul = hipBLASLt 16-bit GEMM)")
+        dense = dense_reference_16(cfg, A, B, dtype, value, stream)
+    elif not args.no_dense:
         log("bench: dense reference (rebuilt operands, same MFMA kernel)")
         Ad = dA if dense_a else rebuild_dense_on_gpu(dA, A, dtype)
         Bd = dB if dense_b else rebuild_dense_on_gpu(dB, B, dtype)
@@ -336,15 +429,14 @@ def main():
         log("bench: CPU oracle baseline on a bounded sample")
         cpu = cpu_baseline(cfg, A, B, C_in, F, args.cpu_seconds)
 
-    order = ",".join("left" if T.tlr_plan_rect(g.plan, r)["order"] == T.TLR_ORDER_LEFT else "right"
-                     for r in range(info["runs"]))
     out = {
-        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD and dtype == "f64" else
         f"TLR GEMM useful TFLOP/s + % of roofline, {cfg['name']}", "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": cfg["name"], "N": N, "b": cfg["b"], "opA": cfg["opA"], "opB": cfg["opB"],
                    "alpha": cfg["alpha"], "beta": cfg["beta"], "useful_flops": F, "order": order,
+                   **({"stored_rank_flops": F_stored} if sixteen else {}),
                    "runs": info["runs"], "streams": n_streams, "pipelined": bool(args.pipeline),
                    "workspace_GiB": round(info["workspace_bytes"] / 2 ** 30, 3)},
         "roofline": roofline,

@@ -25,7 +25,11 @@
 // Work split: four wave64s in a 2 x 2 grid, each owning a 64 x BN/2 strip of
 // the block as 4 x (BN/32) MFMA tiles of 16 x 16.  LDS holds two stages; the
 // global loads of stage s+1 are in flight while stage s's MFMAs run, and one
-// barrier per stage separates the LDS stores from the next reads.
+// barrier per stage separates the LDS stores from the next reads.  (Measured
+// on the final update: MFMA time is hidden entirely; the LDS traffic of the
+// fragment reads and transposed stores and the per-stage barrier set the
+// pace.  Loading two stages ahead, or reading fragments one k-step ahead with
+// the barrier between the k-steps, measured slower.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,8 +98,10 @@ __device__ __forceinline__ void transpose8(const u4 (&x)[8], u4 (&y)[8]) {
 // One operand tile of a stage as seen by one loading thread: unit (rg, kg) =
 // rows 8rg .. 8rg+7 (of the A tile, or columns of the B tile) and k
 // 8kg .. 8kg+7.  With kc (K-contiguous) vector e is row 8rg+e at k 8kg;
-// otherwise it is k 8kg+e at rows 8rg .. 8rg+7.  The uniform part e*ld of the
-// address goes into the instruction's scalar offset.
+// otherwise it is k 8kg+e at rows 8rg .. 8rg+7.  Vector e sits e*ld elements
+// past vector 0; that step goes into the lane's offset (given to the scalar
+// offset instead, the compiler held it in vector registers inside the K loop
+// and wrapped every load in a loop over distinct lane values).
 struct Unit {
   const uint16_t *base;   // operand at (row 0 of the block, k 0)
   int64_t kstep;          // elements per stage along k
@@ -113,7 +119,7 @@ __device__ __forceinline__ void load_unit(const Unit &u, int st, int krem, u4 (&
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const bool ok = cok && u.s0 + e < s_lim;
-    x[e] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? u.lane : OOB16, e * u.ldb, 0));
+    x[e] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? u.lane + e * u.ldb : OOB16, 0, 0));
   }
 }
 
@@ -182,7 +188,7 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
   const bool loads_a = wave < 2;
   const int uidx = loads_a ? tid : tid - 128;
   const int kg = uidx & 7, rg = uidx >> 3;
-  const bool has_unit = loads_a || rg < BN / 8;
+  const bool has_unit = loads_a || (wave - 2) * 64 < BN;   // whole waves: uniform
 
   for (int sidx = 0; sidx < t.nseg; ++sidx) {
     const DevSeg &d = t.seg[sidx];

@@ -23,6 +23,11 @@ def _short(name: str) -> str:
     m = re.search(r"(grouped_gemm_kernel<[^>]*>|single_gemm_kernel<[^>]*>|scale_kernel<[^>]*>)", name)
     if m:
         return m.group(1)
+    m = re.search(r"(grouped_gemm16_kernel|scale16_kernel)I(DF16b|DF16_)((?:Li\d+E)*)", name)
+    if m:
+        t = "bfloat16" if m.group(2) == "DF16b" else "half"
+        args = re.findall(r"Li(\d+)E", m.group(3))
+        return f"{m.group(1)}<{', '.join([t] + args)}>"
     m = re.search(r"(grouped_gemm_kernel|single_gemm_kernel|scale_kernel)I([df])((?:Li\d+E)*)", name)
     if m:
         t = "double" if m.group(2) == "d" else "float"
@@ -102,11 +107,14 @@ def _counter_means(d: str):
     return vals
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sixteen_bit: bool = False) -> str:
+    """Hash of the kernel sources of one family (32/64-bit: gemm.hip; 16-bit:
+    gemm16.hip), so that stored counter results of a changed kernel are not
+    reused."""
     import hashlib
     h = hashlib.sha256()
     here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-    for f in ("gemm.hip", "tlr_desc.h"):
+    for f in ("gemm16.hip" if sixteen_bit else "gemm.hip", "tlr_desc.h"):
         h.update(open(os.path.join(here, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -128,7 +136,7 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, kernel_regex, copy_byt
     wr = kw * 1024.0 * wscale
     return {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
             "fetch_kib_raw": kf, "write_kib_raw": kw, "fetch_scale": fscale, "write_scale": wscale,
-            "kernel_regex": kernel_regex, "kernel_hash": kernel_source_hash()}
+            "kernel_regex": kernel_regex, "kernel_hash": kernel_source_hash("gemm16" in kernel_regex)}
 
 
 def main(argv=None):
