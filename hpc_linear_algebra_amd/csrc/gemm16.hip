@@ -14,22 +14,25 @@
 //
 // The 16-bit matrix cores take, per lane, 8 consecutive k of one row of A and
 // of one column of B.  Both operands therefore pass through LDS stored
-// K-contiguous: [row][k] for A, [column][k] for B, rows of 64 k padded to 72
-// elements (144 bytes: consecutive rows start four banks apart).  A stage
-// (64 k) is cut into 8 x 8 units, one per thread (threads 0..127: the A tile,
-// 128..255: the B tile); a thread loads its unit as eight 16-byte vectors.  An
-// operand that is K-contiguous in memory gives eight row pieces that go to LDS
-// as they are; an M- (or N-) contiguous one gives eight k-columns of 8 rows,
-// transposed in registers (v_perm_b32) before the eight 16-byte LDS stores.
+// K-contiguous: [row][k] for A, [column][k] for B, rows of 32 k padded to 40
+// elements (80 bytes: 8 consecutive rows start on 8 different 16-byte bank
+// groups).  A stage (32 k) is cut into 8 x 8 units, one per thread (wave 0:
+// the A tile, wave 1: the B tile); a thread loads its unit as eight 16-byte
+// vectors.  An operand that is K-contiguous in memory gives eight row pieces
+// that go to LDS as they are; an M- (or N-) contiguous one gives eight
+// k-columns of 8 rows, transposed in registers (v_perm_b32) before the eight
+// 16-byte LDS stores.
 //
 // Work split: four wave64s in a 2 x 2 grid, each owning a 64 x BN/2 strip of
 // the block as 4 x (BN/32) MFMA tiles of 16 x 16.  LDS holds two stages; the
 // global loads of stage s+1 are in flight while stage s's MFMAs run, and one
-// barrier per stage separates the LDS stores from the next reads.  (Measured
-// on the final update: MFMA time is hidden entirely; the LDS traffic of the
-// fragment reads and transposed stores and the per-stage barrier set the
-// pace.  Loading two stages ahead, or reading fragments one k-step ahead with
-// the barrier between the k-steps, measured slower.)
+// barrier per stage separates the LDS stores from the next reads.  Short
+// stages keep LDS at 40 KB and registers at 164 per lane, so three
+// workgroups share a CU and overlap each other's barrier-separated phases.
+// (Measured on the final update: MFMA time is hidden entirely; LDS traffic
+// and the per-stage barriers set the pace.  Stages of 64 k with two
+// workgroups per CU were 13% slower; loading two stages ahead, or reading
+// fragments a k-step ahead, slower still.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,8 +45,8 @@ namespace tlr {
 namespace {
 
 constexpr int BM16 = 128;        // block rows
-constexpr int KS = 64;           // k per stage
-constexpr int LROW = 72;         // LDS row stride in elements (64 k + 8)
+constexpr int KS = 32;           // k per stage
+constexpr int LROW = 40;         // LDS row stride in elements (32 k + 8)
 constexpr int NT16 = 256;        // four wave64s
 
 template <int NJ> struct Blk16 {
@@ -184,11 +187,13 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
     }
   }
 
-  // loading role: threads 0..127 the A tile (16 x 8 units), 128..255 the B tile
-  const bool loads_a = wave < 2;
-  const int uidx = loads_a ? tid : tid - 128;
-  const int kg = uidx & 7, rg = uidx >> 3;
-  const bool has_unit = loads_a || (wave - 2) * 64 < BN;   // whole waves: uniform
+  // loading role: wave 0 the A tile (16 x 4 units), wave 1 the B tile (BN/8 x
+  // 4 units: all of wave 1, or its first half for BN = 64); waves 2 and 3
+  // only compute
+  const bool loads_a = wave == 0;
+  const int uidx = loads_a ? tid : tid - 64;
+  const int kg = uidx & 3, rg = uidx >> 2;
+  const bool has_unit = loads_a || (wave == 1 && uidx < BN / 2);
 
   for (int sidx = 0; sidx < t.nseg; ++sidx) {
     const DevSeg &d = t.seg[sidx];
@@ -225,24 +230,20 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
     for (int st = 0; st < nst; ++st) {
       const bool more = st + 1 < nst;
       if (more && has_unit) load_unit(u, st + 1, K - (st + 1) * KS, x);
+      // one MFMA k-step of 32 per stage
       const uint16_t *a_t = As[st & 1];
       const uint16_t *b_t = Bs[st & 1];
-      const int krem = K - st * KS;
+      u4 af[4], bf[NJ];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 1 && krem <= 32) break;   // every k of the second step is past K
-        u4 af[4], bf[NJ];
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const u4 *>(a_t + (64 * wm + 16 * i + r) * LROW + 8 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const u4 *>(a_t + (64 * wm + 16 * i + r) * LROW + 32 * ks + 8 * g);
+      for (int j = 0; j < NJ; ++j)
+        bf[j] = *reinterpret_cast<const u4 *>(b_t + (wn * 16 * NJ + 16 * j + r) * LROW + 8 * g);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          bf[j] = *reinterpret_cast<const u4 *>(b_t + (wn * 16 * NJ + 16 * j + r) * LROW + 32 * ks + 8 * g);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
-      }
+        for (int j = 0; j < NJ; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
       if (more && has_unit) {
         if (loads_a) store_unit<true>(As[(st + 1) & 1], rg, kg, u.kc, x);
         else store_unit<false>(Bs[(st + 1) & 1], rg, kg, u.kc, x);
@@ -284,7 +285,7 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
 }
 
 template <typename H, int STAGE, int NJ>
-__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(3)))
 void grouped_gemm16_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
                            const int64_t *__restrict__ coltab, Bases bases, float alpha, float beta, float cscale) {
   const DevTile e = tiles[blockIdx.x];
