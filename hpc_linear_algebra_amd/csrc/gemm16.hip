@@ -16,23 +16,24 @@
 // of one column of B.  Both operands therefore pass through LDS stored
 // K-contiguous: [row][k] for A, [column][k] for B, rows of 32 k padded to 40
 // elements (80 bytes: 8 consecutive rows start on 8 different 16-byte bank
-// groups).  A stage (32 k) is cut into 8 x 8 units, one per thread (wave 0:
-// the A tile, wave 1: the B tile); a thread loads its unit as eight 16-byte
-// vectors.  An operand that is K-contiguous in memory gives eight row pieces
-// that go to LDS as they are; an M- (or N-) contiguous one gives eight
-// k-columns of 8 rows, transposed in registers (v_perm_b32) before the eight
-// 16-byte LDS stores.
+// groups).  A stage (32 k) is cut into units of four 16-byte vectors, one per
+// thread (waves 0-1: the A tile, waves 2-3: the B tile).  An operand that is
+// K-contiguous in memory gives units of 4 rows x 8 k whose row pieces go to
+// LDS as they are; an M- (or N-) contiguous one gives units of 8 rows x 4 k,
+// transposed in registers (v_perm_b32) into eight 8-byte LDS stores.
 //
 // Work split: four wave64s in a 2 x 2 grid, each owning a 64 x BN/2 strip of
 // the block as 4 x (BN/32) MFMA tiles of 16 x 16.  LDS holds two stages; the
 // global loads of stage s+1 are in flight while stage s's MFMAs run, and one
 // barrier per stage separates the LDS stores from the next reads.  Short
-// stages keep LDS at 40 KB and registers at 164 per lane, so three
-// workgroups share a CU and overlap each other's barrier-separated phases.
-// (Measured on the final update: MFMA time is hidden entirely; LDS traffic
-// and the per-stage barriers set the pace.  Stages of 64 k with two
-// workgroups per CU were 13% slower; loading two stages ahead, or reading
-// fragments a k-step ahead, slower still.)
+// stages and small units keep LDS at 40 KB and registers at 128 per lane, so
+// four workgroups share a CU and overlap each other's barrier-separated
+// phases (the lane's output column offsets go to scratch around the K loop).
+// Measured on the final update: MFMA time is hidden entirely; LDS traffic and
+// the per-stage barriers set the pace.  Against this form, two loading waves
+// with 8-vector units (three workgroups per CU) were 12% slower, stages of
+// 64 k (two workgroups per CU) 30% slower, and loading two stages ahead or
+// reading fragments a k-step ahead slower still.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,25 +87,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc16(const void *p) {
 // In bits: m = [w h | g g | p | v v] sits at LDS row [w h | p | g g | v v].
 __device__ __forceinline__ int a_lds_row(int m) { return (m & ~0x1C) | ((m & 0x4) << 2) | ((m & 0x18) >> 1); }
 
-// 8 x 8 transpose of 16-bit elements: x[e] holds (s = e, c = 0..7); y[c]
-// holds (s = 0..7, c).  Dword w of a vector holds elements 2w (low half) and
-// 2w+1 (high half).
-__device__ __forceinline__ void transpose8(const u4 (&x)[8], u4 (&y)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low halves of (lo, hi)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) y[c][w] = __builtin_amdgcn_perm(x[2 * w + 1][c >> 1], x[2 * w][c >> 1], sel);
-  }
-}
-
-// One operand tile of a stage as seen by one loading thread: unit (rg, kg) =
-// rows 8rg .. 8rg+7 (of the A tile, or columns of the B tile) and k
-// 8kg .. 8kg+7.  With kc (K-contiguous) vector e is row 8rg+e at k 8kg;
-// otherwise it is k 8kg+e at rows 8rg .. 8rg+7.  Vector e sits e*ld elements
-// past vector 0; that step goes into the lane's offset (given to the scalar
-// offset instead, the compiler held it in vector registers inside the K loop
-// and wrapped every load in a loop over distinct lane values).
+// One operand tile of a stage as seen by one loading thread (rows of the A
+// tile, or columns of the B tile).  With kc (K-contiguous) vector e is row
+// s0+e at k c0 .. c0+7; otherwise it is k s0+e at rows c0 .. c0+7.  Vector e
+// sits e*ld elements past vector 0; that step goes into the lane's offset
+// (given to the scalar offset instead, the compiler held it in vector
+// registers inside the K loop and wrapped every load in a loop over distinct
+// lane values).
 struct Unit {
   const uint16_t *base;   // operand at (row 0 of the block, k 0)
   int64_t kstep;          // elements per stage along k
@@ -114,27 +103,44 @@ struct Unit {
   bool kc;
 };
 
-__device__ __forceinline__ void load_unit(const Unit &u, int st, int krem, u4 (&x)[8]) {
+__device__ __forceinline__ void load_unit(const Unit &u, int st, int krem, u4 (&x)[4]) {
   const __amdgpu_buffer_rsrc_t rs = rsrc16(u.base + (int64_t)st * u.kstep);
   // k limit of this stage: contiguous index for kc, strided otherwise
   const int s_lim = u.kc ? u.s_lim : krem, c_lim = u.kc ? krem : u.c_lim;
   const bool cok = u.c0 < c_lim;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 4; ++e) {
     const bool ok = cok && u.s0 + e < s_lim;
     x[e] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? u.lane + e * u.ldb : OOB16, 0, 0));
   }
 }
 
-// LDS stores of a unit: row (of the tile) 8rg + e gets k 8kg .. 8kg+7.
+// LDS stores of a unit.  K-contiguous (kc): vector e is row 4a+e at k
+// 8b..8b+7, stored as it is.  Otherwise vector e is k 4b+e at rows
+// 8a..8a+7; transposed, row 8a+c gets k 4b..4b+3 (8 bytes).
 template <bool IS_A>
-__device__ __forceinline__ void store_unit(uint16_t *tile, int rg, int kg, bool kc, const u4 (&x)[8]) {
-  u4 y[8];
-  if (!kc) transpose8(x, y);
+__device__ __forceinline__ void store_unit(uint16_t *tile, int a, int b, bool kc, const u4 (&x)[4]) {
+  if (kc) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = IS_A ? a_lds_row(8 * rg + e) : 8 * rg + e;
-    *reinterpret_cast<u4 *>(tile + row * LROW + 8 * kg) = kc ? x[e] : y[e];
+    for (int e = 0; e < 4; ++e) {
+      const int row = IS_A ? a_lds_row(4 * a + e) : 4 * a + e;
+      *reinterpret_cast<u4 *>(tile + row * LROW + 8 * b) = x[e];
+    }
+  } else {
+    // dword w of a vector holds elements 2w (low half) and 2w+1 (high half);
+    // v_perm_b32 takes bytes 0-3 from its second source and 4-7 from its
+    // first: selector 0x05040100 packs the two low halves, 0x07060302 the
+    // two high halves
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u2 y;
+      y[0] = __builtin_amdgcn_perm(x[1][c >> 1], x[0][c >> 1], sel);
+      y[1] = __builtin_amdgcn_perm(x[3][c >> 1], x[2][c >> 1], sel);
+      const int row = IS_A ? a_lds_row(8 * a + c) : 8 * a + c;
+      *reinterpret_cast<u2 *>(tile + row * LROW + 4 * b) = y;
+    }
   }
 }
 
@@ -187,13 +193,11 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
     }
   }
 
-  // loading role: wave 0 the A tile (16 x 4 units), wave 1 the B tile (BN/8 x
-  // 4 units: all of wave 1, or its first half for BN = 64); waves 2 and 3
-  // only compute
-  const bool loads_a = wave == 0;
-  const int uidx = loads_a ? tid : tid - 64;
-  const int kg = uidx & 3, rg = uidx >> 2;
-  const bool has_unit = loads_a || (wave == 1 && uidx < BN / 2);
+  // loading role: waves 0-1 the A tile (128 units), waves 2-3 the B tile (BN
+  // units: both waves, or wave 2 alone for BN = 64)
+  const bool loads_a = wave < 2;
+  const int uidx = loads_a ? tid : tid - 128;
+  const bool has_unit = loads_a || (wave - 2) * 64 < BN;
 
   for (int sidx = 0; sidx < t.nseg; ++sidx) {
     const DevSeg &d = t.seg[sidx];
@@ -213,18 +217,20 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
       u.base = u.kc ? p + (int64_t)first * ld : p + first;
       u.kstep = u.kc ? KS : (int64_t)KS * ld;
       u.ldb = (uint32_t)(ld * 2);
-      const int srow = u.kc ? 8 * rg : 8 * kg, ccol = u.kc ? 8 * kg : 8 * rg;
+      // kc: rows 4rq.. (rq = uidx/4) at k chunk uidx%4; else k 4kq.. (kq = uidx%8) at rows 8rg.. (rg = uidx/8)
+      const int srow = u.kc ? 4 * (uidx >> 2) : 4 * (uidx & 7), ccol = u.kc ? 8 * (uidx & 3) : 8 * (uidx >> 3);
       u.lane = (uint32_t)((int64_t)srow * ld + ccol) * 2u;
       u.s0 = srow;
       u.c0 = ccol;
       u.s_lim = u.kc ? rem : 0;   // the k limit is filled in per stage
       u.c_lim = u.kc ? 0 : rem;
     }
-    u4 x[8];
+    u4 x[4];
+    const int ua = u.kc ? uidx >> 2 : uidx >> 3, ub = u.kc ? uidx & 3 : uidx & 7;
     if (has_unit) {
       load_unit(u, 0, K, x);
-      if (loads_a) store_unit<true>(As[0], rg, kg, u.kc, x);
-      else store_unit<false>(Bs[0], rg, kg, u.kc, x);
+      if (loads_a) store_unit<true>(As[0], ua, ub, u.kc, x);
+      else store_unit<false>(Bs[0], ua, ub, u.kc, x);
     }
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
@@ -245,8 +251,8 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
       if (more && has_unit) {
-        if (loads_a) store_unit<true>(As[(st + 1) & 1], rg, kg, u.kc, x);
-        else store_unit<false>(Bs[(st + 1) & 1], rg, kg, u.kc, x);
+        if (loads_a) store_unit<true>(As[(st + 1) & 1], ua, ub, u.kc, x);
+        else store_unit<false>(Bs[(st + 1) & 1], ua, ub, u.kc, x);
       }
       __syncthreads();
     }
@@ -285,7 +291,7 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
 }
 
 template <typename H, int STAGE, int NJ>
-__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(4)))
 void grouped_gemm16_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
                            const int64_t *__restrict__ coltab, Bases bases, float alpha, float beta, float cscale) {
   const DevTile e = tiles[blockIdx.x];
