@@ -254,6 +254,8 @@ def main():
                          "dense_tlr: workload 2 with the operands swapped")
     ap.add_argument("--dtype", default=None, choices=["f64", "f32", "f16", "bf16"],
                     help="element type in place of the workload's own (same draws, rounded to it)")
+    ap.add_argument("--order", default="auto", choices=["auto", "left", "right"],
+                    help="association order of every rectangle (auto: the planner's choice, fewer useful flops)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -300,9 +302,11 @@ def main():
     tdt = _TORCH[dtype]
     Cd = dense_to_device(C_in, dtype=dtype) if C_in is not None else torch.zeros((N, N), dtype=tdt, device="cuda")
     n_streams = 2 if args.pipeline else 1
+    flags = (T.TLR_PLAN_PIPELINE if args.pipeline else 0) | \
+        {"auto": 0, "left": T.TLR_PLAN_FORCE_LEFT, "right": T.TLR_PLAN_FORCE_RIGHT}[args.order]
     g = TLRGemm(dtype, cfg["opA"], None if dense_a else dA, cfg["opB"], None if dense_b else dB, ldc=N,
                 dense_shape=dense_shape, ldb=N if (dense_a or dense_b) else 0, budget=cfg["budget"] or 0,
-                n_streams=n_streams, flags=T.TLR_PLAN_PIPELINE if args.pipeline else 0)
+                n_streams=n_streams, flags=flags)
     info = g.info
     launches = g.launches()
     stream = torch.cuda.current_stream()
