@@ -93,6 +93,15 @@ def test_budget_rectangles_pipelined(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_boundary_regions_on_streams(dtype):
+    # N = 520 with b = 128: a boundary tile of 8; regions on their own streams, beta = 1
+    A, B, C = _pair(37, 520, 128, dtype, lo=0, hi=48)
+    for flags in (0, F_RIGHT, F_LEFT):
+        say(f"{dtype} regions on 3 streams flags={flags}")
+        check_tlr(A, B, "T", "N", 1.25, 1.0, C, n_streams=3, flags=flags)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_per_contraction_tile_loop(dtype):
     A, B, C = _pair(29, 384, 64, dtype, lo=0, hi=40)
     say(f"{dtype} per-k loop")
