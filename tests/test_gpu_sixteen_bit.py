@@ -146,3 +146,23 @@ def test_n16384_b512_sampled(dtype):
     err = (num / den) ** 0.5
     say(f"{dtype} N={N}: sampled rel Frobenius error {err:.3e}")
     assert err <= TOL[dtype]
+
+
+def test_misaligned_buffer_is_refused():
+    """A 16-bit buffer off a 16-byte boundary is rejected on the host before
+    any launch (the kernel moves 16-byte vectors); C is left untouched."""
+    import torch
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_to_device
+    A, B, C = _pair(41, 128, 64, "f16")
+    dA, dB = DeviceTLR(A), DeviceTLR(B)
+    g = TLRGemm("f16", "N", dA, "N", dB, ldc=128)
+    Cd = dense_to_device(C, dtype="f16", ld=136)      # one spare column of slack for the shifted view
+    before = Cd.clone()
+    with pytest.raises(T.TLRError) as e:
+        T.tlr_gemm_execute(g.plan, 1.0, dA.buffers(), dB.buffers(), 0, 0, 1.0, Cd.data_ptr() + 2, 128,
+                           g.ws.data_ptr(), g.ws.numel(), [torch.cuda.current_stream().cuda_stream])
+    assert e.value.status == T.TLR_ERR_INVALID_ARG
+    assert "16-byte" in T.tlr_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(Cd, before)
