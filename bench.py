@@ -336,8 +336,15 @@ def main():
                      for r in range(info["runs"]))
     F = info["useful_flops"]
     F_stored = F
-    if sixteen and len(set(order.split(","))) == 1:
-        F = logical_flops(cfg, A, B, order.split(",")[0])
+    basis = "ranks"
+    if sixteen:
+        # with one order for every rectangle the logical-rank count is exact; with
+        # mixed orders the count stays on the stored (rounded-up) ranks
+        if len(set(order.split(","))) == 1:
+            F = logical_flops(cfg, A, B, order.split(",")[0])
+            basis = "logical ranks"
+        else:
+            basis = "stored ranks (rounded up to multiples of 8; the rectangles use different orders)"
     value = F / (ms * 1e-3) / 1e12
     log(f"bench: {ms:.3f} ms/step, {value:.2f} useful TFLOP/s (wall {wall*1e3/args.steps:.3f} ms/step)")
 
@@ -440,7 +447,7 @@ def main():
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": cfg["name"], "N": N, "b": cfg["b"], "opA": cfg["opA"], "opB": cfg["opB"],
                    "alpha": cfg["alpha"], "beta": cfg["beta"], "useful_flops": F, "order": order,
-                   **({"stored_rank_flops": F_stored} if sixteen else {}),
+                   **({"stored_rank_flops": F_stored, "useful_flops_basis": basis} if sixteen else {}),
                    "runs": info["runs"], "streams": n_streams, "pipelined": bool(args.pipeline),
                    "workspace_GiB": round(info["workspace_bytes"] / 2 ** 30, 3)},
         "roofline": roofline,
