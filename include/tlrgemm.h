@@ -259,7 +259,10 @@ tlr_status tlr_plan_bind(tlr_plan *p, void *dev_desc, size_t bytes, void *stream
  *               and joined back to streams[0] with events.
  * beta == 0 never reads C (NaN in C does not propagate); alpha == 0 only scales C.
  * Asynchronous: no host synchronisation.
- * Errors: TLR_ERR_NOT_BOUND, TLR_ERR_INVALID_ARG (NULL buffers, ld mismatch),
+ * 16-bit types: every buffer (factors, diagonals, dense operand, C, workspace)
+ * must be 16-byte aligned.
+ * Errors: TLR_ERR_NOT_BOUND, TLR_ERR_INVALID_ARG (NULL buffers, ld mismatch,
+ * a 16-bit buffer off a 16-byte boundary; nothing is launched),
  * TLR_ERR_WORKSPACE (workspace too small), TLR_ERR_HIP (launch failure).
  */
 tlr_status tlr_gemm_execute(tlr_plan *p, double alpha,
