@@ -1251,9 +1251,11 @@ static tlr_status build_per_k(Plan &p, const Sums &s) {
 static tlr_status check_16bit(const Plan &p) {
   auto m8 = [](int64_t x) { return x % 8 == 0; };
   const char *why = nullptr;
+  // (a leading dimension matters only when its matrix has elements)
   if (!m8(p.m) || !m8(p.n) || !m8(p.k)) why = "16-bit types: every matrix dimension must be a multiple of 8";
-  else if (!m8(p.ldc)) why = "16-bit types: ldc must be a multiple of 8";
-  else if ((p.dense_a || p.dense_b) && (!m8(p.ldb) || !m8(p.dense_rows) || !m8(p.dense_cols)))
+  else if (p.m > 0 && p.n > 0 && !m8(p.ldc)) why = "16-bit types: ldc must be a multiple of 8";
+  else if ((p.dense_a || p.dense_b) &&
+           (!m8(p.dense_rows) || !m8(p.dense_cols) || (p.dense_rows > 0 && p.dense_cols > 0 && !m8(p.ldb))))
     why = "16-bit types: the dense operand's dimensions and leading dimension must be multiples of 8";
   if (why) return fail(TLR_ERR_INVALID_ARG, why);
   for (const View *v : {&p.A, &p.B}) {

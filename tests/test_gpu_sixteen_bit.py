@@ -166,3 +166,17 @@ def test_misaligned_buffer_is_refused():
     assert "16-byte" in T.tlr_last_error()
     torch.cuda.synchronize()
     assert torch.equal(Cd, before)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_empty_single_tile_and_full_rank(dtype):
+    rng = np.random.default_rng(2)
+    E = random_tlr(rng, 0, 0, 8, has_diag=True, dtype=dtype)
+    assert run_tlr(E, E, "N", "N", 1.0, 0.0, None).shape == (0, 0)
+    A, B, C = _pair(18, 96, 128, dtype)                    # q = 1: one dense diagonal tile, a dense GEMM
+    say(f"{dtype} single tile")
+    check_tlr(A, B, "T", "N", 1.0, 0.5, C)
+    A, B, C = _pair(19, 128, 32, dtype, lo=32, hi=32)      # every off-diagonal tile at full rank 32
+    say(f"{dtype} full rank")
+    check_tlr(A, B, "N", "N", 1.0, 0.5, C, flags=F_LEFT)
+    check_tlr(A, B, "N", "T", 1.0, 0.5, C, flags=F_RIGHT)

@@ -58,6 +58,8 @@ def test_sixteen_bit_rules(dt):
     with pytest.raises(T.TLRError) as e:     # dense operand with 36 columns
         T.tlr_gemm_analyze(dt, "N", ok, "N", None, 256, 36, 256, 256)
     assert e.value.status == T.TLR_ERR_INVALID_ARG
+    e0 = _shape(0, 8, np.zeros((0, 0), np.int32))   # an empty product: no leading dimension is used
+    T.tlr_gemm_analyze(dt, "N", e0, "N", e0, ldc=1)
     with pytest.raises(T.TLRError) as e:     # dense GEMM entry: 32/64-bit only
         T.tlr_dense_gemm(dt, "N", "N", 8, 8, 8, 1.0, 0, 8, 0, 8, 0.0, 0, 8)
     assert e.value.status == T.TLR_ERR_UNSUPPORTED
