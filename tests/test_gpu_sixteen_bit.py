@@ -180,3 +180,16 @@ def test_empty_single_tile_and_full_rank(dtype):
     say(f"{dtype} full rank")
     check_tlr(A, B, "N", "N", 1.0, 0.5, C, flags=F_LEFT)
     check_tlr(A, B, "N", "T", 1.0, 0.5, C, flags=F_RIGHT)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_rectangular_operands(dtype):
+    rng = np.random.default_rng(43)
+    A = random_tlr(rng, 256, 384, 64, rank_lo=0, rank_hi=40, has_diag=False, dtype=dtype)
+    B = random_tlr(rng, 384, 200, 64, rank_lo=0, rank_hi=40, has_diag=False, dtype=dtype)
+    C = on_grid(rng.standard_normal((256, 200)), dtype)
+    for flags in (F_RIGHT, F_LEFT):
+        say(f"{dtype} rectangular 256x384 * 384x200 flags={flags}")
+        check_tlr(A, B, "N", "N", 0.5, 1.0, C, flags=flags)
+    At = random_tlr(rng, 384, 256, 64, rank_lo=0, rank_hi=40, has_diag=False, dtype=dtype)
+    check_tlr(At, B, "T", "N", 1.0, 0.0, None)
