@@ -47,7 +47,9 @@
  * rejects a misaligned buffer.  The products are accumulated in float; each
  * workspace intermediate (the coupling blocks, the right or left products)
  * and C are rounded to the 16-bit type once, when written, and alpha and beta
- * are applied in float.
+ * are applied in float.  In half precision those intermediates must stay
+ * within its range (|x| <= 65504; beyond it they become infinite); bfloat16
+ * has float's range.
  *
  * Ownership: every device buffer (factors, diagonals, dense B, C, workspace,
  * descriptor buffer) belongs to the caller.  The library never allocates
