@@ -398,10 +398,22 @@ def main():
         torch.cuda.synchronize()
         dms = e0.elapsed_time(e1) / reps
         dense_tf = 2.0 * N ** 3 / (dms * 1e-3) / 1e12
+        # context only: the vendor's GEMM (torch.matmul, rocBLAS / hipBLASLt) on the same operands
+        torch.matmul(Ad, Bd)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            Vw = torch.matmul(Ad, Bd)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / reps
+        del Vw
         dense = {"tflops": round(dense_tf, 3), "ms": round(dms, 3),
                  "parity": round(value / dense_tf, 4),
+                 "vendor_tflops": round(2.0 * N ** 3 / (vms * 1e-3) / 1e12, 3),
                  "note": "useful TFLOP/s of the TLR product / TFLOP/s of the library's dense MFMA GEMM on the "
-                         "rebuilt N x N operands (dense time scaled by the executed-flop ratio)"}
+                         "rebuilt N x N operands (dense time scaled by the executed-flop ratio); vendor_tflops: "
+                         "torch.matmul on the same operands, for context"}
         if dense_a:
             Ad = None
         if dense_b:
