@@ -193,3 +193,47 @@ def test_rectangular_operands(dtype):
         check_tlr(A, B, "N", "N", 0.5, 1.0, C, flags=flags)
     At = random_tlr(rng, 384, 256, 64, rank_lo=0, rank_hi=40, has_diag=False, dtype=dtype)
     check_tlr(At, B, "T", "N", 1.0, 0.0, None)
+
+
+@pytest.mark.parametrize("c", [4, 5])
+def test_large_workloads_sampled_half(c):
+    """The N = 30000 (1 GiB budget) and N = 32768 (heavy ranks) workloads with
+    their values rounded to half precision, run as the benchmark runs them
+    (one stream), compared tile by tile on corner, boundary, diagonal and
+    off-diagonal tiles, and the tile of the heaviest rank."""
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_to_device
+    from tlr_inputs import CONFIGS, config_inputs, config_ranks, tile_sizes
+    cfg = CONFIGS[c]
+    N, b = cfg["N"], cfg["b"]
+    say(f"half workload {c}: generating")
+    A, B, C_in = config_inputs(c, dtype="f16")
+    dA, dB = DeviceTLR(A), DeviceTLR(B)
+    g = TLRGemm("f16", cfg["opA"], dA, cfg["opB"], dB, ldc=N, budget=cfg["budget"] or 0)
+    if C_in is None:
+        Cd = torch.full((N, N), float("nan"), dtype=torch.float16, device="cuda")
+    else:
+        Cd = dense_to_device(C_in, dtype="f16")
+    say(f"half workload {c}: runs={g.info['runs']}")
+    g(cfg["alpha"], dA, dB, cfg["beta"], Cd)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(Cd).all().item())
+    sz = tile_sizes(N, b)
+    off = reference.offsets(sz)
+    q = len(sz)
+    tiles = {(0, 0), (q - 1, q - 1), (0, q - 1), (q - 1, 0), (q // 2, q // 3)}
+    R = config_ranks(c, 0)
+    i, j = np.unravel_index(np.argmax(R), R.shape)
+    tiles.add((int(i), int(j)))
+    num = den = 0.0
+    for (i, j) in sorted(tiles):
+        r0, r1, c0, c1 = off[i], off[i] + sz[i], off[j], off[j] + sz[j]
+        got = Cd[c0:c1, r0:r1].float().cpu().numpy().T.astype(np.float64)
+        cin = None if C_in is None else C_in[r0:r1, c0:c1]
+        ref = reference.gemm_reference_block(cfg["alpha"], cfg["opA"], A, cfg["opB"], B, cfg["beta"], cin,
+                                             (r0, r1), (c0, c1))
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    err = (num / den) ** 0.5
+    say(f"half workload {c}: sampled rel Frobenius error {err:.3e}")
+    assert err <= TOL["f16"]
