@@ -335,6 +335,19 @@ __device__ __forceinline__ void run_segment(SegCtx<T> c, int tid, int arow, int 
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(fa[i][q], b[j], acc[i][j]);
+      if (MORE) {
+        // Interleave the next k-step's B fragment reads with this k-step's
+        // MFMAs: one LDS read, then MI MFMAs, from the start of the k-step.
+        // Left to itself the compiler issued the reads after all but the
+        // last MFMA, and the next k-step's first MFMAs waited for them;
+        // interleaved, the final update and the dense GEMM ran 2% faster.
+        // (sched_group_barrier masks: 0x100 LDS reads, 0x008 MFMAs.)
+#pragma unroll
+        for (int k = 0; k < NJ; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, MI, 0);
+        }
+      }
       if (MORE) load_a<T, MODE>(c, k1, q, fa);
       if (MORE && q == 1) {
         store_b<MODE, NJ>(bm, rb, Bs[nxt]);
