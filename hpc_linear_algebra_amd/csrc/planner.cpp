@@ -526,7 +526,7 @@ static double task_exec_flops(const DevTask &d) {
 // is a multiple of NUM_XCD entries and the XCD of an entry does not depend on
 // which sub-tables precede it.
 // Block width of a launch.  128 x 128 blocks move the fewest operand bytes per
-// flop; 128 x 64 blocks (half the accumulators, three workgroups per CU) spread
+// flop; 128 x 64 blocks (half the accumulators, four workgroups per CU) spread
 // a launch of few blocks over more CUs.  The final update stays wide; the
 // others go narrow when 128 x 128 blocks would give fewer than four workgroups
 // per CU (the coupling and diagonal-term GEMMs: few, with K = b).  Measured on
