@@ -530,7 +530,7 @@ static double task_exec_flops(const DevTask &d) {
 // a launch of few blocks over more CUs.  The final update stays wide; the
 // others go narrow when 128 x 128 blocks would give fewer than four workgroups
 // per CU (the coupling and diagonal-term GEMMs: few, with K = b).  Measured on
-// the store-bound right/left product, narrow blocks were slower.
+// the store-bound right/left product, narrow blocks were no faster.
 static int launch_bn(int stage, const TaskList &tl) {
   if (stage == 3) return BN;
   int64_t blocks = 0;
