@@ -609,9 +609,13 @@ static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &si
   const int b = emit_launch(p, 2, group, rect, l2);
   const int c = emit_launch(p, 3, group, rect, l3);
   if (d < 0) return;
-  // fork before the first launch of the group's stream that follows in this
-  // rectangle, or at the group's end when there is none
-  p.launches[d].fork_at = a >= 0 ? a : (b >= 0 ? b : c);
+  // fork before the coupling launch, so that the side launch runs beside
+  // stages 1 and 2.  Without a coupling launch the fork is the side launch's
+  // own position (fork_at -1): its event is then recorded on the group's
+  // stream after everything enqueued there so far and before the side stream
+  // waits on it.  A later launch (stage 2 or 3) would record the event only
+  // after the side stream's wait has been enqueued, which orders nothing.
+  p.launches[d].fork_at = a;
   if (c >= 0) p.launches[c].wait_launch = d;
 }
 
@@ -1032,6 +1036,39 @@ static tlr_status validate(const Plan &p, bool deep) {
   }
   for (size_t t = 0; t < p.tasks.size(); ++t)
     if (seen[t] != want[t]) return fail(TLR_ERR_INVALID_ARG, "internal: blocks of a task missing or repeated");
+  // stream order: the executor enqueues the groups one after another, each
+  // group's launches in list order.  An event must be recorded before a
+  // stream waits on it in the same execute, otherwise the wait sees the
+  // previous execute's record (or none) and orders nothing.  So a side
+  // launch's fork point (where its fork event is recorded on the group's
+  // stream) is in its own group at or before it, and a launch waits only for
+  // a launch enqueued earlier.
+  {
+    std::vector<int64_t> pos(p.launches.size(), -1);
+    std::vector<int> grp(p.launches.size(), -1);
+    int64_t at = 0;
+    for (size_t g = 0; g < p.groups.size(); ++g)
+      for (int l : p.groups[g].launches) {
+        if (l < 0 || l >= (int)p.launches.size() || pos[l] >= 0)
+          return fail(TLR_ERR_INVALID_ARG, "internal: launch lists of the groups malformed");
+        pos[l] = at++;
+        grp[l] = (int)g;
+      }
+    for (size_t l = 0; l < p.launches.size(); ++l) {
+      const Launch &L = p.launches[l];
+      if (pos[l] < 0) return fail(TLR_ERR_INVALID_ARG, "internal: launch in no group");
+      if (L.stage == STAGE_SIDE && L.fork_at >= 0) {
+        if (L.fork_at >= (int)p.launches.size() || grp[L.fork_at] != grp[l] || pos[L.fork_at] > pos[l])
+          return fail(TLR_ERR_INVALID_ARG, "internal: side launch " + std::to_string(l) +
+                                               " forks after its own wait is enqueued");
+      }
+      if (L.wait_launch >= 0) {
+        if (L.wait_launch >= (int)p.launches.size() || pos[L.wait_launch] >= pos[l])
+          return fail(TLR_ERR_INVALID_ARG, "internal: launch " + std::to_string(l) +
+                                               " waits for a launch enqueued after it");
+      }
+    }
+  }
   if (!deep) return TLR_OK;
 
   // deep check: replay every launch on per-element state

@@ -155,3 +155,60 @@ def test_pipelined_rectangles_two_streams(dtype):
         assert g.info["groups"] == 2 and g.info["runs"] >= 2
         ref = reference.gemm_reference(1.0, "T", A, "N", B, 1.0, C)
         assert reference.rel_fro(got, ref) <= TOL[dtype]
+
+
+def _block_diagonal(t):
+    """The operand with every off-diagonal tile dropped (rank 0): only the
+    dense diagonal is left."""
+    z = padded_tlr(t, 0)
+    for key in list(z.U):
+        z.ranks[key] = 0
+        z.U[key] = z.U[key][:, :0]
+        z.V[key] = z.V[key][:, :0]
+    return z
+
+
+@pytest.mark.parametrize("which", ["A", "B"])
+@pytest.mark.parametrize("flags", [F_LEFT, F_RIGHT])
+def test_no_coupling_back_to_back_executes(which, flags):
+    """One operand block-diagonal (no coupling launch at all), a budget that
+    splits C into several rectangles sharing one workspace arena, and two
+    executes of one plan enqueued back to back with different values of the
+    other operand.  The side launch of each rectangle writes its
+    diagonal-term products into the arena; it must start only after the
+    previous rectangle's (and the previous execute's) final update has read
+    it.  Both results are compared with the oracle."""
+    import torch
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_from_device, dense_to_device
+    n, b = 640, 64
+    A1, B1, C = _pair(41, n, b, lo=4, hi=30)
+    A2, B2, _ = _pair(42, n, b, lo=4, hi=30)
+    if which == "A":
+        A1 = _block_diagonal(A1)
+        B2.ranks[:] = B1.ranks          # same structure, new values
+        B2.U = {k: np.random.default_rng(7).standard_normal(v.shape) for k, v in B1.U.items()}
+        B2.V = {k: np.random.default_rng(8).standard_normal(v.shape) for k, v in B1.V.items()}
+        pairs = [(A1, B1), (A1, B2)]
+    else:
+        B1 = _block_diagonal(B1)
+        A2.ranks[:] = A1.ranks
+        A2.U = {k: np.random.default_rng(7).standard_normal(v.shape) for k, v in A1.U.items()}
+        A2.V = {k: np.random.default_rng(8).standard_normal(v.shape) for k, v in A1.V.items()}
+        pairs = [(A1, B1), (A2, B1)]
+    dev = [(DeviceTLR(a), DeviceTLR(bb)) for a, bb in pairs]
+    sa, sb = dev[0][0].shape, dev[0][1].shape
+    w = T.tlr_gemm_workspace_bytes("f64", "N", sa, "N", sb, flags=flags, runs=4)
+    g = TLRGemm("f64", "N", dev[0][0], "N", dev[0][1], ldc=n, budget=w, flags=flags)
+    assert g.info["runs"] >= 2
+    stages = [L["stage"] for L in g.launches()]
+    assert 1 not in stages and 4 in stages
+    Cs = [dense_to_device(C) for _ in pairs]
+    say(f"no-coupling {which} flags={flags} runs={g.info['runs']} launches={len(stages)}")
+    for (da, db), Cd in zip(dev, Cs):
+        g(1.0, da, db, 0.5, Cd)
+    torch.cuda.synchronize()
+    for (a, bb), Cd in zip(pairs, Cs):
+        got = dense_from_device(Cd, n, n)
+        ref = reference.gemm_reference(1.0, "N", a, "N", bb, 0.5, C)
+        assert reference.rel_fro(got, ref) <= 1e-12

@@ -341,3 +341,34 @@ def test_per_k_plans(seed):
     with pytest.raises(T.TLRError) as e:
         T.tlr_gemm_analyze("f64", "N", sa, "N", None, n, n, ldb=n, ldc=n, flags=T.TLR_PLAN_PER_K)
     assert e.value.status == T.TLR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("flags", [T.TLR_PLAN_FORCE_LEFT, T.TLR_PLAN_FORCE_RIGHT, 0])
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_no_coupling_plans_keep_stream_order(flags, which):
+    """A rectangle with no coupling work (one operand block-diagonal: dense
+    diagonal, every off-diagonal rank 0) still has diagonal-term products on
+    the side stream.  Its fork event must be recorded on the group's stream
+    before the side stream waits on it; the planner's own check of the
+    enqueue order (run on every plan) rejects any other plan, so every
+    analysis below must succeed, under budgets that split C into several
+    rectangles, with and without boundary regions on their own streams."""
+    rng = np.random.default_rng(31)
+    for n, b, n_streams in ((256, 64, 1), (300, 64, 3)):
+        q = -(-n // b)
+        Z = np.zeros((q, q), np.int32)
+        R = _rand_ranks(rng, q, b, True, 1, 20)
+        sa = T.Shape(n, n, b, Z if which == "A" else R, True)
+        sb = T.Shape(n, n, b, R if which == "A" else Z, True)
+        for runs in (1, 2, 4):
+            try:
+                w = T.tlr_gemm_workspace_bytes("f64", "N", sa, "N", sb, n_streams=n_streams, flags=flags, runs=runs)
+            except T.TLRError as e:           # the forced order cannot reach that many runs' budget
+                assert e.status == T.TLR_ERR_WORKSPACE
+                continue
+            p = T.tlr_gemm_analyze("f64", "N", sa, "N", sb, ldc=n, workspace_budget=w, n_streams=n_streams,
+                                   flags=flags | T.TLR_PLAN_VALIDATE)
+            info = T.tlr_plan_info(p)
+            stages = [T.tlr_plan_launch(p, l)["stage"] for l in range(info["launches"])]
+            assert 1 not in stages
+            assert 4 in stages
