@@ -1,33 +1,26 @@
-"""Planted mistakes in the oracle are caught by its pins.
+"""Planted mistakes in the oracle make its pins fail.
 
 Each test patches one plausible bug into an oracle function (on the CPU, for
-the duration of the test only) and checks that the corresponding pin fails:
-a dropped diagonal term, an ignored transpose, a transposed tile placement,
-C read when beta = 0, alpha applied to C, column sums used for rho, and a
-dropped coupling term in the flop count."""
-import json
-import os
-
+the duration of the test only), then runs the pin that is meant to catch it
+(a test function of tests/test_oracle_*.py, called directly) and requires
+that pin to fail with an AssertionError.  The unpatched pins pass in their
+own modules.  Planted mistakes: a dropped diagonal tile, an ignored
+transpose, a transposed tile placement, C read when beta = 0, alpha applied
+to C, column sums taken for rho, a dropped coupling term in the flop count,
+and a diagonal-term workspace sized by the wrong tile list."""
 import numpy as np
+import pytest
 
-from oracle import brute, plan_arith as pa, reference
-from tlr_inputs import random_tlr, tile_sizes
-
-GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
-
-
-def _brute_agrees(opA="N", opB="N", beta=0.5, n=10, b=4, seed=3):
-    rng = np.random.default_rng(seed)
-    A = random_tlr(rng, n, n, b, rank_lo=1, has_diag=True, scale=1.0)
-    B = random_tlr(rng, n, n, b, rank_lo=1, has_diag=True, scale=1.0)
-    C = rng.standard_normal((n, n))
-    ref = reference.gemm_reference(0.75, opA, A, opB, B, beta, C)
-    bf, _ = brute.tile_loop(0.75, opA, A, opB, B, beta, C, "right")
-    return reference.rel_fro(bf, ref) <= 1e-13
+import test_oracle_brute as pin_brute
+import test_oracle_invariants as pin_inv
+import test_oracle_plan_arith as pin_arith
+from oracle import plan_arith as pa
+from oracle import reference
 
 
-def test_unpatched_agrees():
-    assert _brute_agrees() and _brute_agrees("T", "T")
+def _fails(pin, *args):
+    with pytest.raises(AssertionError):
+        pin(*args)
 
 
 def test_dropped_diagonal_is_caught(monkeypatch):
@@ -37,37 +30,35 @@ def test_dropped_diagonal_is_caught(monkeypatch):
         out = orig(t, i, j)
         return np.zeros_like(out) if (t.has_diag and i == j) else out
     monkeypatch.setattr(reference, "dense_tile", bad)
-    assert not _brute_agrees()
+    _fails(pin_brute.test_tlr_tlr_all_ops, 3, 4, 0)
+    _fails(pin_inv.test_block_diagonal_when_offdiag_ranks_zero)
 
 
 def test_ignored_transpose_is_caught(monkeypatch):
     monkeypatch.setattr(reference, "_op", lambda M, op: M)
-    assert not _brute_agrees("T", "N")
+    _fails(pin_brute.test_tlr_tlr_all_ops, 2, 3, 0)
+    _fails(pin_inv.test_transpose_by_factor_swap, "T", "N")
 
 
 def test_transposed_tile_placement_is_caught(monkeypatch):
     orig = reference.dense_tile
 
     def bad(t, i, j):
-        if t.has_diag and i == j:
+        if (t.has_diag and i == j) or t.row_sizes[i] != t.row_sizes[j]:
             return orig(t, i, j)
-        out = orig(t, j, i) if (t.row_sizes[i] == t.row_sizes[j]) else orig(t, i, j)
-        return out
+        return orig(t, j, i)
     monkeypatch.setattr(reference, "dense_tile", bad)
-    assert not _brute_agrees(n=12, b=4)
+    _fails(pin_brute.test_tlr_tlr_all_ops, 3, 4, 0)
 
 
 def test_beta_zero_reading_c_is_caught(monkeypatch):
+    orig = reference.gemm_reference
+
     def bad(alpha, opA, A, opB, B, beta, C_in):
-        Ad = reference._op(reference.reconstruct(A), opA)
-        Bd = reference._op(reference.reconstruct(B), opB)
-        return alpha * (Ad @ Bd) + beta * np.asarray(C_in)
+        out = orig(alpha, opA, A, opB, B, 1.0 if beta == 0.0 else beta, C_in)
+        return out - (np.asarray(C_in) if beta == 0.0 and C_in is not None else 0.0)
     monkeypatch.setattr(reference, "gemm_reference", bad)
-    rng = np.random.default_rng(1)
-    A = random_tlr(rng, 8, 8, 4, has_diag=True)
-    B = random_tlr(rng, 8, 8, 4, has_diag=True)
-    got = reference.gemm_reference(1.0, "N", A, "N", B, 0.0, np.full((8, 8), np.nan))
-    assert not np.all(np.isfinite(got))
+    _fails(pin_inv.test_beta_zero_ignores_c, np.nan)
 
 
 def test_alpha_on_c_is_caught(monkeypatch):
@@ -76,21 +67,39 @@ def test_alpha_on_c_is_caught(monkeypatch):
     def bad(alpha, opA, A, opB, B, beta, C_in):
         return alpha * orig(1.0, opA, A, opB, B, beta, C_in)
     monkeypatch.setattr(reference, "gemm_reference", bad)
-    assert not _brute_agrees()
+    _fails(pin_brute.test_tlr_tlr_all_ops, 2, 3, 1)
+    _fails(pin_inv.test_linearity)
 
 
 def test_rho_from_column_sums_is_caught(monkeypatch):
     monkeypatch.setattr(pa, "rho", lambda RA: [int(x) for x in np.asarray(RA).sum(axis=0)])
-    RA = np.array(GOLD["A_ranks"])
-    assert pa.rho(RA) != GOLD["printed"]["rho"]
+    _fails(pin_arith.test_worked_example, "B_a")
+    _fails(pin_arith.test_worked_example, "B_b")
 
 
-def test_dropped_coupling_flops_is_caught():
-    rng = np.random.default_rng(2)
-    A = random_tlr(rng, 9, 9, 3, rank_lo=1, has_diag=True, scale=1.0)
-    B = random_tlr(rng, 9, 9, 3, rank_lo=1, has_diag=True, scale=1.0)
-    s = tile_sizes(9, 3)
-    _, flops = brute.tile_loop(1.0, "N", A, "N", B, 0.0, None, "right")
-    good = pa.useful_flops(A.ranks, B.ranks, s, s, s, True, True, "right")
-    coupling = sum(2 * a * c * d for (_, _, _, (a, c, d)) in pa.coupling_products(A.ranks, B.ranks, s))
-    assert flops == good and flops != good - coupling
+def test_dropped_coupling_flops_is_caught(monkeypatch):
+    orig = pa.useful_flops
+
+    def bad(RA, RB, ms, ks, ns, dA, dB, order, I=None, J=None):
+        RA_, RB_ = np.asarray(RA), np.asarray(RB)
+        I_ = range(RA_.shape[0]) if I is None else I
+        J_ = range(RB_.shape[1]) if J is None else J
+        coupling = sum(2 * ra * rb * sk for (i, k, j, (ra, rb, sk)) in pa.coupling_products(RA_, RB_, ks)
+                       if i in I_ and j in J_ and not (dA and i == k) and not (dB and k == j))
+        return orig(RA, RB, ms, ks, ns, dA, dB, order, I, J) - coupling
+    monkeypatch.setattr(pa, "useful_flops", bad)
+    _fails(pin_arith.test_brute_force_flops_equal_useful_flops, 1, 9, 3, True, "N", "N")
+    _fails(pin_arith.test_uniform_rank_closed_form, 3, 8, 2, 5)
+
+
+def test_diagonal_workspace_with_wrong_sizes_is_caught(monkeypatch):
+    orig = pa.workspace_elements
+
+    def bad(RA, RB, ms, ks, ns, dA, dB, order, I, J):
+        # X_i = D_A,ii W_{i,J} sized with the column tile list instead of the row one
+        w = orig(RA, RB, ms, ks, ns, dA, dB, order, I, J)
+        if order == "right" and dA:
+            w["diag"] = sum(ns[i] * sum(int(np.asarray(RB)[i, j]) for j in J) for i in I)
+        return w
+    monkeypatch.setattr(pa, "workspace_elements", bad)
+    _fails(pin_arith.test_workspace_elements_hand_counts, pin_arith.WS_R, "right")

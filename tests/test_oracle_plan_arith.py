@@ -120,3 +120,42 @@ def test_workspace_elements_worked_example():
     assert w["S"] == sum(M * N for (M, N, K) in GOLD["printed"]["stage1_shapes_MNK"])
     w = pa.workspace_elements(RA, RB, ms, ks, ns, False, False, "left", [0, 1], [0, 1, 2])
     assert w["terminal"] == 512 * 304
+
+
+# Hand counts of one rectangle's intermediates, with dense diagonals and
+# sub-rectangles ("TLR Matrix Multiplication", "The easy terms": the diagonal
+# term of A gives X_i = D_A,ii W_{i,J}, s_i rows by sum_{j in J} r^B_ij
+# columns; that of B gives X'_j = V_{I,j}^T D_B,jj, sum_{i in I} r^A_ij rows
+# by s_j columns; "Tile-Low-Rank GEMM: Designing Storage Around the
+# Contraction", "One product, three stages": S_k is sum_{i in I} r_ik by
+# sum_{j in J} r_kj, T_i is rho_i by the width of J, Y_j the height of I by
+# gamma_j).  Tile sizes differ along the three dimensions, so a swapped size
+# list changes the count.  Every number below was added up by hand.
+#
+# Case R: op(A) 11 x 11 with a dense diagonal (tiles 4, 4, 3), op(B) 11 x 14
+# without one (column tiles 4, 4, 4, 2); I = tile rows {1, 2}, J = tile
+# columns {1, 2, 3}.
+#   S: k=0 (3+2)(2+0+3)=25, k=1 (0+2)(0+2+1)=6, k=2 (1+0)(1+1+0)=2 -> 33
+#   right: rho_1 = 4, rho_2 = 4, width 4+4+2 = 10 -> T 80;
+#          X_1 = 4 rows x (0+2+1) = 12, X_2 = 3 rows x (1+1+0) = 6 -> 18
+#   left:  gamma = 3, 3, 4, height 4+3 = 7 -> Y 70; no diagonal in B -> 0
+# Case L: op(A) 14 x 11 without a diagonal (row tiles 4, 4, 4, 2), op(B)
+# 11 x 11 with one (tiles 4, 4, 3); I = {0, 2, 3}, J = {0, 2}.
+#   S: k=0 (1+0+1)(0+1)=2, k=1 (0+3+1)(1+3)=16, k=2 (2+1+1)(2+0)=8 -> 26
+#   left:  gamma_0 = 3, gamma_2 = 4, height 4+4+2 = 10 -> Y 70;
+#          X'_0 = (1+0+1) x 4 = 8, X'_2 = (2+1+1) x 3 = 12 -> 20
+#   right: rho = 3, 4, 3, width 4+3 = 7 -> T 70; no diagonal in A -> 0
+WS_R = dict(RA=[[0, 1, 2], [3, 0, 1], [2, 2, 0]], RB=[[1, 2, 0, 3], [1, 0, 2, 1], [2, 1, 1, 0]],
+            ms=[4, 4, 3], ks=[4, 4, 3], ns=[4, 4, 4, 2], dA=True, dB=False, I=[1, 2], J=[1, 2, 3],
+            right={"S": 33, "terminal": 80, "diag": 18}, left={"S": 33, "terminal": 70, "diag": 0})
+WS_L = dict(RA=[[1, 0, 2], [2, 1, 0], [0, 3, 1], [1, 1, 1]], RB=[[0, 2, 1], [1, 0, 3], [2, 1, 0]],
+            ms=[4, 4, 4, 2], ks=[4, 4, 3], ns=[4, 4, 3], dA=False, dB=True, I=[0, 2, 3], J=[0, 2],
+            right={"S": 26, "terminal": 70, "diag": 0}, left={"S": 26, "terminal": 70, "diag": 20})
+
+
+@pytest.mark.parametrize("case", [WS_R, WS_L], ids=["diag_A", "diag_B"])
+@pytest.mark.parametrize("order", ["right", "left"])
+def test_workspace_elements_hand_counts(case, order):
+    w = pa.workspace_elements(np.array(case["RA"]), np.array(case["RB"]), case["ms"], case["ks"], case["ns"],
+                              case["dA"], case["dB"], order, case["I"], case["J"])
+    assert w == case[order]
