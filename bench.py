@@ -32,6 +32,23 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "TLR GEMM useful TFLOP/s + % of roofline, fp64 TLRxTLR->dense N=16384"
 DEFAULT_WORKLOAD = "3"
 
+# Launch configuration the benchmark times for each workload unless --streams
+# or --pipeline say otherwise: streams given to execute, and whether the
+# rectangles alternate between two arenas on two streams.  The full-size GPU
+# parity tests run exactly these configurations.
+LAUNCH = {"1": {"streams": 1, "pipeline": False}, "2": {"streams": 1, "pipeline": False},
+          "3": {"streams": 1, "pipeline": False}, "4": {"streams": 1, "pipeline": False},
+          "5": {"streams": 1, "pipeline": False}, "dense_tlr": {"streams": 1, "pipeline": False}}
+
+
+def launch_config(workload: str, streams=None, pipeline=None):
+    """(n_streams, pipelined) for a workload: the LAUNCH entry, overridden by
+    explicit values.  Pipelining needs two streams."""
+    d = LAUNCH.get(workload, {"streams": 1, "pipeline": False})
+    pipe = d["pipeline"] if pipeline is None else bool(pipeline)
+    ns = d["streams"] if streams is None else int(streams)
+    return max(ns, 2 if pipe else 1), pipe
+
 
 def workload(name: str, dtype=None):
     """Inputs of a bench workload: "1".."5" are the seeded workloads of
@@ -261,8 +278,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-GEMM reference")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--pipeline", type=int, default=0,
-                    help="1: rectangles alternate between two workspace arenas on two streams")
+    ap.add_argument("--pipeline", type=int, default=None,
+                    help="1: rectangles alternate between two workspace arenas on two streams "
+                         "(default: the workload's LAUNCH entry)")
+    ap.add_argument("--streams", type=int, default=None,
+                    help="streams given to execute; with two or more the boundary regions of C run on their "
+                         "own streams (default: the workload's LAUNCH entry)")
     ap.add_argument("--comparator", action="store_true",
                     help="also time the per-contraction-tile loop (one pass over C per k) on operands padded to "
                          "one rank: the batched-GEMM comparator the three-stage product is set against")
@@ -301,8 +322,8 @@ def main():
     dense_shape = A.shape if dense_a else (B.shape if dense_b else None)
     tdt = _TORCH[dtype]
     Cd = dense_to_device(C_in, dtype=dtype) if C_in is not None else torch.zeros((N, N), dtype=tdt, device="cuda")
-    n_streams = 2 if args.pipeline else 1
-    flags = (T.TLR_PLAN_PIPELINE if args.pipeline else 0) | \
+    n_streams, pipelined = launch_config(args.workload, args.streams, args.pipeline)
+    flags = (T.TLR_PLAN_PIPELINE if pipelined else 0) | \
         {"auto": 0, "left": T.TLR_PLAN_FORCE_LEFT, "right": T.TLR_PLAN_FORCE_RIGHT}[args.order]
     g = TLRGemm(dtype, cfg["opA"], None if dense_a else dA, cfg["opB"], None if dense_b else dB, ldc=N,
                 dense_shape=dense_shape, ldb=N if (dense_a or dense_b) else 0, budget=cfg["budget"] or 0,
@@ -460,7 +481,7 @@ def main():
         "config": {"workload": cfg["name"], "N": N, "b": cfg["b"], "opA": cfg["opA"], "opB": cfg["opB"],
                    "alpha": cfg["alpha"], "beta": cfg["beta"], "useful_flops": F, "order": order,
                    **({"stored_rank_flops": F_stored, "useful_flops_basis": basis} if sixteen else {}),
-                   "runs": info["runs"], "streams": n_streams, "pipelined": bool(args.pipeline),
+                   "runs": info["runs"], "groups": info["groups"], "streams": n_streams, "pipelined": pipelined,
                    "workspace_GiB": round(info["workspace_bytes"] / 2 ** 30, 3)},
         "roofline": roofline,
         "path_roofline": {"bound": "mfma" if roof >= peak else "hbm", "achieved": round(value, 3),

@@ -556,13 +556,17 @@ __global__ void scale_kernel(T *C, int64_t m, int64_t n, int64_t ldc, T beta) {
 }
 
 // beta/alpha when C can be pre-scaled into the accumulators, else 0 (then the
-// epilogue reads C).
+// epilogue reads C and adds beta*C after scaling by alpha).  The pre-scaled
+// form computes alpha*((beta/alpha)*C + sum), so it is used only when
+// |beta/alpha| <= 1 (the scaled C cannot overflow where C does not) and
+// |beta/alpha| is a normal number of T (a subnormal ratio would drop digits
+// of the beta*C term).
 template <typename T>
 T preload_scale(double alpha, double beta) {
   if (beta == 0.0 || alpha == 0.0) return T(0);
-  const double r = beta / alpha;
-  const double lim = sizeof(T) == 8 ? 1e300 : 1e30;
-  return (r == r && r < lim && r > -lim) ? T(r) : T(0);
+  const double r = beta / alpha, a = r < 0 ? -r : r;
+  const double tiny = sizeof(T) == 8 ? 2.2250738585072014e-308 : 1.1754943508222875e-38;
+  return (a <= 1.0 && a >= tiny) ? T(r) : T(0);
 }
 
 template <typename T, int STAGE, int NJ>

@@ -312,10 +312,13 @@ __global__ void scale16_kernel(uint16_t *C, int64_t m, int64_t n, int64_t ldc, f
   }
 }
 
+// beta/alpha for the pre-scaled C update alpha*((beta/alpha)*C + sum), used
+// only when |beta/alpha| <= 1 and normal in float; otherwise 0 and the
+// epilogue reads C (as in the 32/64-bit kernel).
 float preload_scale16(double alpha, double beta) {
   if (beta == 0.0 || alpha == 0.0) return 0.0f;
-  const double r = beta / alpha;
-  return (r == r && r < 1e30 && r > -1e30) ? (float)r : 0.0f;
+  const double r = beta / alpha, a = r < 0 ? -r : r;
+  return (a <= 1.0 && a >= 1.1754943508222875e-38) ? (float)r : 0.0f;
 }
 
 template <typename H, int NJ>

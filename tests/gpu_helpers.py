@@ -19,6 +19,10 @@ from tlr_inputs import TLRTiles
 # float accumulation adds at most K * 2^-24 per element, far below u.
 TOL = {"f64": 1e-12, "f32": 1e-5, "f16": 2.0 * 2.0 ** -11, "bf16": 2.0 * 2.0 ** -8}
 
+# unit roundoff of each element type; 16-bit products accumulate in float
+UNIT = {"f64": 2.0 ** -53, "f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+ACC_UNIT = {"f64": 2.0 ** -53, "f32": 2.0 ** -24, "f16": 2.0 ** -24, "bf16": 2.0 ** -24}
+
 
 def say(*a):
     print(*a, flush=True)
@@ -89,13 +93,67 @@ def run_tlr(A, B, opA: str, opB: str, alpha: float, beta: float, C_in,
     return out
 
 
+def abs_operand(t):
+    """The operand with every factor, diagonal tile or dense entry replaced by
+    its absolute value (rebuilt, tile (i,j) is |U_ij| |V_ij|^T)."""
+    if not isinstance(t, TLRTiles):
+        return np.abs(np.asarray(t, dtype=np.float64))
+    a = copy.copy(t)
+    a.U = {k: np.abs(np.asarray(v, dtype=np.float64)) for k, v in t.U.items()}
+    a.V = {k: np.abs(np.asarray(v, dtype=np.float64)) for k, v in t.V.items()}
+    a.diag = None if t.diag is None else [np.abs(np.asarray(d, dtype=np.float64)) for d in t.diag]
+    return a
+
+
+def element_bound_factor(dtype: str, k: int, b: int) -> float:
+    """Factor f of the per-element bound |C_gpu - C| <= f * scale, scale =
+    |alpha| |A|_f |B|_f + |beta| |C_in| with |X|_f the operand rebuilt from
+    the absolute values of its factors.  Every element is an inner product
+    along a chain of at most three products: the coupling (inner length
+    <= b), the right or left product (<= b) and the final update (<= k + b
+    with the diagonal-term segment), so the first-order rounding bound of a
+    product chain gives (k + 3b) accumulation roundings plus the roundings of
+    the stored intermediates and of alpha / beta.  For the 16-bit types the
+    three stored results (coupling, right/left product, C) are rounded to the
+    16-bit type and the sums are accumulated in float.  fp64 is compared with
+    an fp64 oracle whose own error obeys the same bound: factor 2."""
+    acc = (k + 3 * b + 4) * ACC_UNIT[dtype]
+    if dtype in ("f16", "bf16"):
+        return 3 * UNIT[dtype] + acc
+    return 2 * acc if dtype == "f64" else acc
+
+
+def check_elements(got, ref, scale, dtype: str, k: int, b: int, what: str = ""):
+    """Per-element bound of element_bound_factor (catches one wrong block or
+    element that a norm over the whole matrix would hide)."""
+    f = element_bound_factor(dtype, k, b)
+    bad = np.abs(np.asarray(got, np.float64) - ref) > f * scale + 1e-300
+    if np.any(bad):
+        r, c = np.argwhere(bad)[0]
+        raise AssertionError(f"{what} {int(bad.sum())} elements beyond the per-element bound, e.g. ({r},{c}): "
+                             f"got {got[r, c]!r} ref {ref[r, c]!r} bound {f * scale[r, c]:.3e}")
+
+
+def inner_dim(A, opA):
+    if isinstance(A, TLRTiles):
+        return op_dims(A, opA)[1]
+    A = np.asarray(A)
+    return A.shape[1] if opA == "N" else A.shape[0]
+
+
 def check_tlr(A, B, opA, opB, alpha, beta, C_in, **kw):
+    """The GPU product against the oracle: relative Frobenius error within
+    TOL and every element within the per-element bound."""
     got = run_tlr(A, B, opA, opB, alpha, beta, C_in, **kw)
     ref = reference.gemm_reference(alpha, opA, A, opB, B, beta, C_in)
     err = reference.rel_fro(got, ref)
     dtype = kw.get("dtype") or (A.dtype if isinstance(A, TLRTiles) else B.dtype)
     assert np.all(np.isfinite(got)), "non-finite output"
     assert err <= TOL[dtype], f"relative Frobenius error {err:.3e} > {TOL[dtype]:.0e}"
+    scale = reference.gemm_reference(abs(alpha), opA, abs_operand(A), opB, abs_operand(B), abs(beta),
+                                     None if beta == 0 else np.abs(np.asarray(C_in, np.float64)))
+    tb = A.b if isinstance(A, TLRTiles) else B.b
+    check_elements(got, ref, scale, dtype, inner_dim(A, opA), tb)
     return err
 
 

@@ -16,7 +16,7 @@ import itertools
 import numpy as np
 import pytest
 
-from gpu_helpers import TOL, check_tlr, gpu_ready, run_tlr, say
+from gpu_helpers import TOL, abs_operand, check_elements, check_tlr, gpu_ready, run_tlr, say
 from oracle import reference
 from tlr_inputs import on_grid, random_tlr
 
@@ -143,6 +143,9 @@ def test_n16384_b512_sampled(dtype):
                                              C_in[r0:r1, c0:c1], (r0, r1), (c0, c1))
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
+        scale = reference.gemm_reference_block(1.0, cfg["opA"], abs_operand(A), cfg["opB"], abs_operand(B), 1.0,
+                                               np.abs(C_in[r0:r1, c0:c1].astype(np.float64)), (r0, r1), (c0, c1))
+        check_elements(got, ref, scale, dtype, N, b, f"{dtype} tile ({i},{j})")
     err = (num / den) ** 0.5
     say(f"{dtype} N={N}: sampled rel Frobenius error {err:.3e}")
     assert err <= TOL[dtype]
@@ -226,6 +229,7 @@ def test_large_workloads_sampled_half(c):
     i, j = np.unravel_index(np.argmax(R), R.shape)
     tiles.add((int(i), int(j)))
     num = den = 0.0
+    Aa, Ba = abs_operand(A), abs_operand(B)
     for (i, j) in sorted(tiles):
         r0, r1, c0, c1 = off[i], off[i] + sz[i], off[j], off[j] + sz[j]
         got = Cd[c0:c1, r0:r1].float().cpu().numpy().T.astype(np.float64)
@@ -234,6 +238,10 @@ def test_large_workloads_sampled_half(c):
                                              (r0, r1), (c0, c1))
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
+        scale = reference.gemm_reference_block(abs(cfg["alpha"]), cfg["opA"], Aa, cfg["opB"], Ba, abs(cfg["beta"]),
+                                               None if cin is None else np.abs(cin.astype(np.float64)),
+                                               (r0, r1), (c0, c1))
+        check_elements(got, ref, scale, "f16", N, b, f"half workload {c} tile ({i},{j})")
     err = (num / den) ** 0.5
     say(f"half workload {c}: sampled rel Frobenius error {err:.3e}")
     assert err <= TOL["f16"]

@@ -212,3 +212,13 @@ def test_no_coupling_back_to_back_executes(which, flags):
         got = dense_from_device(Cd, n, n)
         ref = reference.gemm_reference(1.0, "N", a, "N", bb, 0.5, C)
         assert reference.rel_fro(got, ref) <= 1e-12
+
+
+@pytest.mark.parametrize("dtype,alpha", [("f32", 1e-29), ("f64", 1e-299)])
+def test_tiny_alpha_large_c_does_not_overflow(dtype, alpha):
+    """beta / alpha far above 1: C must not be pre-scaled by beta / alpha (that
+    overflows for |C| ~ 1e10) but updated as alpha * sum + beta * C."""
+    A, B, _ = _pair(51, 200, 64, dtype=dtype)
+    C = 1e10 * np.random.default_rng(52).standard_normal((200, 200))
+    check_tlr(A, B, "N", "N", alpha, 1.0, C)
+    check_tlr(A, B, "T", "N", alpha, -0.5, C, flags=F_LEFT)
