@@ -202,6 +202,15 @@ tlr_status tlr_gemm_execute(tlr_plan *h, double alpha, const tlr_buffers *A, con
   })
 }
 
+tlr_status tlr_gemm_execute_noalloc(tlr_plan *h, double alpha, const tlr_buffers *A, const tlr_buffers *B,
+                                    const void *B_dense, int64_t ldb, double beta, void *C, int64_t ldc,
+                                    void *const *streams, int32_t n_streams) {
+  if (!h) return tlr::fail(TLR_ERR_INVALID_ARG, "execute_noalloc: null plan");
+  TLR_GUARD({
+    return tlr::plan_execute_noalloc(&h->p, alpha, A, B, B_dense, ldb, beta, C, ldc, streams, n_streams);
+  })
+}
+
 tlr_status tlr_plan_profile(tlr_plan *h, int32_t max_executes) {
   if (!h) return tlr::fail(TLR_ERR_INVALID_ARG, "profile: null plan");
   TLR_GUARD({ return tlr::plan_profile(&h->p, max_executes); })

@@ -137,6 +137,9 @@ tlr_status plan_bind(Plan *p, void *dev_desc, size_t bytes, void *stream);
 tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_buffers *B,
                         const void *B_dense, int64_t ldb, double beta, void *C, int64_t ldc,
                         void *ws, size_t ws_bytes, void *const *streams, int n_streams);
+tlr_status plan_execute_noalloc(Plan *p, double alpha, const tlr_buffers *A, const tlr_buffers *B,
+                                const void *B_dense, int64_t ldb, double beta, void *C, int64_t ldc,
+                                void *const *streams, int n_streams);
 tlr_status plan_profile(Plan *p, int max_exec);
 tlr_status plan_profile_read(Plan *p, double *stage_ms, double *launch_ms, int32_t *execs);
 void plan_release_device(Plan *p);

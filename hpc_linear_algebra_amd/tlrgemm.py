@@ -23,11 +23,12 @@ TLR_ORDER_RIGHT, TLR_ORDER_LEFT = 0, 1
 TLR_PLAN_FORCE_RIGHT, TLR_PLAN_FORCE_LEFT, TLR_PLAN_NO_REGIONS, TLR_PLAN_VALIDATE = 0x1, 0x2, 0x4, 0x8
 TLR_PLAN_PIPELINE = 0x10
 TLR_PLAN_PER_K = 0x20
+TLR_STATIC_WORKSPACE_BYTES = 256 * 1024 * 1024
 
 EXPORTED = [
     "tlr_gemm_analyze", "tlr_gemm_workspace_bytes", "tlr_plan_info", "tlr_plan_rect",
     "tlr_plan_stage_shapes", "tlr_plan_launch", "tlr_plan_destroy", "tlr_plan_bind",
-    "tlr_gemm_execute", "tlr_plan_profile", "tlr_plan_profile_read", "tlr_dense_gemm",
+    "tlr_gemm_execute", "tlr_gemm_execute_noalloc", "tlr_plan_profile", "tlr_plan_profile_read", "tlr_dense_gemm",
     "tlr_status_string", "tlr_last_error", "tlr_version",
 ]
 
@@ -83,6 +84,8 @@ def lib():
     L.tlr_plan_bind.argtypes = [P, P, c_size_t, P]
     L.tlr_gemm_execute.argtypes = [P, c_double, POINTER(tlr_buffers), POINTER(tlr_buffers), P, c_int64,
                                    c_double, P, c_int64, P, c_size_t, POINTER(P), c_int32]
+    L.tlr_gemm_execute_noalloc.argtypes = [P, c_double, POINTER(tlr_buffers), POINTER(tlr_buffers), P, c_int64,
+                                           c_double, P, c_int64, POINTER(P), c_int32]
     L.tlr_plan_profile.argtypes = [P, c_int32]
     L.tlr_plan_profile_read.argtypes = [P, POINTER(c_double), POINTER(c_double), POINTER(c_int32)]
     L.tlr_dense_gemm.argtypes = [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_double, P, c_int64,
@@ -222,6 +225,17 @@ def tlr_gemm_execute(p: Plan, alpha: float, A: Optional[tlr_buffers], B: Optiona
                                 c_void_p(B_dense or None), ldb, beta, c_void_p(C or None), ldc,
                                 c_void_p(workspace or None), workspace_bytes, arr, max(1, len(streams)))
     _check(st, "tlr_gemm_execute")
+
+
+def tlr_gemm_execute_noalloc(p: Plan, alpha: float, A: Optional[tlr_buffers], B: Optional[tlr_buffers],
+                             B_dense: int, ldb: int, beta: float, C: int, ldc: int, streams: Sequence[int]):
+    """tlr_gemm_execute with the library's static device workspace (no workspace argument)."""
+    arr = (c_void_p * max(1, len(streams)))(*[c_void_p(s or None) for s in streams])
+    st = lib().tlr_gemm_execute_noalloc(p.h, alpha, ctypes.byref(A) if A is not None else None,
+                                        ctypes.byref(B) if B is not None else None,
+                                        c_void_p(B_dense or None), ldb, beta, c_void_p(C or None), ldc, arr,
+                                        max(1, len(streams)))
+    _check(st, "tlr_gemm_execute_noalloc")
 
 
 def tlr_plan_profile(p: Plan, max_executes: int):

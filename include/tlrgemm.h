@@ -53,8 +53,10 @@
  *
  * Ownership: every device buffer (factors, diagonals, dense B, C, workspace,
  * descriptor buffer) belongs to the caller.  The library never allocates
- * device memory.  A plan owns host memory and the HIP events it creates; the
- * plan copies the rank tables at analysis time.
+ * device memory; the one piece it holds is the static workspace array of
+ * tlr_gemm_execute_noalloc (TLR_STATIC_WORKSPACE_BYTES per GPU, part of the
+ * loaded code object).  A plan owns host memory and the HIP events it
+ * creates; the plan copies the rank tables at analysis time.
  *
  * Errors: every entry point returns a tlr_status and writes its outputs only
  * on TLR_OK.  tlr_last_error() returns a thread-local description of the most
@@ -273,6 +275,33 @@ tlr_status tlr_gemm_execute(tlr_plan *p, double alpha,
                             double beta, void *C, int64_t ldc,
                             void *workspace, size_t workspace_bytes,
                             void *const *streams, int32_t n_streams);
+
+/* Bytes of the static device workspace of tlr_gemm_execute_noalloc (per GPU). */
+#define TLR_STATIC_WORKSPACE_BYTES (256u * 1024u * 1024u)
+
+/*
+ * tlr_gemm_execute_noalloc: tlr_gemm_execute without a workspace argument,
+ * for callers that cannot allocate device memory at the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * same plan runs the same launches; the workspace is the library's own static
+ * device array of TLR_STATIC_WORKSPACE_BYTES, one per GPU, which every GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the plan must already
+ * be bound (tlr_plan_bind, whose descriptor buffer the caller allocates once).
+ * Every call on one GPU shares that GPU's array and leaves its last contents
+ * in it (no product reads workspace it has not written first, so nothing
+ * needs clearing).  Calls on one GPU must be ordered (one stream, or events
+ * between them): calls that overlap race on the shared array.
+ *   Arguments as for tlr_gemm_execute.
+ * Errors: as tlr_gemm_execute; TLR_ERR_WORKSPACE when the plan needs more than
+ * TLR_STATIC_WORKSPACE_BYTES (analyse with a budget at most that size);
+ * nothing is launched then.
+ */
+tlr_status tlr_gemm_execute_noalloc(tlr_plan *p, double alpha,
+                                    const tlr_buffers *A, const tlr_buffers *B,
+                                    const void *B_dense, int64_t ldb,
+                                    double beta, void *C, int64_t ldc,
+                                    void *const *streams, int32_t n_streams);
 
 /*
  * tlr_plan_profile: record a HIP event pair around every launch of the next
