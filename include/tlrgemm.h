@@ -199,11 +199,16 @@ tlr_status tlr_gemm_workspace_bytes(tlr_dtype dt, tlr_op opA, const tlr_shape *A
                                     int32_t n_streams, uint32_t flags, int32_t runs,
                                     size_t *bytes_out);
 
-/* tlr_plan_info: fill *out.  Errors: TLR_ERR_INVALID_ARG on NULL. */
+/* tlr_plan_info: fill *out.  Plumbing: the pages define no such call; the
+ * counts are the rank arithmetic of "Association order and workspace" (useful
+ * flops, final-stage costs F_R and F_L) and the sizes this library needs.
+ * Errors: TLR_ERR_INVALID_ARG on NULL. */
 tlr_status tlr_plan_info(const tlr_plan *p, tlr_plan_summary *out);
 
 /*
- * tlr_plan_rect: rectangle `idx` (0 <= idx < runs) of the schedule.
+ * tlr_plan_rect: rectangle `idx` (0 <= idx < runs) of the schedule
+ * (introspection; the rectangles are those of "Association order and
+ * workspace", the call itself is plumbing the pages do not define).
  *   out_i32[0..5] = first tile row, end tile row (exclusive), first tile
  *                   column, end tile column, order (tlr_order), group.
  *   ws_bytes      workspace the rectangle uses inside its group's arena.
@@ -214,7 +219,8 @@ tlr_status tlr_plan_rect(const tlr_plan *p, int32_t idx, int32_t *out_i32,
 
 /*
  * tlr_plan_stage_shapes: (M, N, K) triples of the logical GEMMs of one stage of
- * rectangle `rect`, in order:
+ * rectangle `rect` (introspection, for checking the plan against the shapes
+ * the GEMM page prints; the call is plumbing the pages do not define), in order:
  *   stage 1  one coupling GEMM per contraction tile k ("One product, three
  *            stages", Stage 1): (sum_{i in I} r_ik, sum_{j in J} r_kj, s_k);
  *   stage 3  the final GEMMs: per tile row i (right order) (m_i, sum_J n_j, rho_i),
@@ -225,7 +231,8 @@ tlr_status tlr_plan_stage_shapes(const tlr_plan *p, int32_t rect, int32_t stage,
                                  int64_t *mnk, int32_t cap, int32_t *count);
 
 /*
- * tlr_plan_launch: launch `idx` (0 <= idx < launches) of one execute.
+ * tlr_plan_launch: launch `idx` (0 <= idx < launches) of one execute
+ * (introspection; plumbing the pages do not define).
  *   out_i32[0..3] = stage, tasks, workgroups, group.  Stages: 1 coupling,
  *   2 right/left product, 3 final update, 4 the diagonal-term products that
  *   read only the inputs (X = op(D_A) W or X' = V^T op(D_B), and the op(D_A) W
@@ -235,7 +242,8 @@ tlr_status tlr_plan_stage_shapes(const tlr_plan *p, int32_t rect, int32_t stage,
  */
 tlr_status tlr_plan_launch(const tlr_plan *p, int32_t idx, int32_t *out_i32, double *out_f64);
 
-/* tlr_plan_destroy: free the plan and its events (NULL is accepted). */
+/* tlr_plan_destroy: free the plan and its events (NULL is accepted).  Plumbing:
+ * the pages define no such call. */
 tlr_status tlr_plan_destroy(tlr_plan *p);
 
 /* ---- device entry points ------------------------------------------------- */
@@ -245,12 +253,21 @@ tlr_status tlr_plan_destroy(tlr_plan *p);
  * device buffer of at least descriptor_bytes bytes (256-byte aligned), on
  * `stream`, and create the plan's fork/join events on the current device.
  * The buffer must stay alive and unmodified while the plan is executed.
+ * Plumbing the pages do not define: the GEMM page only says that this setup
+ * is done once per rank structure and skipped afterwards ("Association order
+ * and workspace").
  * Errors: TLR_ERR_INVALID_ARG (NULL, too small, misaligned), TLR_ERR_HIP.
  */
 tlr_status tlr_plan_bind(tlr_plan *p, void *dev_desc, size_t bytes, void *stream);
 
 /*
- * tlr_gemm_execute: C <- alpha op(A) op(B) + beta C with the bound plan.
+ * tlr_gemm_execute: C <- alpha op(A) op(B) + beta C with the bound plan: the
+ * BLAS-style operation of the GEMM page's introduction, with a dense C and one
+ * or both operands in TLR format ("Tile-Low-Rank GEMM: Designing Storage
+ * Around the Contraction", introduction), evaluated in the three stages of
+ * "One product, three stages" (coupling, right or left product, one update of
+ * C with the sum over k inside the GEMM) and with the diagonal terms of "TLR
+ * Matrix Multiplication", "Regular TLR GEMM".
  *   A, B        device buffers of the analysed TLR operands (NULL for the
  *               dense one).
  *   B_dense     the dense operand (dense A or dense B as analysed), leading
@@ -304,6 +321,7 @@ tlr_status tlr_gemm_execute_noalloc(tlr_plan *p, double alpha,
                                     void *const *streams, int32_t n_streams);
 
 /*
+ * Profiling (plumbing the pages do not define; it feeds the measurement).
  * tlr_plan_profile: record a HIP event pair around every launch of the next
  * `max_executes` executes (0 switches recording off).  Creates the events on
  * the current device.  Errors: TLR_ERR_HIP.
@@ -334,11 +352,12 @@ tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64
                           const void *B, int64_t ldb, double beta, void *C, int64_t ldc,
                           void *stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (plumbing; the pages define no error
+ * handling). */
 const char *tlr_status_string(tlr_status s);
-/* Thread-local detail of the last failure on this thread ("" if none). */
+/* Thread-local detail of the last failure on this thread ("" if none; plumbing). */
 const char *tlr_last_error(void);
-/* Library version string. */
+/* Library version string (plumbing). */
 const char *tlr_version(void);
 
 #ifdef __cplusplus
