@@ -123,6 +123,22 @@ def traffic_from_profiles(stage: int, workload_name: str, sixteen_bit: bool = Fa
     return d.get("bytes_per_launch")
 
 
+def mfma_busy_from_profiles(stage: int, workload_name: str, sixteen_bit: bool = False):
+    """MFMA busy fraction of the dominant kernel from a committed rocprofv3
+    counter run of this workload, if it was taken on the current kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", f"stage{stage}_mfma_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("kernel_hash") != kernel_hash(sixteen_bit):
+        return None
+    return d.get("mfma_busy")
+
+
 def rebuild_dense_on_gpu(dev, t, dtype):
     """Dense N x N copy of a stored TLR operand, built with the library's own
     dense GEMM (U_ij V_ij^T per tile) and copies of the diagonal tiles."""
@@ -245,22 +261,31 @@ def cpu_baseline(cfg, A, B, C_in, useful_flops, budget_s=15.0):
     order = [(int(x) // q, int(x) % q) for x in rng.permutation(q * q)]
     t0 = time.perf_counter()
     done = 0
+    tm = {}
     for (i, j) in order:
         r0, r1, c0, c1 = off[i], off[i] + sz[i], off[j], off[j] + sz[j]
         cin = None if C_in is None else C_in[r0:r1, c0:c1]
         reference.gemm_reference_block(cfg["alpha"], cfg["opA"], A, cfg["opB"], B, cfg["beta"], cin,
-                                       (r0, r1), (c0, c1))
+                                       (r0, r1), (c0, c1), timings=tm)
         done += 1
         if time.perf_counter() - t0 > budget_s and done >= 2:
             break
     dt = time.perf_counter() - t0
     full_s = dt * (q * q) / done
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except Exception:
+        aff = None
     return {"value": useful_flops / full_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
+            "reconstruct_s": round(tm.get("reconstruct_s", 0.0), 3), "matmul_s": round(tm.get("matmul_s", 0.0), 3),
+            "measured_s": round(dt, 3), "tiles": done, "tiles_total": q * q,
+            "host_cpu_count": os.cpu_count(), "host_affinity": aff, "blas_threads": int(threads),
             "sample": f"{done} of {q*q} output tiles ({sz[0]}x{sz[0]}) rebuilt densely in fp64 from the row "
                       f"panel of op(A) and column panel of op(B) and multiplied with numpy BLAS; "
-                      f"{dt:.2f} s measured, scaled by {q*q}/{done} to the whole product "
-                      f"(host cpu_count={os.cpu_count()})"}
+                      f"{dt:.2f} s measured ({tm.get('reconstruct_s', 0.0):.2f} s rebuilding panels, "
+                      f"{tm.get('matmul_s', 0.0):.2f} s in the matmul), scaled by {q*q}/{done} to the whole "
+                      f"product (host cpu_count={os.cpu_count()})"}
 
 
 def main():
@@ -335,21 +360,36 @@ def main():
     streams = [stream.cuda_stream] + [x.cuda_stream for x in side]
     log(f"bench: plan runs={info['runs']} launches={info['launches']} ws={info['workspace_bytes']/2**30:.2f} GiB "
         f"useful={info['useful_flops']:.4e}")
-    for _ in range(args.warmup):
+    # with beta != 0 every step starts from the same C: a pristine device copy
+    # is restored before each step, outside the step's events
+    C0 = Cd.clone() if cfg["beta"] != 0 else None
+
+    def step():
+        if C0 is not None:
+            Cd.copy_(C0)
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        e[0].record(stream)
         g(cfg["alpha"], dA, dB, cfg["beta"], Cd, streams)
+        e[1].record(stream)
+        return e
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    # timed region: K steps, HIP events around every launch on its own stream
+    # timed region: K steps, one HIP event pair per step on streams[0] (the
+    # execute joins its other streams back into it) and one around every
+    # launch on the launch's own stream
     T.tlr_plan_profile(g.plan, args.steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        g(cfg["alpha"], dA, dB, cfg["beta"], Cd, streams)
-    ev1.record(stream)
+    evs = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    step_ms = [a.elapsed_time(b) for (a, b) in evs]
+    ms = sum(step_ms) / args.steps
+    srt = sorted(step_ms)
+    step_stats = {"mean": round(ms, 4), "median": round(srt[len(srt) // 2] if len(srt) % 2 else
+                                                        0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]), 4),
+                  "min": round(srt[0], 4), "max": round(srt[-1], 4)}
     stage_ms, launch_ms, nexec = T.tlr_plan_profile_read(g.plan, info["launches"])
     T.tlr_plan_profile(g.plan, 0)
     assert nexec == args.steps
@@ -367,7 +407,9 @@ def main():
         else:
             basis = "stored ranks (rounded up to multiples of 8; the rectangles use different orders)"
     value = F / (ms * 1e-3) / 1e12
-    log(f"bench: {ms:.3f} ms/step, {value:.2f} useful TFLOP/s (wall {wall*1e3/args.steps:.3f} ms/step)")
+    log(f"bench: {ms:.3f} ms/step (median {step_stats['median']:.3f}, min {step_stats['min']:.3f}, max "
+        f"{step_stats['max']:.3f}), {value:.2f} useful TFLOP/s (wall {wall*1e3/args.steps:.3f} ms/step with the "
+        f"restores of C)")
 
     # dominant kernel: the launch with the largest measured time
     per_launch = [x / args.steps for x in launch_ms]
@@ -392,7 +434,8 @@ def main():
     else:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"], sixteen),
-                    "kernel": kname, "launch_ms": round(per_launch[dom], 4)}
+                    "kernel": kname, "launch_ms": round(per_launch[dom], 4),
+                    "mfma_busy": mfma_busy_from_profiles(L["stage"], cfg["name"], sixteen)}
 
     dense = None
     if not args.no_dense and sixteen:
@@ -408,33 +451,41 @@ def main():
         def dense_call():
             T.tlr_dense_gemm(dtype, cfg["opA"], cfg["opB"], N, N, N, cfg["alpha"], Ad.data_ptr(), N,
                              Bd.data_ptr(), N, cfg["beta"], Cw.data_ptr(), N, s)
-        dense_call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 3
-        e0.record(stream)
-        for _ in range(reps):
+        for _ in range(2):
             dense_call()
-        e1.record(stream)
         torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / reps
+        reps = 10
+        devs = []
+        for _ in range(reps):
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
+            dense_call()
+            e[1].record(stream)
+            devs.append(e)
+        torch.cuda.synchronize()
+        d_ms = sorted(a.elapsed_time(b) for (a, b) in devs)
+        dms = sum(d_ms) / reps
         dense_tf = 2.0 * N ** 3 / (dms * 1e-3) / 1e12
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps_v = 3
         # context only: the vendor's GEMM (torch.matmul, rocBLAS / hipBLASLt) on the same operands
         torch.matmul(Ad, Bd)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(reps):
+        for _ in range(reps_v):
             Vw = torch.matmul(Ad, Bd)
         e1.record(stream)
         torch.cuda.synchronize()
-        vms = e0.elapsed_time(e1) / reps
+        vms = e0.elapsed_time(e1) / reps_v
         del Vw
-        dense = {"tflops": round(dense_tf, 3), "ms": round(dms, 3),
+        dense = {"tflops": round(dense_tf, 3), "ms": round(dms, 3), "ms_min": round(d_ms[0], 3),
+                 "ms_max": round(d_ms[-1], 3), "reps": reps,
                  "parity": round(value / dense_tf, 4),
                  "vendor_tflops": round(2.0 * N ** 3 / (vms * 1e-3) / 1e12, 3),
-                 "note": "useful TFLOP/s of the TLR product / TFLOP/s of the library's dense MFMA GEMM on the "
-                         "rebuilt N x N operands (dense time scaled by the executed-flop ratio); vendor_tflops: "
-                         "torch.matmul on the same operands, for context"}
+                 "note": "parity = useful TFLOP/s of the TLR product / TFLOP/s (2 N^3 per call) of the library's "
+                         "dense MFMA GEMM on the rebuilt N x N operands, which equals the dense time multiplied by "
+                         "useful flops / 2 N^3, divided by the TLR time; vendor_tflops: torch.matmul on the same "
+                         "operands, for context"}
         if dense_a:
             Ad = None
         if dense_b:
@@ -487,6 +538,7 @@ def main():
         "path_roofline": {"bound": "mfma" if roof >= peak else "hbm", "achieved": round(value, 3),
                           "roof": round(roof, 2), "unit": "TFLOP/s", "frac": round(value / roof, 4),
                           "arith_intensity": round(ai, 2)},
+        "step_ms": step_stats,
         "stages_ms": {"stage1": round(stage_ms[0] / nexec, 4), "stage2": round(stage_ms[1] / nexec, 4),
                       "stage3": round(stage_ms[2] / nexec, 4), "side": round(stage_ms[4] / nexec, 4),
                       "execute": round(stage_ms[3] / nexec, 4)},

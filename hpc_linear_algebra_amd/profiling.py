@@ -5,6 +5,7 @@ short markdown, for the committed profiles.
   python -m hpc_linear_algebra_amd.profiling pmc DIR [DIR ...] --command "..." > out.md
   python -m hpc_linear_algebra_amd.profiling traffic --fetch D --write D --copy-fetch D \
          --copy-write D --kernel REGEX --out profiles/stage3_traffic_WORKLOAD.json
+  python -m hpc_linear_algebra_amd.profiling mfma DIR --kernel REGEX --out profiles/stage3_mfma_WORKLOAD.json
 
 DIR is a rocprofv3 output directory written with --output-format csv.
 """
@@ -139,9 +140,29 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, kernel_regex, copy_byt
             "kernel_regex": kernel_regex, "kernel_hash": kernel_source_hash("gemm16" in kernel_regex)}
 
 
+SIMDS = 256 * 4     # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8            # GRBM_GUI_ACTIVE reads as the sum over the 8 XCDs
+
+
+def mfma_busy(pmc_dir, kernel_regex):
+    """Fraction of the kernel's active cycles in which a SIMD's matrix unit is
+    busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) divided by the
+    SIMD count times the active cycles of one XCD (GRBM_GUI_ACTIVE / 8), per
+    dispatch, averaged over the dispatches matching kernel_regex."""
+    vals = _counter_means(pmc_dir)
+
+    def mean_for(counter):
+        v = [x for (k, c), xs in vals.items() if c == counter and re.search(kernel_regex, k) for x in xs]
+        return sum(v) / len(v) if v else None
+    busy, active = mean_for("SQ_VALU_MFMA_BUSY_CYCLES"), mean_for("GRBM_GUI_ACTIVE")
+    frac = busy / (SIMDS * active / XCDS) if busy is not None and active else None
+    return {"mfma_busy": frac, "mfma_busy_cycles": busy, "gui_active_cycles": active,
+            "kernel_regex": kernel_regex, "kernel_hash": kernel_source_hash("gemm16" in kernel_regex)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["stats", "pmc", "traffic"])
+    ap.add_argument("mode", choices=["stats", "pmc", "traffic", "mfma"])
     ap.add_argument("dirs", nargs="*")
     ap.add_argument("--command", default="")
     ap.add_argument("--fetch")
@@ -151,9 +172,10 @@ def main(argv=None):
     ap.add_argument("--kernel", default=r"grouped_gemm_kernel<double, 3")
     ap.add_argument("--out")
     a = ap.parse_args(argv)
-    if a.mode == "traffic":
+    if a.mode in ("traffic", "mfma"):
         import json
-        d = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernel)
+        d = (traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.kernel) if a.mode == "traffic"
+             else mfma_busy(a.dirs[0], a.kernel))
         d["command"] = a.command
         txt = json.dumps(d, indent=1)
         if a.out:

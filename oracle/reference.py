@@ -12,6 +12,7 @@ fp32 inputs are used as stored (already rounded) and upcast to float64.
 """
 from __future__ import annotations
 
+import time
 from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -106,9 +107,13 @@ def _op_col_panel(t: TLRTiles, op: str, c0: int, c1: int) -> np.ndarray:
 
 def gemm_reference_block(alpha: float, opA: str, A: TLRTiles, opB: str, B,
                          beta: float, C_block: Optional[np.ndarray],
-                         rows: Tuple[int, int], cols: Tuple[int, int]) -> np.ndarray:
+                         rows: Tuple[int, int], cols: Tuple[int, int],
+                         timings: Optional[dict] = None) -> np.ndarray:
     """Block C[rows[0]:rows[1], cols[0]:cols[1]] of the same product, built from
-    the row panel of op(A) and the column panel of op(B) only."""
+    the row panel of op(A) and the column panel of op(B) only.  ``timings``, if
+    given, accumulates the seconds spent rebuilding the panels
+    ("reconstruct_s") and multiplying ("matmul_s")."""
+    t0 = time.perf_counter()
     if isinstance(A, TLRTiles):
         Ap = _op_row_panel(A, opA, rows[0], rows[1])
     else:
@@ -119,9 +124,13 @@ def gemm_reference_block(alpha: float, opA: str, A: TLRTiles, opB: str, B,
     else:
         Bd = np.asarray(B)
         Bp = (Bd[:, cols[0]:cols[1]] if opB == "N" else Bd[cols[0]:cols[1], :].T).astype(np.float64)
+    t1 = time.perf_counter()
     out = alpha * (Ap @ Bp)
     if beta != 0.0:
         out = out + beta * np.asarray(C_block, dtype=np.float64)
+    if timings is not None:
+        timings["reconstruct_s"] = timings.get("reconstruct_s", 0.0) + (t1 - t0)
+        timings["matmul_s"] = timings.get("matmul_s", 0.0) + (time.perf_counter() - t1)
     return out
 
 

@@ -64,3 +64,17 @@ def test_traffic_scales_by_the_copy(tmp_path):
     assert math.isclose(t["write_bytes"], 500.0 * 1024)
     assert math.isclose(t["bytes_per_launch"], t["read_bytes"] + t["write_bytes"])
     assert t["kernel_hash"] == P.kernel_source_hash(False)
+
+
+def test_mfma_busy_fraction(tmp_path):
+    """Busy fraction = MFMA busy cycles summed over the 1024 SIMDs over (1024 x
+    one XCD's active cycles); GRBM_GUI_ACTIVE reads as the sum over 8 XCDs."""
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "void tlr::(anonymous namespace)::grouped_gemm_kernel<double, 3, 1, 8>(x)"
+    # 8e6 active cycles per XCD; every SIMD busy 6e6 of them -> 0.75
+    _write(str(tmp_path / "p" / "run_counter_collection.csv"), hdr,
+           [[k, "GRBM_GUI_ACTIVE", 8 * 8e6], [k, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 6e6],
+            ["other", "SQ_VALU_MFMA_BUSY_CYCLES", 1.0]])
+    m = P.mfma_busy(str(tmp_path / "p"), r"grouped_gemm_kernel<double, 3")
+    assert math.isclose(m["mfma_busy"], 0.75)
+    assert m["kernel_hash"] == P.kernel_source_hash(False)
