@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtlrgemm.so")
-SOURCES = ["planner.cpp", "abi.cpp", "executor.cpp", "noalloc.cpp", "gemm.hip", "gemm16.hip"]
+SOURCES = ["planner.cpp", "abi.cpp", "executor.cpp", "noalloc.cpp", "gemm.hip", "gemm16.hip", "compress.hip"]
 ARCH = "gfx950"
 
 

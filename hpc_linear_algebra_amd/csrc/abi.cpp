@@ -211,6 +211,30 @@ tlr_status tlr_gemm_execute_noalloc(tlr_plan *h, double alpha, const tlr_buffers
   })
 }
 
+tlr_status tlr_expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const int32_t *ranks_dev,
+                      const tlr_buffers *X, double alpha, double beta, void *C, int64_t ldc, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  TLR_GUARD({
+    return tlr::expand(dt, rows, cols, b, has_diag, ranks_dev, X, alpha, beta, C, ldc, workspace, workspace_bytes,
+                       stream);
+  })
+}
+
+tlr_status tlr_compress_workspace_bytes(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t max_rank,
+                                        size_t *bytes_out) {
+  TLR_GUARD({ return tlr::compress_workspace(dt, rows, cols, b, max_rank, bytes_out); })
+}
+
+tlr_status tlr_compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const void *X,
+                        int64_t ldx, double tol, int32_t max_rank, const void *omega, int32_t *ranks_out, void *diag,
+                        void *outer, void *inner, int64_t capacity, int32_t *info, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  TLR_GUARD({
+    return tlr::compress(dt, rows, cols, b, has_diag, X, ldx, tol, max_rank, omega, ranks_out, diag, outer, inner,
+                         capacity, info, workspace, workspace_bytes, stream);
+  })
+}
+
 tlr_status tlr_plan_profile(tlr_plan *h, int32_t max_executes) {
   if (!h) return tlr::fail(TLR_ERR_INVALID_ARG, "profile: null plan");
   TLR_GUARD({ return tlr::plan_profile(&h->p, max_executes); })

@@ -1,0 +1,660 @@
+// Dense <-> TLR conversions on the GPU: the pieces of a product whose output
+// C is itself TLR ("TLR Matrix Multiplication", "Introduction: TLR GEMM": A, B
+// and C may each be dense or TLR; the TLR-output cases extend the
+// dense-output product).
+//
+//   tlr_expand    C <- alpha X + beta C for a stored TLR operand X (every tile
+//                 U_ij V_ij^T, dense diagonal tiles), C dense.
+//   tlr_compress  a dense matrix to TLR: dense diagonal tiles, and every other
+//                 tile replaced by its truncated SVD of the smallest rank whose
+//                 discarded part meets a relative Frobenius tolerance.
+//
+// Compression of one tile X (s_i x s_j), with s = max_rank + 8 samples:
+//   Y  = X Omega          (s_i x s)  range sketch, Omega given by the caller
+//   Y  = Q R              Householder QR, Q kept (s_i x s)
+//   Bt = X^T Q            (s_j x s)  so that X ~ Q Bt^T = Q Q^T X
+//   Bt = Q2 R2            Householder QR, Q2 (s_j x s) and R2 (s x s) kept
+//   M  = R2^T             X ~ Q M Q2^T
+//   M J = W               one-sided (Hestenes) Jacobi: J orthogonal, the
+//                         columns of W orthogonal with norms sigma_k
+//   X ~ (Q W) (Q2 J)^T    U = Q W (columns of norm sigma), V = Q2 J
+// The energy Q misses is ||X||_F^2 - sum sigma_k^2; the kept rank r is the
+// smallest for which that energy plus the discarded sigma_k^2 stays within
+// (tol ||X||_F)^2.  The products run on the tile-batched MFMA GEMM; QR,
+// Jacobi, the rank scan and the packing are kernels of this file, one
+// workgroup per tile.  Ranks and factor offsets stay on the device: nothing
+// here synchronises with the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "tlr_plan.h"
+
+namespace tlr {
+
+namespace {
+
+constexpr int CT = 256;          // threads of the per-tile kernels (four wave64s)
+constexpr int OVERSAMPLE = 8;    // samples beyond max_rank
+constexpr int S_MAX = 64;        // largest sample count (max_rank <= 56)
+
+__device__ __forceinline__ int tile_rows(int64_t n, int64_t b, int i) { return (int)min<int64_t>(b, n - (int64_t)i * b); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup (every thread gets it).  red holds CT/64 slots.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T *red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  T s = 0;
+#pragma unroll
+  for (int k = 0; k < CT / 64; ++k) s += red[k];
+  return s;
+}
+
+// ||X_t||_F^2 of every tile.
+template <typename T>
+__global__ __launch_bounds__(CT) void tile_norms_kernel(const T *X, int64_t ldx, int qr, int qc, int64_t rows,
+                                                       int64_t cols, int64_t b, T *norms2) {
+  __shared__ T red[CT / 64];
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  const int si = tile_rows(rows, b, i), sj = tile_rows(cols, b, j);
+  const T *x = X + (int64_t)i * b + (int64_t)j * b * ldx;
+  T acc = 0;
+  for (int c = 0; c < sj; ++c)
+    for (int r = threadIdx.x; r < si; r += CT) {
+      const T v = x[r + (int64_t)c * ldx];
+      acc += v * v;
+    }
+  acc = block_sum(acc, red);
+  if (threadIdx.x == 0) norms2[t] = acc;
+}
+
+// Householder QR of every tile's m x n matrix A (column-major, leading dim
+// lda, tile t at A + t * stride), m = s_i (m_sel 0) or s_j (m_sel 1), n <=
+// S_MAX.  A is overwritten by the explicit Q (m x n, orthonormal columns;
+// columns beyond min(m, n) zero); with R != nullptr the n x n upper factor is
+// written to R + t * n * n (column-major, zero below the diagonal).
+// Reflector k: v = x - alpha e_k with alpha = -sign(x_k) ||x||, H = I - beta v v^T,
+// beta = 2 / (v^T v), v kept in column k (rows >= k) until Q is formed.
+template <typename T>
+__global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
+                                                     int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
+                                                     int skip_diag) {
+  __shared__ T red[CT / 64];
+  __shared__ T beta_s[S_MAX];
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  if (skip_diag && i == j) return;
+  const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
+  T *a = A + (int64_t)t * stride;
+  T *rr = R ? R + (int64_t)t * n * n : nullptr;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kmax = min(m, n);
+  if (rr)
+    for (int e = tid; e < n * n; e += CT) rr[e] = 0;
+  for (int k = 0; k < kmax; ++k) {
+    T tail = 0;
+    for (int r = k + 1 + tid; r < m; r += CT) {
+      const T v = a[r + (int64_t)k * lda];
+      tail += v * v;
+    }
+    tail = block_sum(tail, red);
+    const T x0 = a[k + (int64_t)k * lda];
+    const T nrm = sqrt(tail + x0 * x0);
+    const T alpha = x0 >= T(0) ? -nrm : nrm;
+    const T v0 = x0 - alpha;
+    const T vtv = tail + v0 * v0;
+    const T beta = vtv > T(0) ? T(2) / vtv : T(0);
+    __syncthreads();   // every thread has read x0 before it is replaced
+    if (tid == 0) {
+      a[k + (int64_t)k * lda] = v0;
+      beta_s[k] = beta;
+      if (rr) rr[k + (int64_t)k * n] = alpha;
+    }
+    __syncthreads();
+    // trailing columns: A[k:m, c] -= beta (v^T A[k:m, c]) v, one wave per column
+    for (int c = k + 1 + wave; c < n; c += CT / 64) {
+      T s = 0;
+      for (int r = k + lane; r < m; r += 64) s += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
+      s = wave_sum(s);
+      const T f = beta * s;
+      for (int r = k + lane; r < m; r += 64) a[r + (int64_t)c * lda] -= f * a[r + (int64_t)k * lda];
+      if (rr && lane == 0) rr[k + (int64_t)c * n] = a[k + (int64_t)c * lda];
+    }
+    __syncthreads();
+  }
+  // Q = H_0 ... H_{kmax-1} applied to the first n columns of the identity,
+  // formed backwards in place; columns past kmax are zero
+  for (int c = kmax; c < n; ++c)
+    for (int r = tid; r < m; r += CT) a[r + (int64_t)c * lda] = 0;
+  __syncthreads();
+  for (int k = kmax - 1; k >= 0; --k) {
+    const T beta = beta_s[k];
+    for (int c = k + 1 + wave; c < n; c += CT / 64) {
+      // rows < k+1 of column c are zero here, so the sum starts at k + 1
+      T s = 0;
+      for (int r = k + 1 + lane; r < m; r += 64) s += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
+      s = wave_sum(s);
+      const T f = beta * s;
+      // row k of column c becomes -f v0
+      if (lane == 0) a[k + (int64_t)c * lda] = -f * a[k + (int64_t)k * lda];
+      for (int r = k + 1 + lane; r < m; r += 64) a[r + (int64_t)c * lda] -= f * a[r + (int64_t)k * lda];
+    }
+    __syncthreads();
+    const T v0 = a[k + (int64_t)k * lda];
+    __syncthreads();   // v0 read by every thread before column k is rewritten
+    for (int r = tid; r < m; r += CT) {
+      const T vr = a[r + (int64_t)k * lda];
+      a[r + (int64_t)k * lda] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
+    }
+    __syncthreads();
+  }
+}
+
+// One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
+// then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
+// sigma_k) to Wout + t n n, J to Jout + t n n, the columns in decreasing
+// order of sigma to perm + t n, the rank to ranks[t] (0 for a skipped
+// diagonal tile) and flags[t] = 1 when the tolerance was not met within
+// max_rank columns (the rank is then max_rank).
+template <typename T>
+__global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T *Jout, int32_t *perm,
+                                                        int32_t *ranks, int32_t *flags, const T *norms2, int qr,
+                                                        int qc, int n, int max_rank, T tol, T conv,
+                                                        int skip_diag) {
+  __shared__ T Ms[S_MAX * S_MAX];
+  __shared__ T Js[S_MAX * S_MAX];
+  __shared__ T sig2[S_MAX];
+  __shared__ int order[S_MAX];
+  __shared__ T offw[CT / 64];
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (skip_diag && i == j) {
+    if (tid == 0) {
+      ranks[t] = 0;
+      flags[t] = 0;
+    }
+    return;
+  }
+  const T *rt = R + (int64_t)t * n * n;
+  for (int e = tid; e < S_MAX * S_MAX; e += CT) {
+    const int r = e % S_MAX, c = e / S_MAX;
+    Ms[e] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
+    Js[e] = r == c ? T(1) : T(0);
+  }
+  __syncthreads();
+  const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
+  const int npairs = np / 2;
+  for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
+    T off = 0;
+    for (int round = 0; round < np - 1; ++round) {
+      for (int pk = wave; pk < npairs; pk += CT / 64) {
+        // round-robin: position 0 holds player 0, position x >= 1 player 1 + (x - 1 + round) mod (np - 1)
+        auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (np - 1); };
+        int p = player(pk), q = player(np - 1 - pk);
+        if (p > q) { const int x = p; p = q; q = x; }
+        T al = 0, be = 0, ga = 0;
+        for (int r = lane; r < np; r += 64) {
+          const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
+          al += mp * mp;
+          be += mq * mq;
+          ga += mp * mq;
+        }
+        al = wave_sum(al);
+        be = wave_sum(be);
+        ga = wave_sum(ga);
+        const T den = sqrt(al * be);
+        if (den > T(0) && fabs(ga) > conv * den) {
+          off = fmax(off, fabs(ga) / den);
+          const T zeta = (be - al) / (T(2) * ga);
+          const T tt = (zeta >= T(0) ? T(1) : T(-1)) / (fabs(zeta) + sqrt(T(1) + zeta * zeta));
+          const T cs = T(1) / sqrt(T(1) + tt * tt), sn = cs * tt;
+          for (int r = lane; r < np; r += 64) {
+            const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
+            Ms[r + p * S_MAX] = cs * mp - sn * mq;
+            Ms[r + q * S_MAX] = sn * mp + cs * mq;
+            const T jp = Js[r + p * S_MAX], jq = Js[r + q * S_MAX];
+            Js[r + p * S_MAX] = cs * jp - sn * jq;
+            Js[r + q * S_MAX] = sn * jp + cs * jq;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (lane == 0) offw[wave] = off;
+    __syncthreads();
+    T mx = 0;
+#pragma unroll
+    for (int w = 0; w < CT / 64; ++w) mx = fmax(mx, offw[w]);
+    __syncthreads();
+    if (mx <= conv) break;
+  }
+  // column norms, the order of decreasing sigma (ties by column index)
+  for (int c = wave; c < n; c += CT / 64) {
+    T s = 0;
+    for (int r = lane; r < np; r += 64) s += Ms[r + c * S_MAX] * Ms[r + c * S_MAX];
+    s = wave_sum(s);
+    if (lane == 0) sig2[c] = s;
+  }
+  __syncthreads();
+  for (int c = tid; c < n; c += CT) {
+    int pos = 0;
+    for (int d = 0; d < n; ++d) pos += (sig2[d] > sig2[c]) || (sig2[d] == sig2[c] && d < c);
+    order[pos] = c;
+  }
+  __syncthreads();
+  T *wt = Wout + (int64_t)t * n * n;
+  T *jt = Jout + (int64_t)t * n * n;
+  for (int e = tid; e < n * n; e += CT) {
+    const int r = e % n, c = e / n;
+    wt[e] = Ms[r + c * S_MAX];
+    jt[e] = Js[r + c * S_MAX];
+  }
+  for (int c = tid; c < n; c += CT) perm[(int64_t)t * n + c] = order[c];
+  if (tid == 0) {
+    const T x2 = norms2[t];
+    T captured = 0;
+    for (int c = 0; c < n; ++c) captured += sig2[c];
+    const T limit = tol * tol * x2;
+    T tail = x2 > captured ? x2 - captured : T(0);
+    int r = n;
+    bool met = tail <= limit;
+    if (met) {
+      for (int pos = n - 1; pos >= 0; --pos) {
+        const T s2 = sig2[order[pos]];
+        if (tail + s2 <= limit) {
+          tail += s2;
+          r = pos;
+        } else {
+          break;
+        }
+      }
+    }
+    int fl = met ? 0 : 1;
+    if (r > max_rank) {
+      r = max_rank;
+      fl = 1;
+    }
+    ranks[t] = r;
+    flags[t] = fl;
+  }
+}
+
+// Prefix sums of the ranks (one thread): outer offsets in tile-row order,
+// inner offsets in tile-column order; info[0] = columns in all, info[1] =
+// tiles flagged, info[2] = 1 when the columns exceed the capacity.
+__global__ void rank_scan_kernel(const int32_t *ranks, const int32_t *flags, int qr, int qc, int skip_diag,
+                                 int64_t *ooff, int64_t *ioff, int64_t capacity, int32_t *info) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t acc = 0;
+  for (int i = 0; i < qr; ++i)
+    for (int j = 0; j < qc; ++j) {
+      const int t = i + j * qr;
+      ooff[t] = acc;
+      if (!(skip_diag && i == j)) acc += ranks[t];
+    }
+  const int64_t total = acc;
+  acc = 0;
+  int nflag = 0;
+  for (int j = 0; j < qc; ++j)
+    for (int i = 0; i < qr; ++i) {
+      const int t = i + j * qr;
+      ioff[t] = acc;
+      if (!(skip_diag && i == j)) {
+        acc += ranks[t];
+        nflag += flags[t];
+      }
+    }
+  info[0] = (int32_t)min<int64_t>(total, 0x7fffffff);
+  info[1] = nflag;
+  info[2] = total > capacity ? 1 : 0;
+}
+
+// Packed output: kept column k of tile t goes to column ooff[t] + k of outer
+// (U = Q W, the first s_i rows, leading dim b) and ioff[t] + k of inner
+// (V = Q2 J, s_j rows); diagonal tiles are copied into their slots.  Nothing
+// is written when the columns exceed the capacity.
+template <typename T>
+__global__ __launch_bounds__(CT) void pack_kernel(const T *X, int64_t ldx, const T *Uf, const T *Vf, int64_t fstride,
+                                                 const int32_t *perm, const int32_t *ranks, const int64_t *ooff,
+                                                 const int64_t *ioff, const int32_t *info, int qr, int qc,
+                                                 int64_t rows, int64_t cols, int64_t b, int n, int has_diag,
+                                                 T *outer, T *inner, T *diag, int32_t *ranks_out) {
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  const int si = tile_rows(rows, b, i), sj = tile_rows(cols, b, j);
+  if (has_diag && i == j) {
+    if (threadIdx.x == 0) ranks_out[t] = 0;
+    const T *x = X + (int64_t)i * b + (int64_t)j * b * ldx;
+    T *d = diag + (int64_t)i * b * b;
+    for (int e = threadIdx.x; e < si * si; e += CT) {
+      const int r = e % si, c = e / si;
+      d[r + (int64_t)c * b] = x[r + (int64_t)c * ldx];
+    }
+    return;
+  }
+  const int r = ranks[t];
+  if (threadIdx.x == 0) ranks_out[t] = r;
+  if (info[2]) return;
+  const T *uf = Uf + (int64_t)t * fstride;
+  const T *vf = Vf + (int64_t)t * fstride;
+  for (int k = 0; k < r; ++k) {
+    const int src = perm[(int64_t)t * n + k];
+    T *uo = outer + (ooff[t] + k) * b;
+    T *vo = inner + (ioff[t] + k) * b;
+    for (int e = threadIdx.x; e < si; e += CT) uo[e] = uf[e + (int64_t)src * b];
+    for (int e = threadIdx.x; e < sj; e += CT) vo[e] = vf[e + (int64_t)src * b];
+  }
+}
+
+// ---- expansion of a stored TLR operand --------------------------------------
+
+// Column offsets of every tile's factors from the device rank table (one thread).
+__global__ void factor_offsets_kernel(const int32_t *ranks, int qr, int qc, int has_diag, int64_t *ooff,
+                                      int64_t *ioff) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t acc = 0;
+  for (int i = 0; i < qr; ++i)
+    for (int j = 0; j < qc; ++j) {
+      ooff[i + j * qr] = acc;
+      if (!(has_diag && i == j)) acc += ranks[i + j * qr];
+    }
+  acc = 0;
+  for (int j = 0; j < qc; ++j)
+    for (int i = 0; i < qr; ++i) {
+      ioff[i + j * qr] = acc;
+      if (!(has_diag && i == j)) acc += ranks[i + j * qr];
+    }
+}
+
+// C[64 x 64 block of tile t] <- alpha X_t + beta C (C read only when beta != 0):
+// X_t = U V^T for an off-diagonal tile (rank-k chunks of 16 staged in LDS),
+// the dense slot for a diagonal tile.
+constexpr int EB = 64, EK = 16;
+template <typename T>
+__global__ __launch_bounds__(CT) void expand_kernel(const int32_t *ranks, const int64_t *ooff, const int64_t *ioff,
+                                                   const T *outer, const T *inner, const T *diag, int qr, int qc,
+                                                   int64_t rows, int64_t cols, int64_t b, int has_diag, T alpha,
+                                                   T beta, T *C, int64_t ldc, int blocks_per_tile, int bpd) {
+  __shared__ T Us[EK][EB + 1];
+  __shared__ T Vs[EK][EB + 1];
+  const int t = blockIdx.x / blocks_per_tile, blk = blockIdx.x - t * blocks_per_tile;
+  const int i = t % qr, j = t / qr;
+  const int si = tile_rows(rows, b, i), sj = tile_rows(cols, b, j);
+  const int r0 = (blk % bpd) * EB, c0 = (blk / bpd) * EB;
+  if (r0 >= si || c0 >= sj) return;
+  const int tid = threadIdx.x;
+  const int tr = tid % 16, tc = tid / 16;       // 4 x 4 outputs per thread: rows r0 + tr + 16a, cols c0 + tc + 16c
+  T acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0;
+  if (has_diag && i == j) {
+    const T *d = diag + (int64_t)i * b * b;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int rr = r0 + tr + 16 * a, cc = c0 + tc + 16 * c;
+        if (rr < si && cc < sj) acc[a][c] = d[rr + (int64_t)cc * b];
+      }
+  } else {
+    const int rk = ranks[t];
+    const T *u = outer + ooff[t] * b;
+    const T *v = inner + ioff[t] * b;
+    for (int k0 = 0; k0 < rk; k0 += EK) {
+      __syncthreads();
+      for (int e = tid; e < EK * EB; e += CT) {
+        const int kk = e / EB, x = e % EB;
+        const bool okk = k0 + kk < rk;
+        Us[kk][x] = (okk && r0 + x < si) ? u[(int64_t)(k0 + kk) * b + r0 + x] : T(0);
+        Vs[kk][x] = (okk && c0 + x < sj) ? v[(int64_t)(k0 + kk) * b + c0 + x] : T(0);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < EK; ++kk)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[a][c] += Us[kk][tr + 16 * a] * Vs[kk][tc + 16 * c];
+    }
+  }
+  const int64_t base = (int64_t)i * b + (int64_t)j * b * ldc;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int rr = r0 + tr + 16 * a, cc = c0 + tc + 16 * c;
+      if (rr < si && cc < sj) {
+        T *p = C + base + rr + (int64_t)cc * ldc;
+        T y = alpha * acc[a][c];
+        if (beta != T(0)) y += beta * *p;
+        *p = y;
+      }
+    }
+}
+
+template <typename T>
+T *as(void *p) { return static_cast<T *>(p); }
+
+struct CompressLayout {
+  int qr = 0, qc = 0, s = 0;
+  int64_t ntile = 0;
+  size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, ooff = 0,
+         ioff = 0, total = 0;
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+CompressLayout compress_layout(int64_t rows, int64_t cols, int64_t b, int max_rank, size_t es) {
+  CompressLayout L;
+  L.qr = (int)((rows + b - 1) / b);
+  L.qc = (int)((cols + b - 1) / b);
+  L.s = max_rank + OVERSAMPLE;
+  L.ntile = (int64_t)L.qr * L.qc;
+  const size_t panel = al256((size_t)L.ntile * b * L.s * es), core = al256((size_t)L.ntile * L.s * L.s * es);
+  size_t o = 0;
+  L.y = o; o += panel;
+  L.bt = o; o += panel;
+  L.uf = o; o += panel;
+  L.vf = o; o += panel;
+  L.r2 = o; o += core;
+  L.w = o; o += core;
+  L.j = o; o += core;
+  L.norms = o; o += al256((size_t)L.ntile * es);
+  L.perm = o; o += al256((size_t)L.ntile * L.s * 4);
+  L.ranks = o; o += al256((size_t)L.ntile * 4);
+  L.flags = o; o += al256((size_t)L.ntile * 4);
+  L.ooff = o; o += al256((size_t)L.ntile * 8);
+  L.ioff = o; o += al256((size_t)L.ntile * 8);
+  L.total = o;
+  return L;
+}
+
+tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t max_rank) {
+  if (dt == TLR_F16 || dt == TLR_BF16) return fail(TLR_ERR_UNSUPPORTED, "compress: 16-bit types are not provided");
+  if (dt != TLR_F32 && dt != TLR_F64) return fail(TLR_ERR_INVALID_ARG, "compress: bad dtype");
+  if (rows < 0 || cols < 0 || b < 1) return fail(TLR_ERR_INVALID_ARG, "compress: bad dimensions or tile size");
+  if (rows > 0x7fffffff || cols > 0x7fffffff || b > 4096) return fail(TLR_ERR_INVALID_ARG, "compress: dimensions too large");
+  if (max_rank < 0 || max_rank + OVERSAMPLE > S_MAX)
+    return fail(TLR_ERR_UNSUPPORTED, "compress: max_rank must lie in [0, " + std::to_string(S_MAX - OVERSAMPLE) + "]");
+  return TLR_OK;
+}
+
+template <typename T>
+T conv_tol() { return sizeof(T) == 8 ? T(1e-14) : T(1e-6f); }
+
+#define CHECK_LAUNCH(what)                                                                     \
+  do {                                                                                         \
+    hipError_t e_ = hipGetLastError();                                                         \
+    if (e_ != hipSuccess) return fail(TLR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename T>
+tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const void *X, int64_t ldx, double tol,
+                      int max_rank, const void *omega, int32_t *ranks_out, void *diag, void *outer, void *inner,
+                      int64_t capacity, int32_t *info, void *ws, const CompressLayout &L, hipStream_t s) {
+  const tlr_dtype dt = sizeof(T) == 8 ? TLR_F64 : TLR_F32;
+  char *w = static_cast<char *>(ws);
+  const int n = L.s;
+  const int nt = (int)L.ntile;
+  const int skip = has_diag ? 1 : 0;
+  T *norms = as<T>(w + L.norms);
+  hipLaunchKernelGGL(tile_norms_kernel<T>, dim3(nt), dim3(CT), 0, s, static_cast<const T *>(X), ldx, L.qr, L.qc, rows,
+                     cols, b, norms);
+  CHECK_LAUNCH("tile norms");
+  Bases bases;
+  for (auto &p : bases.p) p = nullptr;
+  bases.p[BASE_A_OUTER] = X;
+  bases.p[BASE_B_OUTER] = omega;
+  bases.p[BASE_WS] = ws;
+  const int64_t es = sizeof(T);
+  auto wsoff = [&](size_t byte_off) { return (int64_t)(byte_off / es); };
+  const int64_t panel = b * n;   // elements per tile of a b x s panel
+  auto ta = [](int64_t off, int64_t f_ro, int64_t f_co, int64_t f_t, int64_t ld, uint8_t base, uint8_t trans) {
+    TileAddr a;
+    a.off = off; a.f_ro = f_ro; a.f_co = f_co; a.f_t = f_t; a.ld = (int32_t)ld; a.base = base; a.trans = trans;
+    return a;
+  };
+  auto gemm = [&](int m_sel, int k_sel, TileAddr A, TileAddr B, TileAddr C, int mode) -> tlr_status {
+    TileGemm g;
+    g.qr = L.qr; g.qc = L.qc; g.rows = rows; g.cols = cols; g.b = b; g.skip_diag = skip;
+    g.m_sel = m_sel; g.k_sel = k_sel; g.n = n; g.n_fixed = n;
+    g.a = A; g.bop = B; g.c = C;
+    const int e = launch_tile_gemm(dt, mode, g, bases, s);
+    if (e) return fail(TLR_ERR_HIP, std::string("tile GEMM launch: ") + hipGetErrorString((hipError_t)e));
+    return TLR_OK;
+  };
+  // pair loads need even sizes, offsets and leading dimensions throughout
+  const bool even = b % 2 == 0 && rows % 2 == 0 && cols % 2 == 0 && ldx % 2 == 0 && n % 2 == 0 &&
+                    reinterpret_cast<uintptr_t>(X) % (2 * es) == 0 && reinterpret_cast<uintptr_t>(omega) % (2 * es) == 0;
+  // 1. Y_t = X_t Omega                       (s_i x s)
+  tlr_status st = gemm(0, 1, ta(0, 1, ldx, 0, ldx, BASE_A_OUTER, 0), ta(0, 0, 0, 0, b, BASE_B_OUTER, 0),
+                       ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
+  if (st != TLR_OK) return st;
+  // 2. Y_t = Q R, Q kept in place
+  hipLaunchKernelGGL(qr_tiles_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.y), (int)b, panel, (T *)nullptr, L.qr,
+                     L.qc, rows, cols, b, 0, n, skip);
+  CHECK_LAUNCH("QR of the sketches");
+  // 3. Bt_t = X_t^T Q_t                      (s_j x s)
+  st = gemm(1, 0, ta(0, 1, ldx, 0, ldx, BASE_A_OUTER, 1), ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0),
+            ta(wsoff(L.bt), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_K : LOAD_SINGLE);
+  if (st != TLR_OK) return st;
+  // 4. Bt_t = Q2 R2
+  hipLaunchKernelGGL(qr_tiles_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.bt), (int)b, panel, as<T>(w + L.r2),
+                     L.qr, L.qc, rows, cols, b, 1, n, skip);
+  CHECK_LAUNCH("QR of the projections");
+  // 5. Jacobi on M = R2^T, ranks
+  hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.r2), as<T>(w + L.w),
+                     as<T>(w + L.j), as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
+                     norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
+  CHECK_LAUNCH("Jacobi SVD");
+  // 6. U_t = Q_t W_t, V_t = Q2_t J_t        (s_i x s, s_j x s)
+  st = gemm(0, 2, ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), ta(wsoff(L.w), 0, 0, (int64_t)n * n, n, BASE_WS, 0),
+            ta(wsoff(L.uf), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
+  if (st != TLR_OK) return st;
+  st = gemm(1, 2, ta(wsoff(L.bt), 0, 0, panel, b, BASE_WS, 0), ta(wsoff(L.j), 0, 0, (int64_t)n * n, n, BASE_WS, 0),
+            ta(wsoff(L.vf), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
+  if (st != TLR_OK) return st;
+  // 7. offsets, 8. packed factors and diagonal slots
+  hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(64), 0, s, as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
+                     L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff), capacity, info);
+  CHECK_LAUNCH("rank scan");
+  hipLaunchKernelGGL(pack_kernel<T>, dim3(nt), dim3(CT), 0, s, static_cast<const T *>(X), ldx, as<T>(w + L.uf),
+                     as<T>(w + L.vf), panel, as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks),
+                     as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff), info, L.qr, L.qc, rows, cols, b, n, skip,
+                     static_cast<T *>(outer), static_cast<T *>(inner), static_cast<T *>(diag), ranks_out);
+  CHECK_LAUNCH("pack");
+  return TLR_OK;
+}
+
+template <typename T>
+tlr_status expand_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const int32_t *ranks, const tlr_buffers *X,
+                    double alpha, double beta, void *C, int64_t ldc, void *ws, hipStream_t s) {
+  const int qr = (int)((rows + b - 1) / b), qc = (int)((cols + b - 1) / b);
+  const int64_t nt = (int64_t)qr * qc;
+  int64_t *ooff = static_cast<int64_t *>(ws);
+  int64_t *ioff = ooff + nt;
+  hipLaunchKernelGGL(factor_offsets_kernel, dim3(1), dim3(64), 0, s, ranks, qr, qc, has_diag, ooff, ioff);
+  CHECK_LAUNCH("factor offsets");
+  const int bpd = (int)((b + EB - 1) / EB);
+  const int bpt = bpd * bpd;
+  hipLaunchKernelGGL(expand_kernel<T>, dim3((unsigned)(nt * bpt)), dim3(CT), 0, s, ranks, ooff, ioff,
+                     static_cast<const T *>(X->outer), static_cast<const T *>(X->inner),
+                     static_cast<const T *>(X->diag), qr, qc, rows, cols, b, has_diag, (T)alpha, (T)beta,
+                     static_cast<T *>(C), ldc, bpt, bpd);
+  CHECK_LAUNCH("expand");
+  return TLR_OK;
+}
+
+}  // namespace
+
+tlr_status compress_workspace(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t max_rank, size_t *bytes) {
+  if (!bytes) return fail(TLR_ERR_INVALID_ARG, "compress: null output");
+  tlr_status st = check_compress_args(dt, rows, cols, b, max_rank);
+  if (st != TLR_OK) return st;
+  *bytes = compress_layout(rows, cols, b, max_rank, dt == TLR_F64 ? 8 : 4).total;
+  return TLR_OK;
+}
+
+tlr_status compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const void *X, int64_t ldx,
+                    double tol, int32_t max_rank, const void *omega, int32_t *ranks_out, void *diag, void *outer,
+                    void *inner, int64_t capacity, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  tlr_status st = check_compress_args(dt, rows, cols, b, max_rank);
+  if (st != TLR_OK) return st;
+  if (has_diag && rows != cols) return fail(TLR_ERR_INVALID_ARG, "compress: a dense diagonal needs a square matrix");
+  if (!(tol >= 0.0)) return fail(TLR_ERR_INVALID_ARG, "compress: tolerance must be >= 0");
+  if (ldx < std::max<int64_t>(1, rows) || ldx >= ((int64_t)1 << 21))
+    return fail(TLR_ERR_INVALID_ARG, "compress: ldx must lie in [rows, 2^21)");
+  if (capacity < 0) return fail(TLR_ERR_INVALID_ARG, "compress: negative capacity");
+  if (rows == 0 || cols == 0) return TLR_OK;
+  const size_t es = dt == TLR_F64 ? 8 : 4;
+  const CompressLayout L = compress_layout(rows, cols, b, max_rank, es);
+  if (!X || !omega || !ranks_out || !info || !ws || (has_diag && !diag) || (capacity > 0 && (!outer || !inner)))
+    return fail(TLR_ERR_INVALID_ARG, "compress: null buffer");
+  if (ws_bytes < L.total) return fail(TLR_ERR_WORKSPACE, "compress: workspace smaller than tlr_compress_workspace_bytes");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(TLR_ERR_INVALID_ARG, "compress: workspace not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == TLR_F64)
+    return compress_t<double>(rows, cols, b, has_diag, X, ldx, tol, max_rank, omega, ranks_out, diag, outer, inner,
+                              capacity, info, ws, L, s);
+  return compress_t<float>(rows, cols, b, has_diag, X, ldx, tol, max_rank, omega, ranks_out, diag, outer, inner,
+                           capacity, info, ws, L, s);
+}
+
+tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const int32_t *ranks,
+                  const tlr_buffers *X, double alpha, double beta, void *C, int64_t ldc, void *ws, size_t ws_bytes,
+                  void *stream) {
+  if (dt == TLR_F16 || dt == TLR_BF16) return fail(TLR_ERR_UNSUPPORTED, "expand: 16-bit types are not provided");
+  if (dt != TLR_F32 && dt != TLR_F64) return fail(TLR_ERR_INVALID_ARG, "expand: bad dtype");
+  if (rows < 0 || cols < 0 || b < 1) return fail(TLR_ERR_INVALID_ARG, "expand: bad dimensions or tile size");
+  if (has_diag && rows != cols) return fail(TLR_ERR_INVALID_ARG, "expand: a dense diagonal needs a square matrix");
+  if (ldc < std::max<int64_t>(1, rows)) return fail(TLR_ERR_INVALID_ARG, "expand: ldc smaller than rows");
+  if (rows == 0 || cols == 0) return TLR_OK;
+  if (!C || !X || !ranks || !ws) return fail(TLR_ERR_INVALID_ARG, "expand: null buffer");
+  if (has_diag && !X->diag) return fail(TLR_ERR_INVALID_ARG, "expand: null diagonal");
+  const int64_t nt = ((rows + b - 1) / b) * ((cols + b - 1) / b);
+  if (ws_bytes < (size_t)(16 * nt)) return fail(TLR_ERR_WORKSPACE, "expand: workspace below 16 bytes per tile");
+  if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(TLR_ERR_INVALID_ARG, "expand: workspace not 8-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == TLR_F64) return expand_t<double>(rows, cols, b, has_diag, ranks, X, alpha, beta, C, ldc, ws, s);
+  return expand_t<float>(rows, cols, b, has_diag, ranks, X, alpha, beta, C, ldc, ws, s);
+}
+
+}  // namespace tlr

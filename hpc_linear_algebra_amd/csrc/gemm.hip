@@ -544,6 +544,48 @@ void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int m
   gemm_block<T, MODE, 8>(t, mtile * KBM, ntile * Blk<8>::KBN, nullptr, bases, alpha, beta, cscale);
 }
 
+// One task per tile of a regular grid (TileGemm): workgroup x = (tile, row
+// block); the tile's task (N <= 128, one block column) is built from the
+// tile's extents.  C = A B, no alpha / beta.
+template <typename T, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void tile_gemm_kernel(TileGemm g, Bases bases, int mb_per_tile) {
+  const int t = blockIdx.x / mb_per_tile, mb = blockIdx.x - t * mb_per_tile;
+  if (t >= g.qr * g.qc) return;
+  const int i = t % g.qr, j = t / g.qr;
+  if (g.skip_diag && i == j) return;
+  const int64_t ro = (int64_t)i * g.b, co = (int64_t)j * g.b;
+  const int si = (int)min<int64_t>(g.b, g.rows - ro), sj = (int)min<int64_t>(g.b, g.cols - co);
+  const int M = g.m_sel == 0 ? si : (g.m_sel == 1 ? sj : g.n_fixed);
+  const int K = g.k_sel == 0 ? si : (g.k_sel == 1 ? sj : g.n_fixed);
+  if (mb * KBM >= M) return;
+  auto opnd = [&](const TileAddr &x) {
+    DevOperand o;
+    o.off = x.off + ro * x.f_ro + co * x.f_co + (int64_t)t * x.f_t;
+    o.ld = x.ld;
+    o.base = x.base;
+    o.trans = x.trans;
+    o.flags = 0;
+    return o;
+  };
+  DevTask task;
+  task.M = M;
+  task.N = g.n;
+  task.c_off = g.c.off + ro * g.c.f_ro + co * g.c.f_co + (int64_t)t * g.c.f_t;
+  task.ctab = -1;
+  task.ldc = g.c.ld;
+  task.c_base = g.c.base;
+  task.final_ = 0;
+  task.nseg = K > 0 ? 1 : 0;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  task.flags = (task.c_off % VEC == 0 && task.ldc % VEC == 0) ? TASK_VEC : 0;
+  task.seg[0].a = opnd(g.a);
+  task.seg[0].b = opnd(g.bop);
+  task.seg[0].K = K;
+  task.seg[0].pad = 0;
+  gemm_block<T, MODE, 8>(task, mb * KBM, 0, nullptr, bases, T(1), T(0), T(0));
+}
+
 template <typename T>
 __global__ void scale_kernel(T *C, int64_t m, int64_t n, int64_t ldc, T beta) {
   const int64_t total = m * n;
@@ -646,6 +688,29 @@ int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &base
     launch_single_t<double>(mode, (unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
   else
     launch_single_t<float>(mode, (unsigned)(per * 8), s, task, bases, alpha, beta, mt, nt, per);
+  return (int)hipGetLastError();
+}
+
+int launch_tile_gemm(tlr_dtype dt, int mode, const TileGemm &g, const Bases &bases, void *stream) {
+  if (dt != TLR_F64 && dt != TLR_F32) return (int)hipErrorInvalidValue;
+  if (g.n <= 0 || g.n > Blk<8>::KBN || g.qr <= 0 || g.qc <= 0) return g.qr <= 0 || g.qc <= 0 ? 0 : (int)hipErrorInvalidValue;
+  const int64_t maxm = g.m_sel == 2 ? g.n_fixed : g.b;
+  const int mb = (int)((maxm + KBM - 1) / KBM);
+  if (mb <= 0) return 0;
+  const dim3 grid((unsigned)((int64_t)g.qr * g.qc * mb)), block(NT);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define TLR_TILE_LAUNCH(TT)                                                                                    \
+  do {                                                                                                         \
+    if (mode == LOAD_PAIR_M)                                                                                   \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_M>), grid, block, 0, s, g, bases, mb);                \
+    else if (mode == LOAD_PAIR_K)                                                                              \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_K>), grid, block, 0, s, g, bases, mb);                \
+    else                                                                                                       \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_SINGLE>), grid, block, 0, s, g, bases, mb);                \
+  } while (0)
+  if (dt == TLR_F64) TLR_TILE_LAUNCH(double);
+  else TLR_TILE_LAUNCH(float);
+#undef TLR_TILE_LAUNCH
   return (int)hipGetLastError();
 }
 

@@ -126,6 +126,27 @@ struct Plan {
   ~Plan();
 };
 
+// One GEMM per tile of a regular tile grid, every tile of a launch the same
+// kind (the per-tile products of dense-to-TLR compression).  Tile (i, j) has
+// s_i = min(b, rows - i b) rows and s_j = min(b, cols - j b) columns; its
+// index is t = i + j qr.  Each workgroup derives its tile's task from its own
+// index, so no descriptor table is needed.  An operand's element offset is
+//   off + (i b) f_ro + (j b) f_co + t f_t.
+struct TileAddr {
+  int64_t off, f_ro, f_co, f_t;
+  int32_t ld;
+  uint8_t base, trans;        // base id (tlr_desc.h); trans as in DevOperand
+};
+struct TileGemm {
+  int32_t qr, qc;
+  int64_t rows, cols, b;
+  int32_t skip_diag;          // 1: tiles with i == j do nothing
+  int32_t m_sel, k_sel;       // extent of M / K: 0 = s_i, 1 = s_j, 2 = n_fixed
+  int32_t n;                  // N of every tile (<= 128)
+  int32_t n_fixed;
+  TileAddr a, bop, c;         // A (M x K), B (K x N), C (M x N, trans ignored)
+};
+
 // Planner (host only).
 tlr_status build_plan(tlr_dtype dt, tlr_op opA, const tlr_shape *A, tlr_op opB,
                       const tlr_shape *B, int64_t dense_rows, int64_t dense_cols,
@@ -140,6 +161,13 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
 tlr_status plan_execute_noalloc(Plan *p, double alpha, const tlr_buffers *A, const tlr_buffers *B,
                                 const void *B_dense, int64_t ldb, double beta, void *C, int64_t ldc,
                                 void *const *streams, int n_streams);
+tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const int32_t *ranks,
+                  const tlr_buffers *X, double alpha, double beta, void *C, int64_t ldc, void *ws, size_t ws_bytes,
+                  void *stream);
+tlr_status compress_workspace(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t max_rank, size_t *bytes);
+tlr_status compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const void *X, int64_t ldx,
+                    double tol, int32_t max_rank, const void *omega, int32_t *ranks_out, void *diag, void *outer,
+                    void *inner, int64_t capacity, int32_t *info, void *ws, size_t ws_bytes, void *stream);
 tlr_status plan_profile(Plan *p, int max_exec);
 tlr_status plan_profile_read(Plan *p, double *stage_ms, double *launch_ms, int32_t *execs);
 void plan_release_device(Plan *p);
@@ -155,6 +183,7 @@ int launch_single(tlr_dtype dt, int mode, const DevTask &task, const Bases &base
                   double beta, void *stream);
 int launch_scale(tlr_dtype dt, void *C, int64_t m, int64_t n, int64_t ldc, double beta,
                  void *stream);
+int launch_tile_gemm(tlr_dtype dt, int mode, const TileGemm &g, const Bases &bases, void *stream);
 // 16-bit types (gemm16.hip); launch_grouped and launch_scale forward to these.
 int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, const DevTile *tiles,
                      int64_t n_tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta,

@@ -51,6 +51,14 @@ class DeviceTLR:
     def buffers(self) -> T.tlr_buffers:
         return T.buffers(_ptr(self.diag), _ptr(self.outer), _ptr(self.inner))
 
+    def ranks_device(self) -> torch.Tensor:
+        """The stored ranks as a device int32 array, column-major q_r x q_c (as
+        tlr_expand reads them)."""
+        if getattr(self, "_ranks_dev", None) is None:
+            cm = np.ascontiguousarray(self.ranks.T).ravel().astype(np.int32)
+            self._ranks_dev = torch.from_numpy(cm).to(self.outer.device if self.outer is not None else "cuda")
+        return self._ranks_dev
+
 
 def dense_to_device(M: np.ndarray, device="cuda", ld: Optional[int] = None,
                     dtype: Optional[str] = None) -> torch.Tensor:
@@ -114,3 +122,55 @@ class TLRGemm:
         T.tlr_gemm_execute(self.plan, alpha, Ab, Bb, Dd, self.ldb, beta, C.data_ptr(), self.ldc,
                            self.ws.data_ptr(), self.ws.numel(), list(streams))
         return C
+
+
+class TLROutputGemm:
+    """C <- alpha op(A) op(B) + beta C with C in TLR format, every off-diagonal
+    result tile truncated to a relative Frobenius tolerance, the diagonal kept
+    dense.  Three library calls on one stream: tlr_expand of C into a dense
+    scratch (skipped when beta == 0), tlr_gemm_execute into that scratch, and
+    tlr_compress of it into the result buffers (device ranks, diagonal slots,
+    packed factors with room for ``capacity`` columns, info[3])."""
+
+    def __init__(self, dtype: str, opA: str, A: DeviceTLR, opB: str, B: DeviceTLR, b: int, has_diag: bool,
+                 max_rank: int, capacity: Optional[int] = None, budget: int = 0, device="cuda"):
+        self.dtype = dtype
+        self.gemm = TLRGemm(dtype, opA, A, opB, B, ldc=(A.rows if opA == "N" else A.cols), budget=budget,
+                            device=device)
+        self.m = self.gemm.info["m"]
+        self.n = self.gemm.info["n"]
+        self.b, self.has_diag, self.max_rank = b, has_diag, max_rank
+        self.qr, self.qc = -(-self.m // b), -(-self.n // b)
+        nt = self.qr * self.qc
+        n_off = nt - (min(self.qr, self.qc) if has_diag else 0)
+        self.capacity = n_off * max_rank if capacity is None else capacity
+        tdt = _TORCH[dtype]
+        self.scratch = torch.empty((self.n, self.m), dtype=tdt, device=device)     # column-major m x n
+        self.ews = torch.empty(max(16 * nt, 256), dtype=torch.uint8, device=device)
+        self.cws = torch.empty(T.tlr_compress_workspace_bytes(dtype, self.m, self.n, b, max_rank),
+                               dtype=torch.uint8, device=device)
+        self.ranks = torch.zeros(nt, dtype=torch.int32, device=device)
+        self.diag = torch.zeros((max(1, self.qr) * b * b) if has_diag else 1, dtype=tdt, device=device)
+        self.outer = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
+        self.inner = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
+        self.info = torch.zeros(3, dtype=torch.int32, device=device)
+
+    def __call__(self, alpha: float, A: DeviceTLR, B: DeviceTLR, beta: float, C: Optional[DeviceTLR], tol: float,
+                 omega: torch.Tensor, stream: Optional[int] = None):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        if beta != 0.0:
+            T.tlr_expand(self.dtype, self.m, self.n, self.b, self.has_diag, C.ranks_device().data_ptr(), C.buffers(),
+                         1.0, 0.0, self.scratch.data_ptr(), self.m, self.ews.data_ptr(), self.ews.numel(), s)
+        self.gemm(alpha, A, B, beta, self.scratch, [s])
+        T.tlr_compress(self.dtype, self.m, self.n, self.b, self.has_diag, self.scratch.data_ptr(), self.m, tol,
+                       self.max_rank, omega.data_ptr(), self.ranks.data_ptr(), _ptr(self.diag) if self.has_diag else 0,
+                       self.outer.data_ptr(), self.inner.data_ptr(), self.capacity, self.info.data_ptr(),
+                       self.cws.data_ptr(), self.cws.numel(), s)
+        return self
+
+    def host_result(self):
+        """(ranks q_r x q_c, outer, inner, diag, info) copied to the host
+        (after the caller has synchronised)."""
+        R = self.ranks.cpu().numpy().reshape(self.qc, self.qr).T.copy()
+        return (R, self.outer.cpu().numpy(), self.inner.cpu().numpy(),
+                self.diag.cpu().numpy() if self.has_diag else None, self.info.cpu().numpy())

@@ -28,7 +28,8 @@ TLR_STATIC_WORKSPACE_BYTES = 256 * 1024 * 1024
 EXPORTED = [
     "tlr_gemm_analyze", "tlr_gemm_workspace_bytes", "tlr_plan_info", "tlr_plan_rect",
     "tlr_plan_stage_shapes", "tlr_plan_launch", "tlr_plan_destroy", "tlr_plan_bind",
-    "tlr_gemm_execute", "tlr_gemm_execute_noalloc", "tlr_plan_profile", "tlr_plan_profile_read", "tlr_dense_gemm",
+    "tlr_gemm_execute", "tlr_gemm_execute_noalloc", "tlr_expand", "tlr_compress_workspace_bytes",
+    "tlr_compress", "tlr_plan_profile", "tlr_plan_profile_read", "tlr_dense_gemm",
     "tlr_status_string", "tlr_last_error", "tlr_version",
 ]
 
@@ -86,6 +87,11 @@ def lib():
                                    c_double, P, c_int64, P, c_size_t, POINTER(P), c_int32]
     L.tlr_gemm_execute_noalloc.argtypes = [P, c_double, POINTER(tlr_buffers), POINTER(tlr_buffers), P, c_int64,
                                            c_double, P, c_int64, POINTER(P), c_int32]
+    L.tlr_expand.argtypes = [c_int32, c_int64, c_int64, c_int32, c_int32, P, POINTER(tlr_buffers), c_double,
+                             c_double, P, c_int64, P, c_size_t, P]
+    L.tlr_compress_workspace_bytes.argtypes = [c_int32, c_int64, c_int64, c_int32, c_int32, POINTER(c_size_t)]
+    L.tlr_compress.argtypes = [c_int32, c_int64, c_int64, c_int32, c_int32, P, c_int64, c_double, c_int32, P, P,
+                               P, P, P, c_int64, P, P, c_size_t, P]
     L.tlr_plan_profile.argtypes = [P, c_int32]
     L.tlr_plan_profile_read.argtypes = [P, POINTER(c_double), POINTER(c_double), POINTER(c_int32)]
     L.tlr_dense_gemm.argtypes = [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_double, P, c_int64,
@@ -236,6 +242,31 @@ def tlr_gemm_execute_noalloc(p: Plan, alpha: float, A: Optional[tlr_buffers], B:
                                         c_void_p(B_dense or None), ldb, beta, c_void_p(C or None), ldc, arr,
                                         max(1, len(streams)))
     _check(st, "tlr_gemm_execute_noalloc")
+
+
+def tlr_expand(dtype, rows: int, cols: int, b: int, has_diag: bool, ranks_dev: int, X: tlr_buffers, alpha: float,
+               beta: float, C: int, ldc: int, workspace: int, workspace_bytes: int, stream: int = 0):
+    st = lib().tlr_expand(_dt(dtype), rows, cols, b, 1 if has_diag else 0, c_void_p(ranks_dev or None),
+                          ctypes.byref(X), alpha, beta, c_void_p(C or None), ldc, c_void_p(workspace or None),
+                          workspace_bytes, c_void_p(stream or None))
+    _check(st, "tlr_expand")
+
+
+def tlr_compress_workspace_bytes(dtype, rows: int, cols: int, b: int, max_rank: int) -> int:
+    out = c_size_t()
+    _check(lib().tlr_compress_workspace_bytes(_dt(dtype), rows, cols, b, max_rank, ctypes.byref(out)),
+           "tlr_compress_workspace_bytes")
+    return int(out.value)
+
+
+def tlr_compress(dtype, rows: int, cols: int, b: int, has_diag: bool, X: int, ldx: int, tol: float, max_rank: int,
+                 omega: int, ranks_out: int, diag: int, outer: int, inner: int, capacity: int, info: int,
+                 workspace: int, workspace_bytes: int, stream: int = 0):
+    st = lib().tlr_compress(_dt(dtype), rows, cols, b, 1 if has_diag else 0, c_void_p(X or None), ldx, tol, max_rank,
+                            c_void_p(omega or None), c_void_p(ranks_out or None), c_void_p(diag or None),
+                            c_void_p(outer or None), c_void_p(inner or None), capacity, c_void_p(info or None),
+                            c_void_p(workspace or None), workspace_bytes, c_void_p(stream or None))
+    _check(st, "tlr_compress")
 
 
 def tlr_plan_profile(p: Plan, max_executes: int):

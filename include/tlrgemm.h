@@ -352,6 +352,80 @@ tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64
                           const void *B, int64_t ldb, double beta, void *C, int64_t ldc,
                           void *stream);
 
+/* ---- TLR output: expansion and compression --------------------------------
+ *
+ * "TLR Matrix Multiplication", "Introduction: TLR GEMM": each of A, B and C
+ * may be stored densely or in TLR format, and the TLR-output cases extend
+ * the dense-output product.  The pages give no algorithm or accuracy target
+ * for them; this library reads them as: the exact result tile, then every
+ * off-diagonal tile replaced by its truncated SVD of the smallest rank whose
+ * discarded part meets a relative Frobenius tolerance tol,
+ *     ||X_ij - U_ij V_ij^T||_F <= tol ||X_ij||_F,
+ * diagonal tiles kept dense.  A product C <- alpha op(A) op(B) + beta C with
+ * a TLR C is then: tlr_expand of C into a dense m x n scratch (alpha = 1,
+ * beta = 0; skipped when beta == 0), tlr_gemm_execute into that scratch with
+ * the caller's alpha and beta, and tlr_compress of the scratch into the new
+ * C.  Only TLR_F32 and TLR_F64; everything runs on `stream` with no host
+ * synchronisation, and the ranks of a compressed result stay on the device
+ * until the caller copies them.
+ */
+
+/*
+ * tlr_expand: C <- alpha X + beta C, X the dense matrix of a stored TLR
+ * operand (tile (i,j) = U_ij V_ij^T of rank r_ij, dense diagonal tiles when
+ * has_diag), C dense rows x cols column-major with leading dim ldc >= rows.
+ *   ranks_dev  DEVICE q_r x q_c int32 ranks, column-major (r_ii = 0 with a
+ *              dense diagonal): the layout of X's packed factors (as for
+ *              tlr_shape.ranks).
+ *   X          device buffers of the operand.
+ *   workspace  device, at least 16 * q_r * q_c bytes, 8-byte aligned (the
+ *              factor offsets, computed on the device).
+ * beta == 0 never reads C.  Errors: TLR_ERR_INVALID_ARG, TLR_ERR_WORKSPACE,
+ * TLR_ERR_UNSUPPORTED (16-bit types), TLR_ERR_HIP.
+ */
+tlr_status tlr_expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag,
+                      const int32_t *ranks_dev, const tlr_buffers *X, double alpha, double beta,
+                      void *C, int64_t ldc, void *workspace, size_t workspace_bytes, void *stream);
+
+/* tlr_compress_workspace_bytes: device workspace tlr_compress needs for a
+ * rows x cols matrix, tile size b and ranks up to max_rank.  Host only.
+ * Errors as for tlr_compress's argument checks. */
+tlr_status tlr_compress_workspace_bytes(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b,
+                                        int32_t max_rank, size_t *bytes_out);
+
+/*
+ * tlr_compress: the dense rows x cols matrix X (column-major, leading dim
+ * ldx) as a TLR operand with tile size b: diagonal tiles dense (has_diag,
+ * square X), every other tile (i,j) the truncated SVD of the smallest rank
+ * r_ij <= max_rank with ||X_ij - U_ij V_ij^T||_F <= tol ||X_ij||_F.
+ * Method: a range sketch X_ij Omega with s = max_rank + 8 samples, its QR,
+ * the projection X_ij^T Q and its QR, and a one-sided Jacobi SVD of the
+ * s x s core; the energy the sketch misses counts as discarded.  The rank is
+ * decided on squared singular values, so tol must lie well above the square
+ * root of the unit roundoff (fp64: tol >= 1e-7; fp32: tol >= 1e-3); for an
+ * input of numerical rank above s - 8 the sketch may miss energy.
+ *   omega      device b x s Gaussian sketch (column-major, leading dim b),
+ *              drawn by the caller, s = max_rank + 8 (max_rank <= 56).
+ *   ranks_out  device q_r x q_c int32, column-major: the new ranks (0 on a
+ *              dense diagonal).
+ *   diag       device q_r slots of b*b (when has_diag), as in the storage above.
+ *   outer, inner  device factor buffers (leading dim b) of `capacity`
+ *              columns each; tile (i,j) is written at the packed offsets of
+ *              its new rank (U packed by tile row, V by tile column).  U has
+ *              orthogonal columns of norms sigma_k, V orthonormal columns.
+ *   info       device int32[3]: [0] columns used (sum of the new ranks),
+ *              [1] tiles that did not meet tol within max_rank (their rank is
+ *              max_rank), [2] 1 when [0] exceeds capacity (then no factor is
+ *              written; ranks and diagonal are).
+ *   workspace  device, tlr_compress_workspace_bytes, 256-byte aligned.
+ * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_WORKSPACE, TLR_ERR_UNSUPPORTED (16-bit
+ * types, max_rank > 56), TLR_ERR_HIP.
+ */
+tlr_status tlr_compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag,
+                        const void *X, int64_t ldx, double tol, int32_t max_rank, const void *omega,
+                        int32_t *ranks_out, void *diag, void *outer, void *inner, int64_t capacity,
+                        int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code (plumbing; the pages define no error
  * handling). */
 const char *tlr_status_string(tlr_status s);

@@ -20,8 +20,12 @@ Contents
               the packing rules, independently of the package's packer.
   checks      invariant checks on a rectangle schedule (cover, disjointness,
               budget).
+  recompress  the TLR-output product: the exact product, then every
+              off-diagonal tile truncated by SVD to the smallest rank that
+              meets a relative Frobenius tolerance; also dense-to-TLR
+              compression.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to values
 printed on the pages, closed forms, special cases and brute force.
 """
-from . import reference, brute, plan_arith, unpack, checks  # noqa: F401
+from . import reference, brute, plan_arith, unpack, checks, recompress  # noqa: F401

@@ -1,0 +1,199 @@
+"""TLR-output products on the GPU against the oracle (oracle/recompress.py),
+through the C ABI: tlr_expand, tlr_compress, and the product C <- alpha op(A)
+op(B) + beta C with C in TLR format (expand C, execute, compress).
+
+The GPU's packed result is read back with the oracle's own unpacker.  What is
+unique is compared exactly or to a bound: the ranks (equal to the oracle's
+truncated-SVD ranks; the inputs have a clear gap in every tile's spectrum
+around the tolerance), every tile's error ||U V^T - X_ij||_F <= tol ||X_ij||_F
+(with a slack of 1e-3 tol for rounding in the rank decision), the truncated
+tile itself (equal to the oracle's truncation within 1e-3 tol ||X_ij||_F
+plus the product's own rounding: 1e-12 fp64, 2e-5 fp32),
+and the dense diagonal tiles (relative error <= 1e-13 fp64, 1e-5 fp32).  The
+factors themselves are not unique and are not compared."""
+import numpy as np
+import pytest
+
+from gpu_helpers import gpu_ready, say
+from oracle import recompress as rc
+from oracle import reference, unpack
+from tlr_inputs import TLR_OUT, gaussian_sketch, random_tlr, tile_sizes, tlr_out_inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_ready(), reason="needs the GPU and libtlrgemm.so")]
+
+DIAG_TOL = {"f64": 1e-13, "f32": 1e-5}
+ROUND = {"f64": 1e-12, "f32": 2e-5}     # rounding of the product itself, relative to a tile
+
+
+def _unpacked(R, outer, inner, diag, rows, cols, b, has_diag, dtype):
+    return unpack.unpack(rows, cols, b, R, has_diag, outer, inner, diag, dtype)
+
+
+def _check_against_oracle(got, X, tol, dtype, ref_ranks=None, what=""):
+    """got: TLRTiles read back from the GPU; X: the exact dense result."""
+    errs = rc.tile_errors(got, X)
+    off = ~np.isnan(errs)
+    worst = float(np.max(errs[off])) if off.any() else 0.0
+    say(f"{what}: max tile error / tol = {worst / tol:.3f}, ranks {got.ranks[off].min() if off.any() else 0}.."
+        f"{got.ranks.max()}")
+    assert worst <= tol * (1 + 1e-3) + ROUND[dtype], worst
+    want = rc.compress(X, got.b, got.has_diag, tol)
+    if ref_ranks is not None:
+        assert np.array_equal(want.ranks, ref_ranks)
+    assert np.array_equal(got.ranks, want.ranks), np.argwhere(got.ranks != want.ranks)[:5]
+    rs, cs = got.row_sizes, got.col_sizes
+    ro, co = reference.offsets(rs), reference.offsets(cs)
+    for i in range(len(rs)):
+        for j in range(len(cs)):
+            x = X[ro[i]:ro[i] + rs[i], co[j]:co[j] + cs[j]]
+            nx = max(np.linalg.norm(x), 1e-300)
+            if got.has_diag and i == j:
+                assert np.linalg.norm(got.diag[i] - x) / nx <= DIAG_TOL[dtype]
+                continue
+            g = got.U[(i, j)] @ got.V[(i, j)].T
+            w = want.U[(i, j)] @ want.V[(i, j)].T
+            assert np.linalg.norm(g - w) / nx <= 1e-3 * tol + ROUND[dtype], (i, j)
+
+
+def _compress_on_gpu(X, b, has_diag, tol, max_rank, dtype="f64", capacity=None, omega=None, sketch_seed=11):
+    import torch
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from hpc_linear_algebra_amd.device import _TORCH, dense_to_device
+    rows, cols = X.shape
+    qr, qc = len(tile_sizes(rows, b)), len(tile_sizes(cols, b))
+    nt = qr * qc
+    n_off = nt - (min(qr, qc) if has_diag else 0)
+    capacity = n_off * max_rank if capacity is None else capacity
+    npd = np.float64 if dtype == "f64" else np.float32
+    Xd = dense_to_device(np.asarray(X, npd))
+    om = torch.from_numpy(np.ascontiguousarray(
+        (gaussian_sketch(sketch_seed, b, max_rank + 8, dtype) if omega is None else omega).T)).cuda()
+    tdt = _TORCH[dtype]
+    ranks = torch.full((nt,), -7, dtype=torch.int32, device="cuda")
+    diag = torch.zeros(max(1, qr * b * b), dtype=tdt, device="cuda")
+    outer = torch.full((max(1, capacity) * b,), 3.0, dtype=tdt, device="cuda")
+    inner = torch.full((max(1, capacity) * b,), 3.0, dtype=tdt, device="cuda")
+    info = torch.full((3,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(T.tlr_compress_workspace_bytes(dtype, rows, cols, b, max_rank), dtype=torch.uint8, device="cuda")
+    T.tlr_compress(dtype, rows, cols, b, has_diag, Xd.data_ptr(), rows, tol, max_rank, om.data_ptr(),
+                   ranks.data_ptr(), diag.data_ptr(), outer.data_ptr(), inner.data_ptr(), capacity, info.data_ptr(),
+                   ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    R = ranks.cpu().numpy().reshape(qc, qr).T.copy()
+    return R, outer.cpu().numpy().astype(np.float64), inner.cpu().numpy().astype(np.float64), \
+        diag.cpu().numpy().astype(np.float64), info.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+@pytest.mark.parametrize("n,b,diag", [(384, 128, True), (300, 64, True), (256, 64, False), (200, 96, False)])
+def test_expand_equals_the_rebuilt_operand(dtype, n, b, diag):
+    import torch
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from hpc_linear_algebra_amd.device import DeviceTLR, dense_from_device, dense_to_device
+    rng = np.random.default_rng(n + b)
+    X = random_tlr(rng, n, n, b, rank_lo=0, rank_hi=40, has_diag=diag, dtype=dtype)
+    C0 = rng.standard_normal((n, n))
+    dX = DeviceTLR(X)
+    for alpha, beta in ((1.0, 0.0), (0.5, -2.0)):
+        Cd = dense_to_device(np.asarray(C0, np.float64 if dtype == "f64" else np.float32), ld=n + 3)
+        ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+        say(f"expand {dtype} n={n} b={b} diag={diag} alpha={alpha} beta={beta}")
+        T.tlr_expand(dtype, n, n, b, diag, dX.ranks_device().data_ptr(), dX.buffers(), alpha, beta, Cd.data_ptr(),
+                     n + 3, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        got = dense_from_device(Cd, n, n)
+        ref = alpha * reference.reconstruct(X) + (beta * C0 if beta != 0 else 0.0)
+        assert reference.rel_fro(got, ref) <= (1e-14 if dtype == "f64" else 1e-6)
+
+
+@pytest.mark.parametrize("n,b,diag", [(512, 128, True), (300, 64, True), (320, 96, False)])
+def test_compress_recovers_generated_ranks(n, b, diag):
+    rng = np.random.default_rng(7 * n + b)
+    t = random_tlr(rng, n, n, b, rank_lo=0, rank_hi=40, has_diag=diag, scale=1.0)
+    X = reference.reconstruct(t)
+    R, outer, inner, dg, info = _compress_on_gpu(X, b, diag, 1e-7, 48)
+    say(f"compress n={n} b={b}: info {info.tolist()}")
+    assert info[1] == 0 and info[2] == 0 and info[0] == int(t.ranks.sum())
+    assert np.array_equal(R, t.ranks)
+    got = _unpacked(R, outer, inner, dg, n, n, b, diag, "f64")
+    _check_against_oracle(got, X, 1e-7, "f64", ref_ranks=t.ranks, what=f"compress n={n}")
+
+
+@pytest.mark.parametrize("dtype,tol", [("f64", 1e-6), ("f64", 1e-3), ("f32", 1e-3)])
+def test_tlr_output_product(dtype, tol):
+    """C <- alpha A B + beta C on the TLR-output workload's recipe at N = 1000,
+    b = 128 (a 104-row boundary tile), against the oracle's exact product
+    truncated tile by tile."""
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLROutputGemm
+    N, b = 1000, 128
+    A, B, C, omega = tlr_out_inputs(N=N, b=b, dtype=dtype)
+    dA, dB, dC = DeviceTLR(A), DeviceTLR(B), DeviceTLR(C)
+    g = TLROutputGemm(dtype, "N", dA, "N", dB, b, True, TLR_OUT["max_rank"])
+    om = torch.from_numpy(np.ascontiguousarray(omega.T)).cuda()
+    for alpha, beta in ((1.0, 1.0), (0.5, 0.0)):
+        say(f"tlr output {dtype} tol={tol} alpha={alpha} beta={beta}")
+        g(alpha, dA, dB, beta, dC, tol, om)
+        torch.cuda.synchronize()
+        R, outer, inner, dg, info = g.host_result()
+        assert info[1] == 0 and info[2] == 0
+        got = _unpacked(R, outer.astype(np.float64), inner.astype(np.float64), dg.astype(np.float64), N, N, b, True,
+                        "f64")
+        X = reference.gemm_reference(alpha, "N", A, "N", B, beta, reference.reconstruct(C) if beta != 0 else None)
+        _check_against_oracle(got, X, tol, dtype, what=f"tlr output {dtype}")
+
+
+def test_beta_zero_never_reads_c():
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLROutputGemm
+    A, B, C, omega = tlr_out_inputs(N=512, b=128)
+    for key in C.U:
+        C.U[key] = np.full_like(C.U[key], np.nan)
+    C.diag = [np.full_like(d, np.nan) for d in C.diag]
+    dA, dB, dC = DeviceTLR(A), DeviceTLR(B), DeviceTLR(C)
+    g = TLROutputGemm("f64", "N", dA, "N", dB, 128, True, 48)
+    g(1.0, dA, dB, 0.0, dC, 1e-6, torch.from_numpy(np.ascontiguousarray(omega.T)).cuda())
+    torch.cuda.synchronize()
+    R, outer, inner, dg, info = g.host_result()
+    got = _unpacked(R, outer, inner, dg, 512, 512, 128, True, "f64")
+    assert np.all(np.isfinite(reference.reconstruct(got)))
+    _check_against_oracle(got, reference.gemm_reference(1.0, "N", A, "N", B, 0.0, None), 1e-6, "f64", what="beta 0")
+
+
+def test_rank_and_capacity_limits_are_reported():
+    rng = np.random.default_rng(5)
+    t = random_tlr(rng, 256, 256, 64, rank_lo=20, rank_hi=30, has_diag=True, scale=1.0)
+    X = reference.reconstruct(t)
+    # ranks 20..30 but at most 16 kept: every off-diagonal tile is flagged and keeps 16 columns
+    R, outer, inner, dg, info = _compress_on_gpu(X, 64, True, 1e-7, 16)
+    off = ~np.eye(4, dtype=bool)
+    assert info[1] == int(off.sum()) and np.all(R[off] == 16) and info[0] == 16 * int(off.sum())
+    # room for fewer columns than needed: ranks and diagonal written, no factor column touched
+    R, outer, inner, dg, info = _compress_on_gpu(X, 64, True, 1e-7, 40, capacity=100)
+    assert info[2] == 1 and np.array_equal(R, t.ranks)
+    assert np.all(outer == 3.0) and np.all(inner == 3.0)
+    ro = reference.offsets(t.row_sizes)
+    for i, s in enumerate(t.row_sizes):
+        assert np.allclose(dg[i * 64 * 64:(i + 1) * 64 * 64].reshape(64, 64).T[:s, :s],
+                           X[ro[i]:ro[i] + s, ro[i]:ro[i] + s], rtol=0, atol=1e-15)
+
+
+def test_full_tlr_output_workload():
+    """The TLR-output workload (N = 8192, b = 256, 32 x 32 tiles, tol 1e-6),
+    every tile compared."""
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLROutputGemm
+    cfg = TLR_OUT
+    N, b = cfg["N"], cfg["b"]
+    say("tlr output workload: generating")
+    A, B, C, omega = tlr_out_inputs()
+    dA, dB, dC = DeviceTLR(A), DeviceTLR(B), DeviceTLR(C)
+    g = TLROutputGemm(cfg["dtype"], cfg["opA"], dA, cfg["opB"], dB, b, True, cfg["max_rank"])
+    g(cfg["alpha"], dA, dB, cfg["beta"], dC, cfg["tol"], torch.from_numpy(np.ascontiguousarray(omega.T)).cuda())
+    torch.cuda.synchronize()
+    R, outer, inner, dg, info = g.host_result()
+    say(f"tlr output workload: info {info.tolist()}")
+    assert info[1] == 0 and info[2] == 0
+    got = _unpacked(R, outer, inner, dg, N, N, b, True, "f64")
+    X = reference.gemm_reference(cfg["alpha"], cfg["opA"], A, cfg["opB"], B, cfg["beta"], reference.reconstruct(C))
+    _check_against_oracle(got, X, cfg["tol"], "f64", what="tlr output workload")

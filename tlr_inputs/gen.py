@@ -161,6 +161,79 @@ def random_tlr(rng: np.random.Generator, rows: int, cols: int, b: int,
     return fill_values(rng, rows, cols, b, R, has_diag, dtype, decay, scale)
 
 
+def basis_tlr(rng: np.random.Generator, rows: int, cols: int, b: int, r0: int, rank_lo: int, rank_hi: int,
+              shared: str, has_diag: bool = True, decay: float = 1.0, dtype: str = "f64") -> TLRTiles:
+    """TLR operand whose factors are drawn inside shared bases, so that
+    products of such operands have tiles of bounded rank (the compressible
+    outputs a TLR-output product is for).  Draw order: the diagonal tiles,
+    then one basis per tile row (s_i x r0) when the outer factors are shared,
+    one per tile column (s_j x r0) when the inner ones are, then per
+    off-diagonal tile (tile-row-major) its rank and its coefficient or free
+    factors.  Entries N(0,1)/sqrt(b); basis column a scaled by decay**a;
+    coefficients N(0,1)/sqrt(r0).  A shared outer factor of tile (i,j) is
+    Phi_i G_ij (G_ij r0 x r_ij), a shared inner one Psi_j H_ij; ``shared`` is
+    "outer", "inner" or "both"."""
+    rs, cs = tile_sizes(rows, b), tile_sizes(cols, b)
+    scale = 1.0 / math.sqrt(b)
+    diag = [rng.standard_normal((s_, s_)) * scale for s_ in rs] if has_diag else None
+    w = decay ** np.arange(r0)
+    phi = [rng.standard_normal((s_, r0)) * scale * w for s_ in rs] if shared in ("outer", "both") else None
+    psi = [rng.standard_normal((s_, r0)) * scale * w for s_ in cs] if shared in ("inner", "both") else None
+    R = np.zeros((len(rs), len(cs)), dtype=np.int32)
+    U, V = {}, {}
+    for i in range(len(rs)):
+        for j in range(len(cs)):
+            if has_diag and i == j:
+                continue
+            r = int(rng.integers(min(rank_lo, rs[i], cs[j]), min(rank_hi, rs[i], cs[j]) + 1))
+            R[i, j] = r
+            u = phi[i] @ (rng.standard_normal((r0, r)) / math.sqrt(r0)) if phi is not None \
+                else rng.standard_normal((rs[i], r)) * scale
+            v = psi[j] @ (rng.standard_normal((r0, r)) / math.sqrt(r0)) if psi is not None \
+                else rng.standard_normal((cs[j], r)) * scale
+            U[(i, j)], V[(i, j)] = u, v
+    if dtype != "f64":
+        diag = None if diag is None else [on_grid(d, dtype) for d in diag]
+        U = {k: on_grid(x, dtype) for k, x in U.items()}
+        V = {k: on_grid(x, dtype) for k, x in V.items()}
+    return TLRTiles(rows, cols, b, R, diag, U, V, dtype)
+
+
+def gaussian_sketch(seed: int, b: int, s: int, dtype: str = "f64") -> np.ndarray:
+    """b x s matrix of N(0,1) entries (the range sketch of dense-to-TLR
+    compression), from numpy.random.default_rng(seed)."""
+    return on_grid(np.random.default_rng(seed).standard_normal((b, s)), dtype)
+
+
+# The TLR-output product (C <- alpha A B + beta C with C in TLR format,
+# compressed to a tolerance): A's outer factors share one basis per tile row,
+# B's inner factors one per tile column, C both, so every result tile has
+# rank at most r0 plus the ranks of the diagonal-term products.
+TLR_OUT = dict(name="tlr_out_f64_n8192_b256", kind="tlr_out", dtype="f64", N=8192, b=256, opA="N", opB="N",
+               alpha=1.0, beta=1.0, r0=16, rank_lo=4, rank_hi=12, c_rank_lo=0, c_rank_hi=8, decay=0.5,
+               tol=1e-6, max_rank=48, seed=6000)
+
+
+def tlr_out_inputs(cfg: Optional[dict] = None, N: Optional[int] = None, b: Optional[int] = None,
+                   dtype: Optional[str] = None):
+    """(A, B, C, omega) of a TLR-output product: the TLR_OUT workload, or the
+    same recipe at another size.  Seeds 1000*6 + stream: 0 = A, 1 = B, 2 = C,
+    3 = the sketch."""
+    cfg = dict(TLR_OUT if cfg is None else cfg)
+    N = N or cfg["N"]
+    b = b or cfg["b"]
+    dt = dtype or cfg["dtype"]
+    sd = cfg["seed"]
+    A = basis_tlr(np.random.default_rng(sd + 0), N, N, b, cfg["r0"], cfg["rank_lo"], cfg["rank_hi"], "outer",
+                  True, cfg["decay"], dt)
+    B = basis_tlr(np.random.default_rng(sd + 1), N, N, b, cfg["r0"], cfg["rank_lo"], cfg["rank_hi"], "inner",
+                  True, cfg["decay"], dt)
+    C = basis_tlr(np.random.default_rng(sd + 2), N, N, b, cfg["r0"], cfg["c_rank_lo"], cfg["c_rank_hi"], "both",
+                  True, cfg["decay"], dt)
+    omega = gaussian_sketch(sd + 3, b, cfg["max_rank"] + 8, dt)
+    return A, B, C, omega
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.
 # ---------------------------------------------------------------------------
