@@ -288,12 +288,115 @@ def cpu_baseline(cfg, A, B, C_in, useful_flops, budget_s=15.0):
                       f"product (host cpu_count={os.cpu_count()})"}
 
 
+def bench_tlr_out(args):
+    """The TLR-output product (C <- alpha A B + beta C, C in TLR format, every
+    off-diagonal result tile truncated to a relative tolerance): expand C into
+    a dense scratch, the dense-output product into it, compress it.  One step
+    is all three; each is timed with its own event pair."""
+    import numpy as np
+    import torch
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLROutputGemm
+    from tlr_inputs import TLR_OUT, tlr_out_inputs
+    cfg = TLR_OUT
+    N, b, dtype = cfg["N"], cfg["b"], cfg["dtype"]
+    torch.cuda.set_device(0)
+    log("bench: generating the TLR-output workload")
+    A, B, C, omega = tlr_out_inputs()
+    dA, dB, dC = DeviceTLR(A), DeviceTLR(B), DeviceTLR(C)
+    g = TLROutputGemm(dtype, cfg["opA"], dA, cfg["opB"], dB, b, True, cfg["max_rank"])
+    om = torch.from_numpy(np.ascontiguousarray(omega.T)).cuda()
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    from hpc_linear_algebra_amd import tlrgemm as T
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        T.tlr_expand(dtype, N, N, b, True, dC.ranks_device().data_ptr(), dC.buffers(), 1.0, 0.0,
+                     g.scratch.data_ptr(), N, g.ews.data_ptr(), g.ews.numel(), s)
+        ev[1].record(stream)
+        g.gemm(cfg["alpha"], dA, dB, cfg["beta"], g.scratch, [s])
+        ev[2].record(stream)
+        T.tlr_compress(dtype, N, N, b, True, g.scratch.data_ptr(), N, cfg["tol"], cfg["max_rank"], om.data_ptr(),
+                       g.ranks.data_ptr(), g.diag.data_ptr(), g.outer.data_ptr(), g.inner.data_ptr(), g.capacity,
+                       g.info.data_ptr(), g.cws.data_ptr(), g.cws.numel(), s)
+        ev[3].record(stream)
+        return ev
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    evs = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    phases = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in evs])
+    total = phases.sum(axis=1)
+    ms = float(total.mean())
+    R, _, _, _, info = g.host_result()
+    F = g.gemm.info["useful_flops"]
+    value = F / (ms * 1e-3) / 1e12
+    es = ES[dtype]
+    q = R.shape[0]
+    out_elems = sum(int(R[i, j]) * (2 * b) for i in range(q) for j in range(q) if i != j) + q * b * b
+    # dominant phase: its rate against its own roofline
+    names = ["expand", "product", "compress"]
+    dom = int(np.argmax(phases.mean(axis=0)))
+    cpu = None
+    if not args.no_cpu:
+        from oracle import recompress as rc
+        from oracle import reference
+        rng = np.random.default_rng(7)
+        Cd = reference.reconstruct(C)
+        t0 = time.perf_counter()
+        done = 0
+        off = reference.offsets([b] * q)
+        for x in rng.permutation(q * q):
+            i, j = int(x) // q, int(x) % q
+            blk = reference.gemm_reference_block(cfg["alpha"], cfg["opA"], A, cfg["opB"], B, cfg["beta"],
+                                                 Cd[off[i]:off[i] + b, off[j]:off[j] + b],
+                                                 (off[i], off[i] + b), (off[j], off[j] + b))
+            if i != j:
+                rc.truncate_tile(blk, cfg["tol"])
+            done += 1
+            if time.perf_counter() - t0 > args.cpu_seconds and done >= 2:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": F / (dt * q * q / done) / 1e12, "unit": "TFLOP/s", "kind": "oracle",
+               "cores": os.cpu_count(),
+               "sample": f"{done} of {q*q} output tiles: the exact tile (rebuilt panels, numpy BLAS) and its SVD "
+                         f"truncation, {dt:.2f} s, scaled by {q*q}/{done}; the dense expansion of C is outside "
+                         f"the timed loop"}
+    out = {
+        "metric": "TLR-output product useful TFLOP/s (expand C, dense-output product, compress), fp64 N=8192",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": cfg["name"], "N": N, "b": b, "opA": cfg["opA"], "opB": cfg["opB"],
+                   "alpha": cfg["alpha"], "beta": cfg["beta"], "tol": cfg["tol"], "max_rank": cfg["max_rank"],
+                   "useful_flops": F, "useful_flops_basis": "the product's useful flops from its ranks"},
+        "phases_ms": {n: round(float(phases[:, k].mean()), 4) for k, n in enumerate(names)},
+        "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(total)), 4),
+                    "min": round(float(total.min()), 4), "max": round(float(total.max()), 4)},
+        "result": {"rank_sum": int(info[0]), "tiles_flagged": int(info[1]), "capacity_exceeded": int(info[2]),
+                   "rank_min": int(min(R[i, j] for i in range(q) for j in range(q) if i != j)),
+                   "rank_max": int(R.max()),
+                   "memory_vs_dense": round(out_elems / float(N * N), 4)},
+        "dominant_phase": names[dom],
+        "roofline": None,
+        "cpu_baseline": cpu,
+    }
+    log(f"bench: {ms:.3f} ms/step ({', '.join(f'{n} {phases[:, k].mean():.3f}' for k, n in enumerate(names))}), "
+        f"wall {wall * 1e3 / args.steps:.3f} ms/step")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="1..5: the seeded workloads (3, the N=16384 TLR x TLR product, is the metric's); "
-                         "dense_tlr: workload 2 with the operands swapped")
+                         "dense_tlr: workload 2 with the operands swapped; tlr_out: the TLR-output product "
+                         "(N=8192, b=256, C in TLR format, compressed to a tolerance)")
     ap.add_argument("--dtype", default=None, choices=["f64", "f32", "f16", "bf16"],
                     help="element type in place of the workload's own (same draws, rounded to it)")
     ap.add_argument("--order", default="auto", choices=["auto", "left", "right"],
@@ -329,6 +432,10 @@ def main():
         print("bench.py measures one GPU only: the TLR GEMM here runs on a single MI355X "
               "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "tlr_out":
+        print(json.dumps(bench_tlr_out(args)), flush=True)
+        return
 
     import numpy as np
     import torch

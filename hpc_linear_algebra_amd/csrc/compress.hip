@@ -50,8 +50,9 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-// Sum over the workgroup (every thread gets it).  red holds CT/64 slots.
-template <typename T>
+// Sum over the workgroup of NTH threads (every thread gets it).  red holds
+// NTH/64 slots.
+template <typename T, int NTH = CT>
 __device__ __forceinline__ T block_sum(T v, T *red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -60,7 +61,7 @@ __device__ __forceinline__ T block_sum(T v, T *red) {
   __syncthreads();
   T s = 0;
 #pragma unroll
-  for (int k = 0; k < CT / 64; ++k) s += red[k];
+  for (int k = 0; k < NTH / 64; ++k) s += red[k];
   return s;
 }
 
@@ -83,36 +84,27 @@ __global__ __launch_bounds__(CT) void tile_norms_kernel(const T *X, int64_t ldx,
   if (threadIdx.x == 0) norms2[t] = acc;
 }
 
-// Householder QR of every tile's m x n matrix A (column-major, leading dim
-// lda, tile t at A + t * stride), m = s_i (m_sel 0) or s_j (m_sel 1), n <=
-// S_MAX.  A is overwritten by the explicit Q (m x n, orthonormal columns;
-// columns beyond min(m, n) zero); with R != nullptr the n x n upper factor is
-// written to R + t * n * n (column-major, zero below the diagonal).
-// Reflector k: v = x - alpha e_k with alpha = -sign(x_k) ||x||, H = I - beta v v^T,
-// beta = 2 / (v^T v), v kept in column k (rows >= k) until Q is formed.
-template <typename T>
-__global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
-                                                     int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
-                                                     int skip_diag) {
-  __shared__ T red[CT / 64];
-  __shared__ T beta_s[S_MAX];
-  const int t = blockIdx.x;
-  const int i = t % qr, j = t / qr;
-  if (skip_diag && i == j) return;
-  const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
-  T *a = A + (int64_t)t * stride;
-  T *rr = R ? R + (int64_t)t * n * n : nullptr;
+// Householder QR of one m x n panel a (column-major, leading dim lda; in LDS
+// or global memory), n <= S_MAX, by a workgroup of NTH threads.  The panel
+// is overwritten by the explicit Q (m x n, orthonormal columns; columns past
+// min(m, n) zero); with rr != nullptr the n x n upper factor is written to rr
+// (column-major, zero below the diagonal).  Reflector k: v = x - alpha e_k with
+// alpha = -sign(x_k) ||x||, H = I - beta v v^T, beta = 2 / (v^T v); v stays in
+// column k (rows >= k) until Q is formed.
+template <typename T, int NTH>
+__device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *red, T *beta_s) {
+  constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kmax = min(m, n);
   if (rr)
-    for (int e = tid; e < n * n; e += CT) rr[e] = 0;
+    for (int e = tid; e < n * n; e += NTH) rr[e] = 0;
   for (int k = 0; k < kmax; ++k) {
     T tail = 0;
-    for (int r = k + 1 + tid; r < m; r += CT) {
+    for (int r = k + 1 + tid; r < m; r += NTH) {
       const T v = a[r + (int64_t)k * lda];
       tail += v * v;
     }
-    tail = block_sum(tail, red);
+    tail = block_sum<T, NTH>(tail, red);
     const T x0 = a[k + (int64_t)k * lda];
     const T nrm = sqrt(tail + x0 * x0);
     const T alpha = x0 >= T(0) ? -nrm : nrm;
@@ -127,11 +119,11 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
     }
     __syncthreads();
     // trailing columns: A[k:m, c] -= beta (v^T A[k:m, c]) v, one wave per column
-    for (int c = k + 1 + wave; c < n; c += CT / 64) {
-      T s = 0;
-      for (int r = k + lane; r < m; r += 64) s += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
-      s = wave_sum(s);
-      const T f = beta * s;
+    for (int c = k + 1 + wave; c < n; c += NW) {
+      T sacc = 0;
+      for (int r = k + lane; r < m; r += 64) sacc += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
+      sacc = wave_sum(sacc);
+      const T f = beta * sacc;
       for (int r = k + lane; r < m; r += 64) a[r + (int64_t)c * lda] -= f * a[r + (int64_t)k * lda];
       if (rr && lane == 0) rr[k + (int64_t)c * n] = a[k + (int64_t)c * lda];
     }
@@ -140,16 +132,16 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
   // Q = H_0 ... H_{kmax-1} applied to the first n columns of the identity,
   // formed backwards in place; columns past kmax are zero
   for (int c = kmax; c < n; ++c)
-    for (int r = tid; r < m; r += CT) a[r + (int64_t)c * lda] = 0;
+    for (int r = tid; r < m; r += NTH) a[r + (int64_t)c * lda] = 0;
   __syncthreads();
   for (int k = kmax - 1; k >= 0; --k) {
     const T beta = beta_s[k];
-    for (int c = k + 1 + wave; c < n; c += CT / 64) {
+    for (int c = k + 1 + wave; c < n; c += NW) {
       // rows < k+1 of column c are zero here, so the sum starts at k + 1
-      T s = 0;
-      for (int r = k + 1 + lane; r < m; r += 64) s += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
-      s = wave_sum(s);
-      const T f = beta * s;
+      T sacc = 0;
+      for (int r = k + 1 + lane; r < m; r += 64) sacc += a[r + (int64_t)k * lda] * a[r + (int64_t)c * lda];
+      sacc = wave_sum(sacc);
+      const T f = beta * sacc;
       // row k of column c becomes -f v0
       if (lane == 0) a[k + (int64_t)c * lda] = -f * a[k + (int64_t)k * lda];
       for (int r = k + 1 + lane; r < m; r += 64) a[r + (int64_t)c * lda] -= f * a[r + (int64_t)k * lda];
@@ -157,13 +149,143 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
     __syncthreads();
     const T v0 = a[k + (int64_t)k * lda];
     __syncthreads();   // v0 read by every thread before column k is rewritten
-    for (int r = tid; r < m; r += CT) {
+    for (int r = tid; r < m; r += NTH) {
       const T vr = a[r + (int64_t)k * lda];
       a[r + (int64_t)k * lda] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
     }
     __syncthreads();
   }
 }
+
+// The same QR for a panel held in LDS, by NTH = 512 threads, with no wave
+// reductions in the inner loops: for reflector k, w = A[k:m, k+1:n]^T v is
+// formed as 8 partial sums per column (thread (column, part) adds rows
+// part, part + 8, ...) combined through LDS, then every thread applies its
+// share of the rank-1 update A -= beta v w^T.  Q is formed backwards the
+// same way.
+constexpr int QR_STAGED_THREADS = 512;
+constexpr int QR_PARTS = QR_STAGED_THREADS / S_MAX;   // 8 partial sums per column
+constexpr int QR_ROWS = 256;                           // rows of a staged panel (b <= 256); two threads per row
+template <typename T>
+__device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, T *beta_s, T *part, T *wv) {
+  constexpr int NTH = QR_STAGED_THREADS;
+  const int tid = threadIdx.x;
+  const int pp = tid % QR_PARTS, cc = tid / QR_PARTS;     // (part, column) of the partial sums
+  const int kmax = min(m, n);
+  if (rr)
+    for (int e = tid; e < n * n; e += NTH) rr[e] = 0;
+  // w_c = sum_{r >= r0} a[r, k] a[r, c] for columns c in (k, n), into wv[c]
+  auto apply_vt = [&](int k, int r0) {
+    const int c = k + 1 + cc;
+    T acc = 0;
+    if (c < n)
+      for (int r = r0 + pp; r < m; r += QR_PARTS) acc += a[r + k * m] * a[r + c * m];
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < n) {
+      T w = 0;
+      if (tid > k) {
+        const T *pt = part + (tid - k - 1) * QR_PARTS;
+#pragma unroll
+        for (int x = 0; x < QR_PARTS; ++x) w += pt[x];
+      }
+      wv[tid] = w;
+    }
+    __syncthreads();
+  };
+  for (int k = 0; k < kmax; ++k) {
+    T tail = 0;
+    for (int r = k + 1 + tid; r < m; r += NTH) tail += a[r + k * m] * a[r + k * m];
+    tail = block_sum<T, NTH>(tail, red);
+    const T x0 = a[k + k * m];
+    const T nrm = sqrt(tail + x0 * x0);
+    const T alpha = x0 >= T(0) ? -nrm : nrm;
+    const T v0 = x0 - alpha;
+    const T vtv = tail + v0 * v0;
+    const T beta = vtv > T(0) ? T(2) / vtv : T(0);
+    __syncthreads();
+    if (tid == 0) {
+      a[k + k * m] = v0;
+      beta_s[k] = beta;
+      if (rr) rr[k + k * n] = alpha;
+    }
+    __syncthreads();
+    apply_vt(k, k);
+    // A[r, c] -= beta w_c v_r for r >= k, c > k: thread (row r, half h) takes
+    // the columns c = k + 1 + h, k + 3 + h, ...
+    {
+      const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
+      if (r < m) {
+        const T vb = beta * a[r + k * m];
+        for (int c = k + 1 + h; c < n; c += QR_STAGED_THREADS / QR_ROWS) a[r + c * m] -= vb * wv[c];
+      }
+    }
+    __syncthreads();
+    if (rr)
+      for (int c = k + 1 + tid; c < n; c += NTH) rr[k + c * n] = a[k + c * m];
+  }
+  for (int c = kmax; c < n; ++c)
+    for (int r = tid; r < m; r += NTH) a[r + c * m] = 0;
+  __syncthreads();
+  for (int k = kmax - 1; k >= 0; --k) {
+    const T beta = beta_s[k];
+    // rows <= k of the columns c > k are zero here: w_c = sum_{r > k} v_r Q[r, c]
+    apply_vt(k, k + 1);
+    const T v0 = a[k + k * m];
+    {
+      // row k of the columns c > k was zero: it becomes -beta w_c v0
+      const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
+      if (r < m) {
+        const T vb = beta * a[r + k * m];
+        for (int c = k + 1 + h; c < n; c += QR_STAGED_THREADS / QR_ROWS)
+          a[r + c * m] = (r == k ? T(0) : a[r + c * m]) - vb * wv[c];
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < m; r += NTH) {
+      const T vr = a[r + k * m];
+      a[r + k * m] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
+    }
+    __syncthreads();
+  }
+}
+
+// QR of every tile's m x n panel (tile t at A + t * stride, leading dim lda),
+// m = s_i (m_sel 0) or s_j (m_sel 1); R (optional) at R + t * n * n.  STAGED:
+// the panel is copied into LDS (m * n <= PANEL elements), factorised there and
+// copied back, by 512 threads; otherwise it is factorised in place in global
+// memory by 256 threads.
+template <typename T> struct QrPanel { static constexpr int ELEMS = 131072 / sizeof(T); };   // 128 KiB of LDS
+
+template <typename T, bool STAGED>
+__global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kernel(
+    T *A, int lda, int64_t stride, T *R, int qr, int qc, int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
+    int skip_diag) {
+  constexpr int NTH = STAGED ? QR_STAGED_THREADS : CT;
+  __shared__ T red[NTH / 64];
+  __shared__ T beta_s[S_MAX];
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  if (skip_diag && i == j) return;
+  const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
+  T *a = A + (int64_t)t * stride;
+  T *rr = R ? R + (int64_t)t * n * n : nullptr;
+  if constexpr (STAGED) {
+    __shared__ T panel[QrPanel<T>::ELEMS];
+    __shared__ T part[QR_STAGED_THREADS];
+    __shared__ T wv[S_MAX];
+    for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
+      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) panel[r + c * m] = a[r + (int64_t)c * lda];
+    __syncthreads();
+    qr_panel_lds<T>(panel, m, rr, n, red, beta_s, part, wv);
+    for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
+      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) a[r + (int64_t)c * lda] = panel[r + c * m];
+  } else {
+    qr_panel<T, NTH>(a, lda, rr, m, n, red, beta_s);
+  }
+}
+
+constexpr int JPARTS = CT / 32;   // partial sums per column pair (CT threads, at most 32 pairs)
 
 // One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
 // then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
@@ -180,7 +302,9 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   __shared__ T Js[S_MAX * S_MAX];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
-  __shared__ T offw[CT / 64];
+  __shared__ T offw[1 + 32];          // [1 + p]: largest |cos| pair thread p met in the sweep
+  __shared__ T gram[3 * CT];
+  __shared__ T rot[2 * 32];
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -197,50 +321,72 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     Ms[e] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
     Js[e] = r == c ? T(1) : T(0);
   }
+  if (tid < 33) offw[tid] = 0;
   __syncthreads();
   const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
   const int npairs = np / 2;
+  // thread (pair, part): pair = tid / 8 (at most 32 pairs), rows part, part + 8, ...
+  const int jp = tid / JPARTS, jpart = tid % JPARTS;
   for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
-    T off = 0;
     for (int round = 0; round < np - 1; ++round) {
-      for (int pk = wave; pk < npairs; pk += CT / 64) {
-        // round-robin: position 0 holds player 0, position x >= 1 player 1 + (x - 1 + round) mod (np - 1)
-        auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (np - 1); };
-        int p = player(pk), q = player(np - 1 - pk);
+      // round-robin: position 0 holds player 0, position x >= 1 player 1 + (x - 1 + round) mod (np - 1)
+      auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (np - 1); };
+      int p = 0, q = 0;
+      if (jp < npairs) {
+        p = player(jp);
+        q = player(np - 1 - jp);
         if (p > q) { const int x = p; p = q; q = x; }
         T al = 0, be = 0, ga = 0;
-        for (int r = lane; r < np; r += 64) {
+        for (int r = jpart; r < np; r += JPARTS) {
           const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
           al += mp * mp;
           be += mq * mq;
           ga += mp * mq;
         }
-        al = wave_sum(al);
-        be = wave_sum(be);
-        ga = wave_sum(ga);
+        gram[3 * tid] = al;
+        gram[3 * tid + 1] = be;
+        gram[3 * tid + 2] = ga;
+      }
+      __syncthreads();
+      if (tid < npairs) {
+        T al = 0, be = 0, ga = 0;
+        for (int x = 0; x < JPARTS; ++x) {
+          al += gram[3 * (tid * JPARTS + x)];
+          be += gram[3 * (tid * JPARTS + x) + 1];
+          ga += gram[3 * (tid * JPARTS + x) + 2];
+        }
+        T cs = 1, sn = 0;
         const T den = sqrt(al * be);
         if (den > T(0) && fabs(ga) > conv * den) {
-          off = fmax(off, fabs(ga) / den);
+          if (fabs(ga) / den > offw[1 + (tid & 31)]) offw[1 + (tid & 31)] = fabs(ga) / den;
           const T zeta = (be - al) / (T(2) * ga);
           const T tt = (zeta >= T(0) ? T(1) : T(-1)) / (fabs(zeta) + sqrt(T(1) + zeta * zeta));
-          const T cs = T(1) / sqrt(T(1) + tt * tt), sn = cs * tt;
-          for (int r = lane; r < np; r += 64) {
+          cs = T(1) / sqrt(T(1) + tt * tt);
+          sn = cs * tt;
+        }
+        rot[2 * tid] = cs;
+        rot[2 * tid + 1] = sn;
+      }
+      __syncthreads();
+      if (jp < npairs) {
+        const T cs = rot[2 * jp], sn = rot[2 * jp + 1];
+        if (sn != T(0))
+          for (int r = jpart; r < np; r += JPARTS) {
             const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
             Ms[r + p * S_MAX] = cs * mp - sn * mq;
             Ms[r + q * S_MAX] = sn * mp + cs * mq;
-            const T jp = Js[r + p * S_MAX], jq = Js[r + q * S_MAX];
-            Js[r + p * S_MAX] = cs * jp - sn * jq;
-            Js[r + q * S_MAX] = sn * jp + cs * jq;
+            const T jpv = Js[r + p * S_MAX], jqv = Js[r + q * S_MAX];
+            Js[r + p * S_MAX] = cs * jpv - sn * jqv;
+            Js[r + q * S_MAX] = sn * jpv + cs * jqv;
           }
-        }
       }
       __syncthreads();
     }
-    if (lane == 0) offw[wave] = off;
-    __syncthreads();
+    // largest |cos| of the sweep (each pair thread kept its own maximum)
     T mx = 0;
-#pragma unroll
-    for (int w = 0; w < CT / 64; ++w) mx = fmax(mx, offw[w]);
+    for (int x = 0; x < 32; ++x) mx = fmax(mx, offw[1 + x]);
+    __syncthreads();
+    if (tid < 32) offw[1 + tid] = 0;
     __syncthreads();
     if (mx <= conv) break;
   }
@@ -295,34 +441,83 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   }
 }
 
-// Prefix sums of the ranks (one thread): outer offsets in tile-row order,
-// inner offsets in tile-column order; info[0] = columns in all, info[1] =
-// tiles flagged, info[2] = 1 when the columns exceed the capacity.
-__global__ void rank_scan_kernel(const int32_t *ranks, const int32_t *flags, int qr, int qc, int skip_diag,
-                                 int64_t *ooff, int64_t *ioff, int64_t capacity, int32_t *info) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int64_t acc = 0;
-  for (int i = 0; i < qr; ++i)
-    for (int j = 0; j < qc; ++j) {
-      const int t = i + j * qr;
-      ooff[t] = acc;
-      if (!(skip_diag && i == j)) acc += ranks[t];
-    }
-  const int64_t total = acc;
-  acc = 0;
-  int nflag = 0;
-  for (int j = 0; j < qc; ++j)
+// Prefix sums of the ranks: outer offsets in tile-row order, inner offsets
+// in tile-column order, one thread per tile row (then per tile column) and
+// one thread for the scan of the q row sums.  info[0] = columns in all,
+// info[1] = tiles flagged, info[2] = 1 when the columns exceed the capacity.
+constexpr int SCAN_THREADS = 256;
+__device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, int skip_diag, int64_t *ooff,
+                                         int64_t *ioff, int64_t *sums, int64_t *total_out) {
+  const int tid = threadIdx.x;
+  // outer: tile (i, j) after every tile of rows < i and tiles (i, j' < j)
+  for (int i = tid; i < qr; i += SCAN_THREADS) {
+    int64_t acc = 0;
+    for (int j = 0; j < qc; ++j) acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
+    sums[i] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
     for (int i = 0; i < qr; ++i) {
-      const int t = i + j * qr;
-      ioff[t] = acc;
-      if (!(skip_diag && i == j)) {
-        acc += ranks[t];
-        nflag += flags[t];
-      }
+      const int64_t x = sums[i];
+      sums[i] = acc;
+      acc += x;
     }
-  info[0] = (int32_t)min<int64_t>(total, 0x7fffffff);
-  info[1] = nflag;
-  info[2] = total > capacity ? 1 : 0;
+    *total_out = acc;
+  }
+  __syncthreads();
+  for (int i = tid; i < qr; i += SCAN_THREADS) {
+    int64_t acc = sums[i];
+    for (int j = 0; j < qc; ++j) {
+      ooff[i + j * qr] = acc;
+      acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
+    }
+  }
+  __syncthreads();
+  // inner: tile (i, j) after every tile of columns < j and tiles (i' < i, j)
+  for (int j = tid; j < qc; j += SCAN_THREADS) {
+    int64_t acc = 0;
+    for (int i = 0; i < qr; ++i) acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
+    sums[j] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int j = 0; j < qc; ++j) {
+      const int64_t x = sums[j];
+      sums[j] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < qc; j += SCAN_THREADS) {
+    int64_t acc = sums[j];
+    for (int i = 0; i < qr; ++i) {
+      ioff[i + j * qr] = acc;
+      acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
+    }
+  }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void rank_scan_kernel(const int32_t *ranks, const int32_t *flags, int qr,
+                                                                int qc, int skip_diag, int64_t *ooff, int64_t *ioff,
+                                                                int64_t *sums, int64_t capacity, int32_t *info) {
+  __shared__ int64_t total;
+  __shared__ int nflag_w[SCAN_THREADS / 64];
+  offsets_by_rows_and_cols(ranks, qr, qc, skip_diag, ooff, ioff, sums, &total);
+  int nf = 0;
+  for (int t = threadIdx.x; t < qr * qc; t += SCAN_THREADS)
+    if (!(skip_diag && t % qr == t / qr)) nf += flags[t];
+  nf = wave_sum(nf);
+  if ((threadIdx.x & 63) == 0) nflag_w[threadIdx.x >> 6] = nf;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int nflag = 0;
+    for (int w = 0; w < SCAN_THREADS / 64; ++w) nflag += nflag_w[w];
+    info[0] = (int32_t)min<int64_t>(total, 0x7fffffff);
+    info[1] = nflag;
+    info[2] = total > capacity ? 1 : 0;
+  }
 }
 
 // Packed output: kept column k of tile t goes to column ooff[t] + k of outer
@@ -364,22 +559,12 @@ __global__ __launch_bounds__(CT) void pack_kernel(const T *X, int64_t ldx, const
 
 // ---- expansion of a stored TLR operand --------------------------------------
 
-// Column offsets of every tile's factors from the device rank table (one thread).
-__global__ void factor_offsets_kernel(const int32_t *ranks, int qr, int qc, int has_diag, int64_t *ooff,
-                                      int64_t *ioff) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int64_t acc = 0;
-  for (int i = 0; i < qr; ++i)
-    for (int j = 0; j < qc; ++j) {
-      ooff[i + j * qr] = acc;
-      if (!(has_diag && i == j)) acc += ranks[i + j * qr];
-    }
-  acc = 0;
-  for (int j = 0; j < qc; ++j)
-    for (int i = 0; i < qr; ++i) {
-      ioff[i + j * qr] = acc;
-      if (!(has_diag && i == j)) acc += ranks[i + j * qr];
-    }
+// Column offsets of every tile's factors from the device rank table.
+__global__ __launch_bounds__(SCAN_THREADS) void factor_offsets_kernel(const int32_t *ranks, int qr, int qc,
+                                                                     int has_diag, int64_t *ooff, int64_t *ioff,
+                                                                     int64_t *sums) {
+  __shared__ int64_t total;
+  offsets_by_rows_and_cols(ranks, qr, qc, has_diag, ooff, ioff, sums, &total);
 }
 
 // C[64 x 64 block of tile t] <- alpha X_t + beta C (C read only when beta != 0):
@@ -457,7 +642,7 @@ struct CompressLayout {
   int qr = 0, qc = 0, s = 0;
   int64_t ntile = 0;
   size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, ooff = 0,
-         ioff = 0, total = 0;
+         ioff = 0, sums = 0, total = 0;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -483,6 +668,7 @@ CompressLayout compress_layout(int64_t rows, int64_t cols, int64_t b, int max_ra
   L.flags = o; o += al256((size_t)L.ntile * 4);
   L.ooff = o; o += al256((size_t)L.ntile * 8);
   L.ioff = o; o += al256((size_t)L.ntile * 8);
+  L.sums = o; o += al256((size_t)std::max(L.qr, L.qc) * 8);
   L.total = o;
   return L;
 }
@@ -498,7 +684,7 @@ tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t
 }
 
 template <typename T>
-T conv_tol() { return sizeof(T) == 8 ? T(1e-14) : T(1e-6f); }
+T conv_tol() { return sizeof(T) == 8 ? T(1e-12) : T(1e-5f); }   // |cos| between kept columns after Jacobi
 
 #define CHECK_LAUNCH(what)                                                                     \
   do {                                                                                         \
@@ -549,16 +735,23 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
                        ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
   // 2. Y_t = Q R, Q kept in place
-  hipLaunchKernelGGL(qr_tiles_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.y), (int)b, panel, (T *)nullptr, L.qr,
-                     L.qc, rows, cols, b, 0, n, skip);
+  const bool staged = b <= QR_ROWS && b * n <= QrPanel<T>::ELEMS;
+  auto qr_launch = [&](T *A, T *R, int m_sel) {
+    if (staged)
+      hipLaunchKernelGGL((qr_tiles_kernel<T, true>), dim3(nt), dim3(QR_STAGED_THREADS), 0, s, A, (int)b, panel, R,
+                         L.qr, L.qc, rows, cols, b, m_sel, n, skip);
+    else
+      hipLaunchKernelGGL((qr_tiles_kernel<T, false>), dim3(nt), dim3(CT), 0, s, A, (int)b, panel, R, L.qr, L.qc,
+                         rows, cols, b, m_sel, n, skip);
+  };
+  qr_launch(as<T>(w + L.y), (T *)nullptr, 0);
   CHECK_LAUNCH("QR of the sketches");
   // 3. Bt_t = X_t^T Q_t                      (s_j x s)
   st = gemm(1, 0, ta(0, 1, ldx, 0, ldx, BASE_A_OUTER, 1), ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0),
             ta(wsoff(L.bt), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_K : LOAD_SINGLE);
   if (st != TLR_OK) return st;
   // 4. Bt_t = Q2 R2
-  hipLaunchKernelGGL(qr_tiles_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.bt), (int)b, panel, as<T>(w + L.r2),
-                     L.qr, L.qc, rows, cols, b, 1, n, skip);
+  qr_launch(as<T>(w + L.bt), as<T>(w + L.r2), 1);
   CHECK_LAUNCH("QR of the projections");
   // 5. Jacobi on M = R2^T, ranks
   hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.r2), as<T>(w + L.w),
@@ -573,8 +766,9 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
             ta(wsoff(L.vf), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
   // 7. offsets, 8. packed factors and diagonal slots
-  hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(64), 0, s, as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
-                     L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff), capacity, info);
+  hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, as<int32_t>(w + L.ranks),
+                     as<int32_t>(w + L.flags), L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
+                     as<int64_t>(w + L.sums), capacity, info);
   CHECK_LAUNCH("rank scan");
   hipLaunchKernelGGL(pack_kernel<T>, dim3(nt), dim3(CT), 0, s, static_cast<const T *>(X), ldx, as<T>(w + L.uf),
                      as<T>(w + L.vf), panel, as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks),
@@ -591,7 +785,9 @@ tlr_status expand_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const i
   const int64_t nt = (int64_t)qr * qc;
   int64_t *ooff = static_cast<int64_t *>(ws);
   int64_t *ioff = ooff + nt;
-  hipLaunchKernelGGL(factor_offsets_kernel, dim3(1), dim3(64), 0, s, ranks, qr, qc, has_diag, ooff, ioff);
+  int64_t *sums = ioff + nt;
+  hipLaunchKernelGGL(factor_offsets_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, ranks, qr, qc, has_diag, ooff, ioff,
+                     sums);
   CHECK_LAUNCH("factor offsets");
   const int bpd = (int)((b + EB - 1) / EB);
   const int bpt = bpd * bpd;
@@ -649,8 +845,9 @@ tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t h
   if (rows == 0 || cols == 0) return TLR_OK;
   if (!C || !X || !ranks || !ws) return fail(TLR_ERR_INVALID_ARG, "expand: null buffer");
   if (has_diag && !X->diag) return fail(TLR_ERR_INVALID_ARG, "expand: null diagonal");
-  const int64_t nt = ((rows + b - 1) / b) * ((cols + b - 1) / b);
-  if (ws_bytes < (size_t)(16 * nt)) return fail(TLR_ERR_WORKSPACE, "expand: workspace below 16 bytes per tile");
+  const int64_t qrr = (rows + b - 1) / b, qcc = (cols + b - 1) / b, nt = qrr * qcc;
+  if (ws_bytes < (size_t)(16 * nt + 8 * std::max(qrr, qcc)))
+    return fail(TLR_ERR_WORKSPACE, "expand: workspace below 16 bytes per tile plus 8 per tile row or column");
   if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(TLR_ERR_INVALID_ARG, "expand: workspace not 8-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64) return expand_t<double>(rows, cols, b, has_diag, ranks, X, alpha, beta, C, ldc, ws, s);
