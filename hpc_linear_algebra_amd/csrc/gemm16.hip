@@ -2,7 +2,8 @@
 //
 // The same task tables as the 32/64-bit kernel (tlr_desc.h): each workgroup
 // reads one entry (task, m0, n0) and computes a 128 x BN block of that task's
-// output (BN = 128 or 64, chosen per launch), accumulating over the task's K
+// output (BN = 128 or 64, chosen per launch; the final update uses a second
+// kernel with 256 x 256 blocks, further down), accumulating over the task's K
 // segments in float with v_mfma_f32_16x16x32_{f16,bf16}, then writes
 // C = alpha*acc + beta*C (final update) or C = acc (workspace intermediates),
 // rounded once to the 16-bit type.
@@ -290,6 +291,312 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
   }
 }
 
+// ---- 256 x 256 blocks for the final update ----------------------------------
+//
+// A 128 x 128 block moves one operand byte from L2 into LDS per 64 flops; at
+// the 16-bit matrix-core rate that is more traffic than the caches deliver,
+// so the final update (the launch with long K and whole output tiles) runs in
+// 256 x 256 blocks instead.  Eight wave64s, two per SIMD, each own 128 x 64
+// of the block (8 x 4 MFMA tiles: 128 accumulator registers, half of what a
+// wave may hold at two waves per SIMD; one workgroup per CU).
+//
+// The two waves of a SIMD take turns.  Waves 0-3 (group 0) multiply while
+// waves 4-7 (group 1) read their next fragments from LDS, store an operand
+// stage into LDS and issue the global loads of a later one; at a barrier the
+// roles swap.  One wave then keeps the SIMD's matrix pipe busy while the other
+// waits on memory.  Group 0 copies the A tiles, group 1 the B tiles.  Stage s
+// (32 k, counted over both K segments of the task) lives in LDS buffer s % 2:
+//   phase 2s:    group 0 multiplies stage s; group 1 reads the fragments of
+//                stage s, stores B(s+1), loads B(s+2)
+//   phase 2s+1:  group 1 multiplies stage s; group 0 reads the fragments of
+//                stage s+1, stores A(s+2), loads A(s+3)
+// so stage s's buffer is read in phases 2s-1 and 2s and refilled (stage s+2)
+// in phases 2s+1 and 2s+2, on the other side of a barrier.
+//
+// LDS rows hold 32 k (64 bytes) unpadded, the 16-byte chunk c of row L at
+// position c ^ ((L >> 1) & 3): the fragment reads of 8 consecutive rows touch
+// 8 distinct 16-byte bank groups.  Rows of both tiles are placed by a_lds_row,
+// so a lane ends with 8 consecutive rows of C; in the B tile that only
+// renames which lane owns which output column.  The loading units are laid
+// out so that lanes 0-7 and 8-15 of a store instruction write rows of
+// opposite parity (the other half of the banks), and every store of a unit
+// sits at one of four per-thread bases plus a constant.
+constexpr int BW = BW16;         // wide block rows and columns (256)
+constexpr int NTW = 512;         // eight wave64s
+constexpr int WROW = 32;         // LDS row stride of the wide kernel (elements)
+constexpr int WTILE = BW * WROW; // elements of one operand tile of a stage
+
+// Block column held by lane r of 16 x 16 tile j in a wave's 64 columns: the
+// inverse of a_lds_row on LDS row 16 j + r.
+__device__ __forceinline__ int wide_col(int j, int r) {
+  return 32 * (j >> 1) + 16 * ((r >> 3) & 1) + 8 * ((r >> 2) & 1) + 4 * (j & 1) + (r & 3);
+}
+
+// One thread's share of an operand stage (256 rows of the A tile or columns of
+// the B tile, 32 k), uidx = 0..255 within its group.  K-contiguous operand:
+// rows 4a .. 4a+3 at k 8b .. 8b+7 (a = uidx / 4, b = uidx % 4), vector e
+// holding row 4a + (e ^ (a & 1)).  Otherwise: k 4b .. 4b+3 at rows 8a .. 8a+7
+// (a = uidx / 8, b = uidx % 8), vector e holding k 4b + e.
+struct WSeg {
+  const uint16_t *base;   // the segment's operand at (row 0 of the block, k 0)
+  int64_t kstep;          // elements per stage along k
+  uint32_t off0, off1;    // byte offsets of the thread's vectors 0 and 1; vectors 2, 3 lie two ld further
+  uint32_t ldb2;          // two leading dimensions, in bytes
+  int K;
+  bool kc;
+};
+
+__device__ __forceinline__ WSeg wide_seg(const DevSeg &d, bool is_a, int uidx, int first, const Bases &bases) {
+  const DevOperand &o = is_a ? d.a : d.b;
+  WSeg u;
+  const uint16_t *p = static_cast<const uint16_t *>(bases.p[o.base]) + o.off;
+  const int64_t ld = o.ld;
+  // A: trans 1 = K-contiguous; B: trans 0 = K-contiguous
+  u.kc = is_a ? o.trans == 1 : o.trans == 0;
+  u.base = u.kc ? p + (int64_t)first * ld : p + first;
+  u.kstep = u.kc ? KS : (int64_t)KS * ld;
+  u.ldb2 = (uint32_t)(ld * 4);
+  // strided index of vector e: s0 + (e ^ sx); contiguous index c0
+  const int s0 = u.kc ? 4 * (uidx >> 2) : 4 * (uidx & 7), sx = u.kc ? (uidx >> 2) & 1 : 0;
+  const int c0 = u.kc ? 8 * (uidx & 3) : 8 * (uidx >> 3);
+  u.off0 = (uint32_t)(((int64_t)(s0 + sx) * ld + c0) * 2);
+  u.off1 = (uint32_t)(((int64_t)(s0 + (1 ^ sx)) * ld + c0) * 2);
+  u.K = d.K;
+  return u;
+}
+
+// rem: rows (A) or columns (B) of the task from the block origin
+__device__ __forceinline__ void wide_load(const WSeg &u, int st, int uidx, int rem, u4 (&x)[4]) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc16(u.base + (int64_t)st * u.kstep);
+  const int krem = u.K - st * KS;
+  const int s0 = u.kc ? 4 * (uidx >> 2) : 4 * (uidx & 7), sx = u.kc ? (uidx >> 2) & 1 : 0;
+  const int c0 = u.kc ? 8 * (uidx & 3) : 8 * (uidx >> 3);
+  const int s_lim = u.kc ? rem : krem, c_lim = u.kc ? krem : rem;
+  const bool cok = c0 < c_lim;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = cok && s0 + (e ^ sx) < s_lim;
+    const uint32_t off = ((e & 1) ? u.off1 : u.off0) + (uint32_t)(e >> 1) * u.ldb2;
+    x[e] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : OOB16, 0, 0));
+  }
+}
+
+// LDS stores of a unit, rows placed by a_lds_row (offsets in elements, 32
+// per row).  Transposed unit (rows 8a .. 8a+7): instruction i = 4 i2 + 2 i1 + i0
+// writes row m = 8a + (i ^ odd) (odd = a & 1), i.e. LDS row
+//   L = 32 (a >> 2) + 16 i2 + 4 (a & 3) + 2 i1 + (i0 ^ odd),
+// chunk (b >> 1) ^ i1 ^ 2 odd, half b & 1.  K-contiguous unit (rows 4a .. 4a+3):
+// vector e = 2 e1 + e0 is row m = 4a + 2 e1 + (e0 ^ odd), LDS row
+//   L = 32 (a >> 3) + 16 odd + 4 ((a >> 1) & 3) + 2 e1 + (e0 ^ odd),
+// chunk b ^ e1 ^ 2 ((a >> 1) & 1).
+__device__ __forceinline__ void wide_store(uint16_t *tile, bool kc, int uidx, const u4 (&x)[4]) {
+  if (kc) {
+    const int a = uidx >> 2, b = uidx & 3, odd = a & 1;
+    const int base = WROW * (32 * (a >> 3) + 16 * odd + 4 * ((a >> 1) & 3));
+    const int ch = b ^ (2 * ((a >> 1) & 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int e1 = e >> 1, e0 = e & 1;
+      *reinterpret_cast<u4 *>(tile + base + 2 * WROW * e1 + WROW * (e0 ^ odd) + 8 * (ch ^ e1)) = x[e];
+    }
+  } else {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const int a = uidx >> 3, b = uidx & 7, odd = a & 1;
+    const int base = WROW * (32 * (a >> 2) + 4 * (a & 3)) + 4 * (b & 1);
+    const int ch = (b >> 1) ^ (2 * odd);
+    // row c of the unit sits in dword c >> 1 of each vector, low half for even
+    // c (selector 0x05040100), high half for odd c (0x07060302); c = i ^ odd
+    const uint32_t sel_even = odd ? 0x07060302u : 0x05040100u, sel_odd = odd ? 0x05040100u : 0x07060302u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int i2 = i >> 2, i1 = (i >> 1) & 1, i0 = i & 1;
+      const uint32_t sel = i0 ? sel_odd : sel_even;
+      u2 y;
+      y[0] = __builtin_amdgcn_perm(x[1][i >> 1], x[0][i >> 1], sel);
+      y[1] = __builtin_amdgcn_perm(x[3][i >> 1], x[2][i >> 1], sel);
+      *reinterpret_cast<u2 *>(tile + base + 16 * WROW * i2 + 2 * WROW * i1 + WROW * (i0 ^ odd) + 8 * (ch ^ i1)) = y;
+    }
+  }
+}
+
+template <typename H>
+__device__ __forceinline__ void gemm_block16w(const DevTask &t, int m0, int n0, const int64_t *coltab,
+                                              const Bases &bases, float alpha, float beta, float cscale) {
+  // [buffer][A tile, B tile]
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2 * WTILE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                 // 0: copies A, multiplies first; 1: copies B
+  const int wm = wave & 1, wn = wave >> 1;   // the wave's 128 x 64: rows 128 wm.., columns 64 wn..
+  const int r = lane & 15, g = lane >> 4;
+  const int M = t.M, N = t.N;
+
+  uint16_t *C = static_cast<uint16_t *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
+  const bool fin = t.final_ != 0;
+  const bool preload = fin && cscale != 0.0f;
+  const bool rd = fin && beta != 0.0f && !preload;
+  auto out_col = [&](int n) -> int64_t { return t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n]; };
+
+  // stages over both K segments
+  const int K0 = t.nseg > 0 ? t.seg[0].K : 0, K1 = t.nseg > 1 ? t.seg[1].K : 0;
+  const int nst0 = K0 > 0 ? (K0 + KS - 1) / KS : 0, nst1 = K1 > 0 ? (K1 + KS - 1) / KS : 0;
+  const int S = nst0 + nst1;
+  const int uidx = tid & 255;
+  const int first = grp == 0 ? m0 : n0, rem = grp == 0 ? M - m0 : N - n0;
+  WSeg u0, u1;
+  if (nst0 > 0) u0 = wide_seg(t.seg[0], grp == 0, uidx, first, bases);
+  if (nst1 > 0) u1 = wide_seg(t.seg[1], grp == 0, uidx, first, bases);
+  // The unit's addresses are recomputed from an opaque copy of uidx at each
+  // use: hoisted out of the K loop they would hold more registers than the
+  // accumulators leave.
+  auto fresh = [](int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto load = [&](int s, u4(&x)[4]) {
+    if (s < nst0) wide_load(u0, s, fresh(uidx), rem, x);
+    else wide_load(u1, s - nst0, fresh(uidx), rem, x);
+  };
+  auto store = [&](int s, const u4(&x)[4]) {
+    wide_store(&lds[s & 1][grp * WTILE], s < nst0 ? u0.kc : u1.kc, fresh(uidx), x);
+  };
+
+  // the first two stages' loads go out before the C preload
+  u4 x0[4], x1[4];
+  if (S > 0) load(0, x0);
+  if (S > 1) load(1, x1);
+
+  f4 acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 64 * wn + wide_col(j, r);
+    const int64_t oc = n < N ? out_col(n) : 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      acc[2 * h][j] = f4{0, 0, 0, 0};
+      acc[2 * h + 1][j] = f4{0, 0, 0, 0};
+      const int m = m0 + 128 * wm + 32 * h + 8 * g;
+      if (preload && n < N && m < M) {
+        const u4 c = *reinterpret_cast<const u4 *>(C + oc + m);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[2 * h + (e >> 2)][j][e & 3] = cscale * to_f<H>((uint16_t)(c[e >> 1] >> (16 * (e & 1))));
+      }
+    }
+  }
+
+  if (S > 0) {
+    u4 af[8], bf[4];
+    // fragment rows 128 wm + 16 i + r and 64 wn + 16 j + r: (row >> 1) & 3 is (r >> 1) & 3
+    const int fa = (128 * wm + r) * WROW + 8 * (g ^ ((r >> 1) & 3));
+    const int fb = WTILE + (64 * wn + r) * WROW + 8 * (g ^ ((r >> 1) & 3));
+    auto read_frags = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u4 *>(&lds[buf][fa + 16 * WROW * i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u4 *>(&lds[buf][fb + 16 * WROW * j]);
+    };
+    auto multiply = [&]() {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
+    };
+    // A phase ends at a barrier that nothing may cross: left to itself the
+    // scheduler sinks MFMAs below the barrier into the memory phase, where the
+    // old and new fragments are then live together.
+    auto phase_end = []() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Global loads run two stages ahead of their LDS stores, in two register
+    // sets: the memory slot of iteration t stores from set t % 2 and refills it.
+    // Prologue: stage 0 and A(1) in LDS; group 0 holds A(2), A(3) in sets
+    // 0, 1 and group 1 holds B(1), B(2).
+    store(0, x0);
+    if (grp == 0) {
+      if (S > 1) store(1, x1);
+      if (S > 2) load(2, x0);
+      if (S > 3) load(3, x1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x0[e] = x1[e];
+      if (S > 2) load(2, x1);
+    }
+    // One loop for both groups, group 1 one phase ahead in barriers: iteration
+    // t is (compute slot, memory slot) = phases (2t, 2t+1) for group 0 and
+    // (2t-1, 2t) for group 1, whose first compute slot is the prologue's.  So
+    // group 0 meets the prologue barrier before the loop and group 1 meets
+    // group 0's last barrier after it: both execute 2S + 3 barriers.
+    if (grp == 0) {
+      phase_end();
+      read_frags(0);
+    }
+    auto iteration = [&](int t, u4(&xs)[4]) {
+      const int c = t - grp;         // stage multiplied
+      if (c >= 0 && c < S) multiply();
+      phase_end();
+      const int q = t + 1 - grp;     // stage whose fragments are read next
+      if (q < S) read_frags(q & 1);
+      if (q + 1 < S) store(q + 1, xs);
+      if (q + 3 < S) load(q + 3, xs);
+      phase_end();
+    };
+    for (int t = 0; t <= S; t += 2) {
+      iteration(t, x0);
+      if (t + 1 <= S) iteration(t + 1, x1);
+    }
+    if (grp == 1) phase_end();
+  }
+
+  // epilogue: lane (r, g) holds rows 128 wm + 32 h + 8 g .. +7 of each of its columns
+  // (the column offsets are computed anew rather than kept from the preload)
+  const int re = fresh(r);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 64 * wn + wide_col(j, re);
+    if (n >= N) continue;
+    const int64_t oc = out_col(n);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int m = m0 + 128 * wm + 32 * h + 8 * g;
+      if (m >= M) continue;
+      u4 *q = reinterpret_cast<u4 *>(C + oc + m);
+      u4 old = u4{0, 0, 0, 0};
+      if (rd) old = *q;
+      u4 z;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float v0 = acc[2 * h + (w >> 1)][j][2 * (w & 1)];
+        float v1 = acc[2 * h + (w >> 1)][j][2 * (w & 1) + 1];
+        if (fin) {
+          v0 *= alpha;
+          v1 *= alpha;
+          if (rd) {
+            v0 += beta * to_f<H>((uint16_t)(old[w] & 0xffffu));
+            v1 += beta * to_f<H>((uint16_t)(old[w] >> 16));
+          }
+        }
+        z[w] = (uint32_t)from_f<H>(v0) | ((uint32_t)from_f<H>(v1) << 16);
+      }
+      *q = z;
+    }
+  }
+}
+
+template <typename H>
+__global__ __launch_bounds__(NTW) void wide_gemm16_kernel(const DevTask *__restrict__ tasks,
+                                                          const DevTile *__restrict__ tiles,
+                                                          const int64_t *__restrict__ coltab, Bases bases,
+                                                          float alpha, float beta, float cscale) {
+  const DevTile e = tiles[blockIdx.x];
+  if (e.task < 0) return;
+  const DevTask &t = tasks[e.task];
+  const bool fin = t.final_ != 0;
+  gemm_block16w<H>(t, e.m0, e.n0, coltab, bases, fin ? alpha : 1.0f, fin ? beta : 0.0f, fin ? cscale : 0.0f);
+}
+
 template <typename H, int STAGE, int NJ>
 __global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(4)))
 void grouped_gemm16_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
@@ -340,7 +647,9 @@ template <typename H>
 void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                 const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const float a = (float)alpha, b = (float)beta, c = preload_scale16(alpha, beta);
-  if (bn == Blk16<2>::BN)
+  if (bn == BW)
+    hipLaunchKernelGGL(wide_gemm16_kernel<H>, dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
+  else if (bn == Blk16<2>::BN)
     launch16_w<H, 2>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
   else
     launch16_w<H, 4>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
@@ -351,7 +660,8 @@ void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tas
 int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
                      const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
   if (n_tiles <= 0) return 0;
-  if (bn != Blk16<2>::BN && bn != Blk16<4>::BN) return (int)hipErrorInvalidValue;
+  if (bn != Blk16<2>::BN && bn != Blk16<4>::BN && bn != BW) return (int)hipErrorInvalidValue;
+  if (bn == BW && stage != 3) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F16)
     launch16_t<_Float16>(stage, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);

@@ -554,7 +554,9 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   const int32_t task0 = (int32_t)p.tasks.size();
   L.task_off = task0;
   L.bn = launch_bn(stage, tl);
-  const int bn = L.bn;
+  L.bm = BM;
+  if (stage == 3 && p.es == 2) L.bm = L.bn = BW16;   // the 16-bit final update: 256 x 256 blocks
+  const int bm = L.bm, bn = L.bn;
   struct TaskCost { int32_t t; int64_t per_block, blocks; int mode; };
   std::vector<TaskCost> order;
   for (size_t t = 0; t < tl.t.size(); ++t) {
@@ -563,7 +565,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
     L.executed_flops += task_exec_flops(d);
     int64_t K = 0;
     for (int s = 0; s < d.nseg; ++s) K += d.seg[s].K;
-    const int64_t blocks = ceil_div(d.M, BM) * ceil_div(d.N, bn);
+    const int64_t blocks = ceil_div(d.M, bm) * ceil_div(d.N, bn);
     // one block costs its K steps plus a fixed share for the C update
     order.push_back({(int32_t)t, K + 32, blocks, task_load_mode(d)});
     p.tasks.push_back(d);
@@ -579,7 +581,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
       int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
       load[x] += c.per_block * c.blocks;
       const DevTask &d = tl.t[c.t];
-      for (int64_t m0 = 0; m0 < d.M; m0 += BM)
+      for (int64_t m0 = 0; m0 < d.M; m0 += bm)
         for (int64_t n0 = 0; n0 < d.N; n0 += bn)
           xl[x].push_back(DevTile{task0 + c.t, (int32_t)m0, (int32_t)n0, 0});
     }
@@ -606,7 +608,7 @@ static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &si
                         TaskList &l3) {
   const int a = emit_launch(p, 1, group, rect, l1);
   const int d = emit_launch(p, STAGE_SIDE, group, rect, side);
-  const int b = emit_launch(p, 2, group, rect, l2);
+  emit_launch(p, 2, group, rect, l2);
   const int c = emit_launch(p, 3, group, rect, l3);
   if (d < 0) return;
   // fork before the coupling launch, so that the side launch runs beside
@@ -1000,10 +1002,12 @@ static tlr_status validate(const Plan &p, bool deep) {
   // workgroup tables: each block of each task exactly once
   std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), -1);
   for (const Launch &L : p.launches) {
-    if ((L.bn != BN && L.bn != BN_NARROW) || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
-      return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block width or task range");
+    const bool shape_ok = L.bm == BM ? (L.bn == BN || L.bn == BN_NARROW)
+                                     : (L.bm == BW16 && L.bn == BW16 && L.stage == 3 && p.es == 2);
+    if (!shape_ok || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
+      return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block shape or task range");
     for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t)
-      want[t] = ceil_div(p.tasks[t].M, BM) * ceil_div(p.tasks[t].N, L.bn);
+      want[t] = ceil_div(p.tasks[t].M, L.bm) * ceil_div(p.tasks[t].N, L.bn);
   }
   for (const Launch &L : p.launches) {
     if (L.tile_off < 0 || L.tile_off + L.n_tiles > (int64_t)p.tiles.size() || L.n_tiles % NUM_XCD)
@@ -1029,7 +1033,7 @@ static tlr_status validate(const Plan &p, bool deep) {
         return fail(TLR_ERR_INVALID_ARG, "internal: task in the table of a load mode it does not qualify for");
       if (x.task < L.task_off || x.task >= L.task_off + L.n_tasks)
         return fail(TLR_ERR_INVALID_ARG, "internal: workgroup entry of another launch's task");
-      if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % BM || x.n0 % L.bn)
+      if (x.m0 < 0 || x.n0 < 0 || x.m0 >= d.M || x.n0 >= d.N || x.m0 % L.bm || x.n0 % L.bn)
         return fail(TLR_ERR_INVALID_ARG, "internal: bad block origin");
       seen[x.task]++;
     }
