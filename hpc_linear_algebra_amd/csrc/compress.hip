@@ -157,17 +157,20 @@ __device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *
   }
 }
 
-// The same QR for a panel held in LDS, by NTH = 512 threads, with no wave
-// reductions in the inner loops: for reflector k, w = A[k:m, k+1:n]^T v is
-// formed as 8 partial sums per column (thread (column, part) adds rows
-// part, part + 8, ...) combined through LDS, then every thread applies its
-// share of the rank-1 update A -= beta v w^T.  Q is formed backwards the
-// same way.
+// The same QR for a panel held in LDS (column stride ld), by NTH = 512
+// threads: for reflector k, w = A[k:m, k+1:n]^T v is formed as 8 partial
+// sums per column (thread (column, part) adds rows part, part + 8, ..., four
+// rows per step with the loads first) combined by shuffles among the 8 lanes
+// of the column, then every thread applies its share of the rank-1 update
+// A -= beta v w^T, four columns per step.  Q is formed backwards the same
+// way.  A wave's partial sums read 8 rows of 8 columns; with ld = m + 8 two
+// neighbouring columns sit on complementary halves of the banks (at
+// ld = m = 256 all eight fell on the same banks).
 constexpr int QR_STAGED_THREADS = 512;
 constexpr int QR_PARTS = QR_STAGED_THREADS / S_MAX;   // 8 partial sums per column
 constexpr int QR_ROWS = 256;                           // rows of a staged panel (b <= 256); two threads per row
 template <typename T>
-__device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, T *beta_s, T *part, T *wv) {
+__device__ __forceinline__ void qr_panel_lds(T *a, int m, int ld, T *rr, int n, T *red, T *beta_s, T *wv) {
   constexpr int NTH = QR_STAGED_THREADS;
   const int tid = threadIdx.x;
   const int pp = tid % QR_PARTS, cc = tid / QR_PARTS;     // (part, column) of the partial sums
@@ -178,26 +181,32 @@ __device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, 
   auto apply_vt = [&](int k, int r0) {
     const int c = k + 1 + cc;
     T acc = 0;
-    if (c < n)
-      for (int r = r0 + pp; r < m; r += QR_PARTS) acc += a[r + k * m] * a[r + c * m];
-    part[tid] = acc;
-    __syncthreads();
-    if (tid < n) {
-      T w = 0;
-      if (tid > k) {
-        const T *pt = part + (tid - k - 1) * QR_PARTS;
-#pragma unroll
-        for (int x = 0; x < QR_PARTS; ++x) w += pt[x];
+    if (c < n) {
+      // four rows per step, loads first, so that eight LDS loads are in flight
+      T acc1 = 0;
+      int r = r0 + pp;
+      for (; r + 3 * QR_PARTS < m; r += 4 * QR_PARTS) {
+        const T v0 = a[r + k * ld], v1 = a[r + QR_PARTS + k * ld], v2 = a[r + 2 * QR_PARTS + k * ld],
+                v3 = a[r + 3 * QR_PARTS + k * ld];
+        const T y0 = a[r + c * ld], y1 = a[r + QR_PARTS + c * ld], y2 = a[r + 2 * QR_PARTS + c * ld],
+                y3 = a[r + 3 * QR_PARTS + c * ld];
+        acc += v0 * y0 + v2 * y2;
+        acc1 += v1 * y1 + v3 * y3;
       }
-      wv[tid] = w;
+      for (; r < m; r += QR_PARTS) acc += a[r + k * ld] * a[r + c * ld];
+      acc += acc1;
     }
+    // the QR_PARTS partial sums of column c sit in consecutive lanes
+#pragma unroll
+    for (int d = 1; d < QR_PARTS; d <<= 1) acc += __shfl_xor(acc, d, QR_PARTS);
+    if (pp == 0 && c < n) wv[c] = acc;
     __syncthreads();
   };
   for (int k = 0; k < kmax; ++k) {
     T tail = 0;
-    for (int r = k + 1 + tid; r < m; r += NTH) tail += a[r + k * m] * a[r + k * m];
+    for (int r = k + 1 + tid; r < m; r += NTH) tail += a[r + k * ld] * a[r + k * ld];
     tail = block_sum<T, NTH>(tail, red);
-    const T x0 = a[k + k * m];
+    const T x0 = a[k + k * ld];
     const T nrm = sqrt(tail + x0 * x0);
     const T alpha = x0 >= T(0) ? -nrm : nrm;
     const T v0 = x0 - alpha;
@@ -205,7 +214,7 @@ __device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, 
     const T beta = vtv > T(0) ? T(2) / vtv : T(0);
     __syncthreads();
     if (tid == 0) {
-      a[k + k * m] = v0;
+      a[k + k * ld] = v0;
       beta_s[k] = beta;
       if (rr) rr[k + k * n] = alpha;
     }
@@ -216,35 +225,57 @@ __device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, 
     {
       const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
       if (r < m) {
-        const T vb = beta * a[r + k * m];
-        for (int c = k + 1 + h; c < n; c += QR_STAGED_THREADS / QR_ROWS) a[r + c * m] -= vb * wv[c];
+        const T vb = beta * a[r + k * ld];
+        constexpr int CS = QR_STAGED_THREADS / QR_ROWS;   // column step
+        int c = k + 1 + h;
+        for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
+          const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
+                  x3 = a[r + (c + 3 * CS) * ld];
+          const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
+          a[r + c * ld] = x0 - vb * w0;
+          a[r + (c + CS) * ld] = x1 - vb * w1;
+          a[r + (c + 2 * CS) * ld] = x2 - vb * w2;
+          a[r + (c + 3 * CS) * ld] = x3 - vb * w3;
+        }
+        for (; c < n; c += CS) a[r + c * ld] -= vb * wv[c];
       }
     }
     __syncthreads();
     if (rr)
-      for (int c = k + 1 + tid; c < n; c += NTH) rr[k + c * n] = a[k + c * m];
+      for (int c = k + 1 + tid; c < n; c += NTH) rr[k + c * n] = a[k + c * ld];
   }
   for (int c = kmax; c < n; ++c)
-    for (int r = tid; r < m; r += NTH) a[r + c * m] = 0;
+    for (int r = tid; r < m; r += NTH) a[r + c * ld] = 0;
   __syncthreads();
   for (int k = kmax - 1; k >= 0; --k) {
     const T beta = beta_s[k];
     // rows <= k of the columns c > k are zero here: w_c = sum_{r > k} v_r Q[r, c]
     apply_vt(k, k + 1);
-    const T v0 = a[k + k * m];
+    const T v0 = a[k + k * ld];
     {
       // row k of the columns c > k was zero: it becomes -beta w_c v0
       const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
       if (r < m) {
-        const T vb = beta * a[r + k * m];
-        for (int c = k + 1 + h; c < n; c += QR_STAGED_THREADS / QR_ROWS)
-          a[r + c * m] = (r == k ? T(0) : a[r + c * m]) - vb * wv[c];
+        const T vb = beta * a[r + k * ld];
+        const bool top = r == k;   // row k of these columns held R: it starts from zero
+        constexpr int CS = QR_STAGED_THREADS / QR_ROWS;   // column step
+        int c = k + 1 + h;
+        for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
+          const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
+                  x3 = a[r + (c + 3 * CS) * ld];
+          const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
+          a[r + c * ld] = (top ? T(0) : x0) - vb * w0;
+          a[r + (c + CS) * ld] = (top ? T(0) : x1) - vb * w1;
+          a[r + (c + 2 * CS) * ld] = (top ? T(0) : x2) - vb * w2;
+          a[r + (c + 3 * CS) * ld] = (top ? T(0) : x3) - vb * w3;
+        }
+        for (; c < n; c += CS) a[r + c * ld] = (top ? T(0) : a[r + c * ld]) - vb * wv[c];
       }
     }
     __syncthreads();
     for (int r = tid; r < m; r += NTH) {
-      const T vr = a[r + k * m];
-      a[r + k * m] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
+      const T vr = a[r + k * ld];
+      a[r + k * ld] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
     }
     __syncthreads();
   }
@@ -252,10 +283,11 @@ __device__ __forceinline__ void qr_panel_lds(T *a, int m, T *rr, int n, T *red, 
 
 // QR of every tile's m x n panel (tile t at A + t * stride, leading dim lda),
 // m = s_i (m_sel 0) or s_j (m_sel 1); R (optional) at R + t * n * n.  STAGED:
-// the panel is copied into LDS (m * n <= PANEL elements), factorised there and
+// the panel is copied into LDS ((m + QR_PAD) * n <= ELEMS), factorised there and
 // copied back, by 512 threads; otherwise it is factorised in place in global
 // memory by 256 threads.
-template <typename T> struct QrPanel { static constexpr int ELEMS = 131072 / sizeof(T); };   // 128 KiB of LDS
+constexpr int QR_PAD = 8;   // LDS column stride of a staged panel: m + QR_PAD
+template <typename T> struct QrPanel { static constexpr int ELEMS = 135168 / sizeof(T); };   // (256 + 8) x 64 doubles
 
 template <typename T, bool STAGED>
 __global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kernel(
@@ -272,20 +304,22 @@ __global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kern
   T *rr = R ? R + (int64_t)t * n * n : nullptr;
   if constexpr (STAGED) {
     __shared__ T panel[QrPanel<T>::ELEMS];
-    __shared__ T part[QR_STAGED_THREADS];
     __shared__ T wv[S_MAX];
+    const int ld = m + QR_PAD;
     for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
-      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) panel[r + c * m] = a[r + (int64_t)c * lda];
+      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) panel[r + c * ld] = a[r + (int64_t)c * lda];
     __syncthreads();
-    qr_panel_lds<T>(panel, m, rr, n, red, beta_s, part, wv);
+    qr_panel_lds<T>(panel, m, ld, rr, n, red, beta_s, wv);
     for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
-      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) a[r + (int64_t)c * lda] = panel[r + c * m];
+      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) a[r + (int64_t)c * lda] = panel[r + c * ld];
   } else {
     qr_panel<T, NTH>(a, lda, rr, m, n, red, beta_s);
   }
 }
 
-constexpr int JPARTS = CT / 32;   // partial sums per column pair (CT threads, at most 32 pairs)
+// Threads per column pair: 8 consecutive lanes of one wave take rows part,
+// part + 8, ... of a pair and combine their partial sums with lane shuffles.
+constexpr int JPARTS = 8;
 
 // One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
 // then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
@@ -303,8 +337,6 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
   __shared__ T offw[1 + 32];          // [1 + p]: largest |cos| pair thread p met in the sweep
-  __shared__ T gram[3 * CT];
-  __shared__ T rot[2 * 32];
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -325,16 +357,23 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   __syncthreads();
   const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
   const int npairs = np / 2;
-  // thread (pair, part): pair = tid / 8 (at most 32 pairs), rows part, part + 8, ...
+  // thread (pair, part): pair jp = tid / 8 (CT / 8 = 32 pairs at most), rows
+  // part, part + 8, ...  The eight lanes of a pair form its 2 x 2 Gram block,
+  // each computes the rotation and applies it to its own rows: one barrier
+  // per round (the next round pairs columns other waves wrote).
   const int jp = tid / JPARTS, jpart = tid % JPARTS;
+  // Columns whose squared norm is below (n eps)^2 ||X||_F^2 are round-off:
+  // they change no rank decision, and a pair holding one counts as
+  // converged (rotating two such columns never reaches the cosine bound, so
+  // every sweep would run).
+  const T eps = sizeof(T) == 8 ? T(2.220446049250313e-16) : T(1.1920929e-7);
+  const T negligible = (T(n) * eps) * (T(n) * eps) * norms2[t];
   for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
     for (int round = 0; round < np - 1; ++round) {
       // round-robin: position 0 holds player 0, position x >= 1 player 1 + (x - 1 + round) mod (np - 1)
       auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (np - 1); };
-      int p = 0, q = 0;
       if (jp < npairs) {
-        p = player(jp);
-        q = player(np - 1 - jp);
+        int p = player(jp), q = player(np - 1 - jp);
         if (p > q) { const int x = p; p = q; q = x; }
         T al = 0, be = 0, ga = 0;
         for (int r = jpart; r < np; r += JPARTS) {
@@ -343,34 +382,19 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
           be += mq * mq;
           ga += mp * mq;
         }
-        gram[3 * tid] = al;
-        gram[3 * tid + 1] = be;
-        gram[3 * tid + 2] = ga;
-      }
-      __syncthreads();
-      if (tid < npairs) {
-        T al = 0, be = 0, ga = 0;
-        for (int x = 0; x < JPARTS; ++x) {
-          al += gram[3 * (tid * JPARTS + x)];
-          be += gram[3 * (tid * JPARTS + x) + 1];
-          ga += gram[3 * (tid * JPARTS + x) + 2];
+#pragma unroll
+        for (int d = 1; d < JPARTS; d <<= 1) {
+          al += __shfl_xor(al, d, JPARTS);
+          be += __shfl_xor(be, d, JPARTS);
+          ga += __shfl_xor(ga, d, JPARTS);
         }
-        T cs = 1, sn = 0;
         const T den = sqrt(al * be);
-        if (den > T(0) && fabs(ga) > conv * den) {
-          if (fabs(ga) / den > offw[1 + (tid & 31)]) offw[1 + (tid & 31)] = fabs(ga) / den;
+        if (al > negligible && be > negligible && fabs(ga) > conv * den) {
+          if (jpart == 0 && fabs(ga) / den > offw[1 + jp]) offw[1 + jp] = fabs(ga) / den;
           const T zeta = (be - al) / (T(2) * ga);
           const T tt = (zeta >= T(0) ? T(1) : T(-1)) / (fabs(zeta) + sqrt(T(1) + zeta * zeta));
-          cs = T(1) / sqrt(T(1) + tt * tt);
-          sn = cs * tt;
-        }
-        rot[2 * tid] = cs;
-        rot[2 * tid + 1] = sn;
-      }
-      __syncthreads();
-      if (jp < npairs) {
-        const T cs = rot[2 * jp], sn = rot[2 * jp + 1];
-        if (sn != T(0))
+          const T cs = T(1) / sqrt(T(1) + tt * tt);
+          const T sn = cs * tt;
           for (int r = jpart; r < np; r += JPARTS) {
             const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
             Ms[r + p * S_MAX] = cs * mp - sn * mq;
@@ -379,6 +403,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
             Js[r + p * S_MAX] = cs * jpv - sn * jqv;
             Js[r + q * S_MAX] = sn * jpv + cs * jqv;
           }
+        }
       }
       __syncthreads();
     }
@@ -735,7 +760,7 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
                        ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
   // 2. Y_t = Q R, Q kept in place
-  const bool staged = b <= QR_ROWS && b * n <= QrPanel<T>::ELEMS;
+  const bool staged = b <= QR_ROWS && (b + QR_PAD) * n <= QrPanel<T>::ELEMS;
   auto qr_launch = [&](T *A, T *R, int m_sel) {
     if (staged)
       hipLaunchKernelGGL((qr_tiles_kernel<T, true>), dim3(nt), dim3(QR_STAGED_THREADS), 0, s, A, (int)b, panel, R,
