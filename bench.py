@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"f64": 78.6, "f32": 157.3, "f16": 2500.0, "bf16": 2500.0}   # MI355X dense MFMA TFLOP/s (datasheet)
+# vector (non-matrix) ALU peaks: 256 CUs x 2.4 GHz x 128 fp64 / 256 fp32 flops per CU and clock
+VECTOR_PEAK = {"f64": 78.6, "f32": 157.3}
 ES = {"f64": 8, "f32": 4, "f16": 2, "bf16": 2}
 HBM_PEAK_GBS = 8000.0
 METRIC = "TLR GEMM useful TFLOP/s + % of roofline, fp64 TLRxTLR->dense N=16384"
@@ -325,10 +327,12 @@ def bench_tlr_out(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    T.tlr_compress_profile(args.steps)
     w0 = time.perf_counter()
     evs = [step() for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    group_ms, calls = T.tlr_compress_profile_read()
     phases = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in evs])
     total = phases.sum(axis=1)
     ms = float(total.mean())
@@ -338,9 +342,21 @@ def bench_tlr_out(args):
     es = ES[dtype]
     q = R.shape[0]
     out_elems = sum(int(R[i, j]) * (2 * b) for i in range(q) for j in range(q) if i != j) + q * b * b
-    # dominant phase: its rate against its own roofline
     names = ["expand", "product", "compress"]
     dom = int(np.argmax(phases.mean(axis=0)))
+    # the dominant kernel: the panel QR (two launches per step, one per QR of
+    # the sketches and of the projections), bound by its own arithmetic
+    n_s = cfg["max_rank"] + 8           # sketch width
+    sizes = [min(b, N - i * b) for i in range(q)]
+
+    def qr_flops(m, n):
+        # per reflector k: w = A^T v and the rank-1 update on an (m-k) x (n-k-1)
+        # block, in the factorisation and again when Q is formed
+        return sum(8.0 * (m - k) * (n - k - 1) for k in range(min(m, n)))
+    qr_work = sum(qr_flops(sizes[i], n_s) for i in range(q) for j in range(q) if i != j)   # one launch
+    qr_ms = (group_ms[2] + group_ms[4]) / (2 * calls)
+    qr_tf = qr_work / (qr_ms * 1e-3) / 1e12
+    vec_peak = VECTOR_PEAK[dtype]
     cpu = None
     if not args.no_cpu:
         from oracle import recompress as rc
@@ -382,7 +398,11 @@ def bench_tlr_out(args):
                    "rank_max": int(R.max()),
                    "memory_vs_dense": round(out_elems / float(N * N), 4)},
         "dominant_phase": names[dom],
-        "roofline": None,
+        "compress_groups_ms": {g: round(x / calls, 4) for g, x in zip(T.COMPRESS_PROFILE_GROUPS, group_ms)},
+        "roofline": {"bound": "alu", "achieved": round(qr_tf, 3), "peak": vec_peak, "unit": "TFLOP/s",
+                     "frac": round(qr_tf / vec_peak, 4), "traffic": None,
+                     "kernel": "panel QR with explicit Q (two launches per step)", "launch_ms": round(qr_ms, 4),
+                     "algorithmic_flops": qr_work},
         "cpu_baseline": cpu,
     }
     log(f"bench: {ms:.3f} ms/step ({', '.join(f'{n} {phases[:, k].mean():.3f}' for k, n in enumerate(names))}), "

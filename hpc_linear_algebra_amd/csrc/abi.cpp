@@ -235,6 +235,14 @@ tlr_status tlr_compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int
   })
 }
 
+tlr_status tlr_compress_profile(int32_t max_calls) {
+  TLR_GUARD({ return tlr::compress_profile(max_calls); })
+}
+
+tlr_status tlr_compress_profile_read(double *group_ms, int32_t *calls) {
+  TLR_GUARD({ return tlr::compress_profile_read(group_ms, calls); })
+}
+
 tlr_status tlr_plan_profile(tlr_plan *h, int32_t max_executes) {
   if (!h) return tlr::fail(TLR_ERR_INVALID_ARG, "profile: null plan");
   TLR_GUARD({ return tlr::plan_profile(&h->p, max_executes); })

@@ -29,7 +29,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "tlr_plan.h"
 
@@ -711,6 +713,50 @@ tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t
 template <typename T>
 T conv_tol() { return sizeof(T) == 8 ? T(1e-12) : T(1e-5f); }   // |cos| between kept columns after Jacobi
 
+// Optional event pairs around the kernel groups of a compression
+// (tlr_compress_profile): 0 tile norms, 1 sketch product, 2 QR of the
+// sketches, 3 projection product, 4 QR of the projections, 5 Jacobi SVD and
+// ranks, 6 factor products, 7 rank scan, 8 packing.
+struct CompressProfile {
+  std::mutex mu;
+  int remaining = 0;   // calls still to record
+  int calls = 0;       // calls recorded since the last read
+  struct Rec {
+    int group;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+};
+CompressProfile &cprof() {
+  static CompressProfile p;
+  return p;
+}
+
+// Events of one call: begin(g) records the start of group g, end() its end.
+struct ProfileMarks {
+  bool on = false;
+  hipStream_t s = nullptr;
+  std::vector<CompressProfile::Rec> recs;
+  bool begin(int group) {
+    if (!on) return true;
+    CompressProfile::Rec r{group, nullptr, nullptr};
+    if (hipEventCreate(&r.a) != hipSuccess) return false;
+    if (hipEventCreate(&r.b) != hipSuccess) {
+      (void)hipEventDestroy(r.a);
+      return false;
+    }
+    recs.push_back(r);
+    return hipEventRecord(r.a, s) == hipSuccess;
+  }
+  bool end() { return !on || hipEventRecord(recs.back().b, s) == hipSuccess; }
+  ~ProfileMarks() {   // hand the events to the record (their work is enqueued)
+    if (!on) return;
+    CompressProfile &p = cprof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.recs.insert(p.recs.end(), recs.begin(), recs.end());
+  }
+};
+
 #define CHECK_LAUNCH(what)                                                                     \
   do {                                                                                         \
     hipError_t e_ = hipGetLastError();                                                         \
@@ -726,10 +772,27 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   const int n = L.s;
   const int nt = (int)L.ntile;
   const int skip = has_diag ? 1 : 0;
+  ProfileMarks pm;
+  pm.s = s;
+  {
+    CompressProfile &p = cprof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (p.remaining > 0) {
+      --p.remaining;
+      ++p.calls;
+      pm.on = true;
+    }
+  }
+#define MARK(call)                                                                  \
+  do {                                                                              \
+    if (!(call)) return fail(TLR_ERR_HIP, "compress: profiling event failed");     \
+  } while (0)
   T *norms = as<T>(w + L.norms);
+  MARK(pm.begin(0));
   hipLaunchKernelGGL(tile_norms_kernel<T>, dim3(nt), dim3(CT), 0, s, static_cast<const T *>(X), ldx, L.qr, L.qc, rows,
                      cols, b, norms);
   CHECK_LAUNCH("tile norms");
+  MARK(pm.end());
   Bases bases;
   for (auto &p : bases.p) p = nullptr;
   bases.p[BASE_A_OUTER] = X;
@@ -756,9 +819,11 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   const bool even = b % 2 == 0 && rows % 2 == 0 && cols % 2 == 0 && ldx % 2 == 0 && n % 2 == 0 &&
                     reinterpret_cast<uintptr_t>(X) % (2 * es) == 0 && reinterpret_cast<uintptr_t>(omega) % (2 * es) == 0;
   // 1. Y_t = X_t Omega                       (s_i x s)
+  MARK(pm.begin(1));
   tlr_status st = gemm(0, 1, ta(0, 1, ldx, 0, ldx, BASE_A_OUTER, 0), ta(0, 0, 0, 0, b, BASE_B_OUTER, 0),
                        ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
+  MARK(pm.end());
   // 2. Y_t = Q R, Q kept in place
   const bool staged = b <= QR_ROWS && (b + QR_PAD) * n <= QrPanel<T>::ELEMS;
   auto qr_launch = [&](T *A, T *R, int m_sel) {
@@ -769,37 +834,52 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
       hipLaunchKernelGGL((qr_tiles_kernel<T, false>), dim3(nt), dim3(CT), 0, s, A, (int)b, panel, R, L.qr, L.qc,
                          rows, cols, b, m_sel, n, skip);
   };
+  MARK(pm.begin(2));
   qr_launch(as<T>(w + L.y), (T *)nullptr, 0);
   CHECK_LAUNCH("QR of the sketches");
+  MARK(pm.end());
   // 3. Bt_t = X_t^T Q_t                      (s_j x s)
+  MARK(pm.begin(3));
   st = gemm(1, 0, ta(0, 1, ldx, 0, ldx, BASE_A_OUTER, 1), ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0),
             ta(wsoff(L.bt), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_K : LOAD_SINGLE);
   if (st != TLR_OK) return st;
+  MARK(pm.end());
   // 4. Bt_t = Q2 R2
+  MARK(pm.begin(4));
   qr_launch(as<T>(w + L.bt), as<T>(w + L.r2), 1);
   CHECK_LAUNCH("QR of the projections");
+  MARK(pm.end());
   // 5. Jacobi on M = R2^T, ranks
+  MARK(pm.begin(5));
   hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.r2), as<T>(w + L.w),
                      as<T>(w + L.j), as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
                      norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
   CHECK_LAUNCH("Jacobi SVD");
+  MARK(pm.end());
   // 6. U_t = Q_t W_t, V_t = Q2_t J_t        (s_i x s, s_j x s)
+  MARK(pm.begin(6));
   st = gemm(0, 2, ta(wsoff(L.y), 0, 0, panel, b, BASE_WS, 0), ta(wsoff(L.w), 0, 0, (int64_t)n * n, n, BASE_WS, 0),
             ta(wsoff(L.uf), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
   st = gemm(1, 2, ta(wsoff(L.bt), 0, 0, panel, b, BASE_WS, 0), ta(wsoff(L.j), 0, 0, (int64_t)n * n, n, BASE_WS, 0),
             ta(wsoff(L.vf), 0, 0, panel, b, BASE_WS, 0), even ? LOAD_PAIR_M : LOAD_SINGLE);
   if (st != TLR_OK) return st;
+  MARK(pm.end());
   // 7. offsets, 8. packed factors and diagonal slots
+  MARK(pm.begin(7));
   hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, as<int32_t>(w + L.ranks),
                      as<int32_t>(w + L.flags), L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
                      as<int64_t>(w + L.sums), capacity, info);
   CHECK_LAUNCH("rank scan");
+  MARK(pm.end());
+  MARK(pm.begin(8));
   hipLaunchKernelGGL(pack_kernel<T>, dim3(nt), dim3(CT), 0, s, static_cast<const T *>(X), ldx, as<T>(w + L.uf),
                      as<T>(w + L.vf), panel, as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks),
                      as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff), info, L.qr, L.qc, rows, cols, b, n, skip,
                      static_cast<T *>(outer), static_cast<T *>(inner), static_cast<T *>(diag), ranks_out);
   CHECK_LAUNCH("pack");
+  MARK(pm.end());
+#undef MARK
   return TLR_OK;
 }
 
@@ -857,6 +937,34 @@ tlr_status compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t
                               capacity, info, ws, L, s);
   return compress_t<float>(rows, cols, b, has_diag, X, ldx, tol, max_rank, omega, ranks_out, diag, outer, inner,
                            capacity, info, ws, L, s);
+}
+
+tlr_status compress_profile(int32_t max_calls) {
+  if (max_calls < 0) return fail(TLR_ERR_INVALID_ARG, "compress profile: negative call count");
+  CompressProfile &p = cprof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.remaining = max_calls;
+  return TLR_OK;
+}
+
+tlr_status compress_profile_read(double *group_ms, int32_t *calls) {
+  if (!group_ms || !calls) return fail(TLR_ERR_INVALID_ARG, "compress profile: null output");
+  CompressProfile &p = cprof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (int k = 0; k < COMPRESS_PROFILE_GROUPS; ++k) group_ms[k] = 0.0;
+  tlr_status st = TLR_OK;
+  for (const CompressProfile::Rec &r : p.recs) {
+    float ms = 0.0f;
+    if (st == TLR_OK && hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = fail(TLR_ERR_HIP, "compress profile: events not complete (synchronise first)");
+    if (st == TLR_OK && r.group >= 0 && r.group < COMPRESS_PROFILE_GROUPS) group_ms[r.group] += ms;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  *calls = p.calls;
+  p.recs.clear();
+  p.calls = 0;
+  return st;
 }
 
 tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const int32_t *ranks,

@@ -167,6 +167,9 @@ tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t h
                   const tlr_buffers *X, double alpha, double beta, void *C, int64_t ldc, void *ws, size_t ws_bytes,
                   void *stream);
 tlr_status compress_workspace(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t max_rank, size_t *bytes);
+constexpr int COMPRESS_PROFILE_GROUPS = 9;
+tlr_status compress_profile(int32_t max_calls);
+tlr_status compress_profile_read(double *group_ms, int32_t *calls);
 tlr_status compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t has_diag, const void *X, int64_t ldx,
                     double tol, int32_t max_rank, const void *omega, int32_t *ranks_out, void *diag, void *outer,
                     void *inner, int64_t capacity, int32_t *info, void *ws, size_t ws_bytes, void *stream);

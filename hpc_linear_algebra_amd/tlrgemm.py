@@ -29,7 +29,8 @@ EXPORTED = [
     "tlr_gemm_analyze", "tlr_gemm_workspace_bytes", "tlr_plan_info", "tlr_plan_rect",
     "tlr_plan_stage_shapes", "tlr_plan_launch", "tlr_plan_destroy", "tlr_plan_bind",
     "tlr_gemm_execute", "tlr_gemm_execute_noalloc", "tlr_expand", "tlr_compress_workspace_bytes",
-    "tlr_compress", "tlr_plan_profile", "tlr_plan_profile_read", "tlr_dense_gemm",
+    "tlr_compress", "tlr_compress_profile", "tlr_compress_profile_read", "tlr_plan_profile",
+    "tlr_plan_profile_read", "tlr_dense_gemm",
     "tlr_status_string", "tlr_last_error", "tlr_version",
 ]
 
@@ -92,6 +93,8 @@ def lib():
     L.tlr_compress_workspace_bytes.argtypes = [c_int32, c_int64, c_int64, c_int32, c_int32, POINTER(c_size_t)]
     L.tlr_compress.argtypes = [c_int32, c_int64, c_int64, c_int32, c_int32, P, c_int64, c_double, c_int32, P, P,
                                P, P, P, c_int64, P, P, c_size_t, P]
+    L.tlr_compress_profile.argtypes = [c_int32]
+    L.tlr_compress_profile_read.argtypes = [POINTER(c_double), POINTER(c_int32)]
     L.tlr_plan_profile.argtypes = [P, c_int32]
     L.tlr_plan_profile_read.argtypes = [P, POINTER(c_double), POINTER(c_double), POINTER(c_int32)]
     L.tlr_dense_gemm.argtypes = [c_int32, c_int32, c_int32, c_int64, c_int64, c_int64, c_double, P, c_int64,
@@ -267,6 +270,23 @@ def tlr_compress(dtype, rows: int, cols: int, b: int, has_diag: bool, X: int, ld
                             c_void_p(outer or None), c_void_p(inner or None), capacity, c_void_p(info or None),
                             c_void_p(workspace or None), workspace_bytes, c_void_p(stream or None))
     _check(st, "tlr_compress")
+
+
+COMPRESS_PROFILE_GROUPS = ("tile norms", "sketch products", "QR of the sketches", "projections",
+                           "QR of the projections", "Jacobi SVD and ranks", "factor products", "rank scan",
+                           "packing")
+
+
+def tlr_compress_profile(max_calls: int):
+    _check(lib().tlr_compress_profile(max_calls), "tlr_compress_profile")
+
+
+def tlr_compress_profile_read():
+    """(milliseconds per kernel group summed over the recorded calls, calls)."""
+    ms = (c_double * len(COMPRESS_PROFILE_GROUPS))()
+    calls = c_int32()
+    _check(lib().tlr_compress_profile_read(ms, ctypes.byref(calls)), "tlr_compress_profile_read")
+    return list(ms), calls.value
 
 
 def tlr_plan_profile(p: Plan, max_executes: int):

@@ -426,6 +426,22 @@ tlr_status tlr_compress(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int
                         int32_t *ranks_out, void *diag, void *outer, void *inner, int64_t capacity,
                         int32_t *info, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Profiling of the compression (plumbing the pages do not define; it feeds the
+ * measurement).  tlr_compress_profile: record a HIP event pair, on the call's
+ * stream, around each kernel group of the next `max_calls` tlr_compress calls
+ * of the process (0 switches recording off).  Errors: TLR_ERR_INVALID_ARG
+ * (negative count).
+ * tlr_compress_profile_read: after the caller has synchronised, sum the
+ * recorded time per group into group_ms[9]: 0 tile norms, 1 sketch products
+ * X_t Omega, 2 QR of the sketches, 3 projections X_t^T Q_t, 4 QR of the
+ * projections, 5 Jacobi SVD and ranks, 6 factor products, 7 rank scan,
+ * 8 packing; *calls = calls recorded.  Resets the record.  Errors:
+ * TLR_ERR_HIP when an event has not completed.
+ */
+tlr_status tlr_compress_profile(int32_t max_calls);
+tlr_status tlr_compress_profile_read(double *group_ms, int32_t *calls);
+
 /* Static description of a status code (plumbing; the pages define no error
  * handling). */
 const char *tlr_status_string(tlr_status s);

@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LINES = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
 MFMA_PEAK = {"f64": 78.6, "f32": 157.3, "f16": 2500.0, "bf16": 2500.0}   # dense TFLOP/s, datasheet
 HBM_PEAK = 8000.0                                                          # GB/s
+VECTOR_PEAK = {"f64": 78.6, "f32": 157.3}   # vector ALU TFLOP/s: 256 CUs x 2.4 GHz x 128 (fp64) / 256 (fp32) per clock
 
 
 def _load(path):
@@ -52,6 +53,8 @@ def test_bench_line_contract(path):
         assert k in r, k
     if r["bound"] == "mfma":
         assert r["unit"] == "TFLOP/s" and r["peak"] == MFMA_PEAK[d["dtype"]]
+    elif r["bound"] == "alu":
+        assert r["unit"] == "TFLOP/s" and r["peak"] == VECTOR_PEAK[d["dtype"]]
     else:
         assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == HBM_PEAK
     assert math.isclose(r["frac"], r["achieved"] / r["peak"], rel_tol=2e-3)

@@ -119,6 +119,26 @@ def test_compress_recovers_generated_ranks(n, b, diag):
     _check_against_oracle(got, X, 1e-7, "f64", ref_ranks=t.ranks, what=f"compress n={n}")
 
 
+def test_compress_profile_records_each_kernel_group():
+    """tlr_compress_profile times every kernel group of exactly the calls asked
+    for, and recording changes no result."""
+    from hpc_linear_algebra_amd import tlrgemm as T
+    rng = np.random.default_rng(17)
+    t = random_tlr(rng, 300, 300, 64, rank_lo=0, rank_hi=20, has_diag=True, scale=1.0)
+    X = reference.reconstruct(t)
+    T.tlr_compress_profile_read()          # drop anything recorded before
+    T.tlr_compress_profile(1)
+    R1, o1, i1, d1, _ = _compress_on_gpu(X, 64, True, 1e-7, 32)
+    R2, o2, i2, d2, _ = _compress_on_gpu(X, 64, True, 1e-7, 32)   # past the count: not recorded
+    ms, calls = T.tlr_compress_profile_read()
+    say(f"compress profile: calls {calls}, groups {[round(x, 4) for x in ms]}")
+    assert calls == 1 and len(ms) == len(T.COMPRESS_PROFILE_GROUPS)
+    assert all(x > 0 for x in ms)
+    assert np.array_equal(R1, R2) and np.array_equal(o1, o2) and np.array_equal(i1, i2) and np.array_equal(d1, d2)
+    ms, calls = T.tlr_compress_profile_read()
+    assert calls == 0 and all(x == 0 for x in ms)
+
+
 @pytest.mark.parametrize("dtype,tol", [("f64", 1e-6), ("f64", 1e-3), ("f32", 1e-3)])
 def test_tlr_output_product(dtype, tol):
     """C <- alpha A B + beta C on the TLR-output workload's recipe at N = 1000,
