@@ -557,7 +557,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"], sixteen),
                     "kernel": kname, "launch_ms": round(per_launch[dom], 4), "algorithmic_bytes": lbytes,
-                    "mfma_tflops": round(achieved, 3)}
+                    "mfma_tflops": round(achieved, 3),
+                    "mfma_busy": mfma_busy_from_profiles(L["stage"], cfg["name"], sixteen)}
     else:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profiles(L["stage"], cfg["name"], sixteen),

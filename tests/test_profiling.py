@@ -23,6 +23,8 @@ def test_short_names():
         == "grouped_gemm16_kernel<half, 3, 4>"
     assert P._short("_ZN3tlr12_GLOBAL__N_121grouped_gemm16_kernelIDF16bLi2ELi2EEEvPKNS_7DevTaskE") \
         == "grouped_gemm16_kernel<bfloat16, 2, 2>"
+    assert P._short("_ZN3tlr12_GLOBAL__N_118wide_gemm16_kernelIDF16_EEvPKNS_7DevTaskEPKNS_7DevTileE") \
+        == "wide_gemm16_kernel<half>"
     assert P._short("_ZN3tlr12_GLOBAL__N_119grouped_gemm_kernelIfLi1ELi0ELi4EEEvPK") \
         == "grouped_gemm_kernel<float, 1, 0, 4>"
 
