@@ -748,12 +748,25 @@ struct ProfileMarks {
     recs.push_back(r);
     return hipEventRecord(r.a, s) == hipSuccess;
   }
-  bool end() { return !on || hipEventRecord(recs.back().b, s) == hipSuccess; }
-  ~ProfileMarks() {   // hand the events to the record (their work is enqueued)
+  bool end() {
+    if (!on) return true;
+    if (hipEventRecord(recs.back().b, s) != hipSuccess) return false;
+    ++ended;
+    return true;
+  }
+  size_t ended = 0;   // leading records whose end event was recorded
+  ~ProfileMarks() {   // hand the complete pairs to the record; a call that failed midway leaves the rest
     if (!on) return;
     CompressProfile &p = cprof();
     std::lock_guard<std::mutex> g(p.mu);
-    p.recs.insert(p.recs.end(), recs.begin(), recs.end());
+    for (size_t k = 0; k < recs.size(); ++k) {
+      if (k < ended) {
+        p.recs.push_back(recs[k]);
+      } else {
+        (void)hipEventDestroy(recs[k].a);
+        (void)hipEventDestroy(recs[k].b);
+      }
+    }
   }
 };
 
