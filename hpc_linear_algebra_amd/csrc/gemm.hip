@@ -586,6 +586,148 @@ void tile_gemm_kernel(TileGemm g, Bases bases, int mb_per_tile) {
   gemm_block<T, MODE, 8>(task, mb * KBM, 0, nullptr, bases, T(1), T(0), T(0));
 }
 
+// Strip blocks for the right/left product (stage 2).  Its tasks have one K
+// segment of at most one stage (ranks up to 16) and store C = acc through the
+// column map, so their time goes to the stores; a 128 x 128 block spends about
+// as long fetching its few operands as it then spends storing.  A strip block
+// covers 128 rows and STRIP_W columns: it loads its A rows into registers and
+// the B operand and the column offsets of all STRIP_W columns into LDS once,
+// then runs 128-column chunks back to back, each a few MFMAs and then the
+// chunk's stores, with no barrier between chunks, so that the stores of one
+// wave run while the MFMAs of the others do.  B is N-contiguous (the coupling
+// matrix as the planner stores it for this product), which keeps every byte
+// offset of the fill below 2^31 (k < 16, leading dimensions below 2^21).
+constexpr int SPAD = 17;                 // odd LDS row stride, as for the B tiles above
+constexpr int LDS_S = STRIP_W + SPAD;
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void strip_gemm_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
+                       const int64_t *__restrict__ coltab, Bases bases) {
+  typedef typename Mfma<T>::v4 v4;
+  constexpr int NJ = 8, KBN = Blk<NJ>::KBN;
+  static_assert(STRIP_W == 2 * NT && STRIP_W % KBN == 0, "strip fill: two columns per thread");
+  __shared__ T Bs[KBK * LDS_S];
+  __shared__ int64_t cols[STRIP_W];
+  const DevTile e = tiles[blockIdx.x];
+  if (e.task < 0) return;
+  const DevTask &t = tasks[e.task];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave * WM;
+  const int r = lane & 15, g = lane >> 4;
+  const int arow = Mfma<T>::arow(r);
+  const int M = t.M, m0 = e.m0, n0 = e.n0;
+  const int nrem = min(t.N - n0, STRIP_W);
+  const int K = t.nseg > 0 ? t.seg[0].K : 0;   // a task without a segment stores zeros
+  const DevSeg &d = t.seg[0];
+  T *C = static_cast<T *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
+
+  T fa[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fa[i][q] = T(0);
+  if (K > 0) {
+    const T *a = static_cast<const T *>(bases.p[d.a.base]) + d.a.off;
+    const T *b = static_cast<const T *>(bases.p[d.b.base]) + d.b.off + n0;
+    SegCtx<T> c;
+    c.lda = d.a.ld;
+    c.ldb = d.b.ld;
+    c.K = K;
+    c.a_xc = d.a.trans == 0;
+    c.b_xc = true;
+    c.aw = c.a_xc ? a + (m0 + wm) : a + (int64_t)(m0 + wm) * c.lda;
+    c.b = b;
+    c.mrem = M - m0 - wm;
+    c.nrem = nrem;
+    c.sr = c.a_xc ? 1 : c.lda;
+    c.sk = c.a_xc ? c.lda : 1;
+    c.row2 = 2 * arow;
+    c.gk = kg_of<MODE>(g);
+    c.a_lane = (uint32_t)(c.row2 * c.sr + c.gk * c.sk) * (uint32_t)sizeof(T);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_a<T, MODE>(c, 0, q, fa);
+    // B (K x nrem, N contiguous) -> LDS rows k, zeros past K and past nrem
+    const __amdgpu_buffer_rsrc_t rs = rsrc(b);
+    if (MODE != SINGLE) {   // pairs along n: a pair lies inside B or ends in its padding
+      const int n = 2 * tid;
+#pragma unroll
+      for (int k = 0; k < KBK; ++k) {
+        const bool ok = k < K && n < nrem;
+        const typename Ld<T>::v2 v = Ld<T>::two(rs, lane_off(ok, (uint32_t)(k * c.ldb + n) * (uint32_t)sizeof(T)), 0);
+        Bs[k * LDS_S + n] = v.x;
+        Bs[k * LDS_S + n + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KBK; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int n = tid + NT * h;
+          const bool ok = k < K && n < nrem;
+          Bs[k * LDS_S + n] = Ld<T>::one(rs, lane_off(ok, (uint32_t)(k * c.ldb + n) * (uint32_t)sizeof(T)), 0);
+        }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = tid + NT * h;
+    cols[n] = n >= nrem ? 0 : (t.ctab < 0 ? (int64_t)(n0 + n) * t.ldc : coltab[t.ctab + n0 + n]);
+  }
+  __syncthreads();
+
+  const bool vec = (t.flags & TASK_VEC) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+  constexpr int P = 16 / (int)sizeof(T), U = 8 / P;
+  typedef T vp __attribute__((ext_vector_type(P)));
+  const int nch = (nrem + KBN - 1) / KBN;
+  for (int ch = 0; ch < nch; ++ch) {
+    v4 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = v4{0, 0, 0, 0};
+    if (K > 0) {
+#pragma unroll
+      for (int q = 0; q < KBK / 4; ++q) {
+        if (kq_of<MODE>(q) >= K) continue;   // every k of this step is past K
+        const T *br = Bs + (kq_of<MODE>(q) + kg_of<MODE>(g)) * LDS_S + ch * KBN + r;
+        T bq[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bq[j] = br[16 * j];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = Mfma<T>::mma(fa[i][q], bq[j], acc[i][j]);
+      }
+    }
+    // stores: the lane layout of gemm_block's epilogue
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = ch * KBN + 16 * j + r;
+      if (n >= nrem) continue;
+      T *cp = C + cols[n];
+#pragma unroll
+      for (int h = 0; h < MI / 2; ++h) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          vp x;
+#pragma unroll
+          for (int q = 0; q < P; ++q) x[q] = acc[2 * h + (q & 1)][j][u * (P / 2) + (q >> 1)];
+          const int m = m0 + wm + 32 * h + 4 * P * u + P * g;
+          if (vec && m + P - 1 < M) {
+            *reinterpret_cast<vp *>(cp + m) = x;
+          } else {
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+              if (m + q < M) cp[m + q] = x[q];
+          }
+        }
+      }
+    }
+  }
+}
+
 template <typename T>
 __global__ void scale_kernel(T *C, int64_t m, int64_t n, int64_t ldc, T beta) {
   const int64_t total = m * n;
@@ -637,11 +779,25 @@ void launch_grouped_w(int stage, int mode, dim3 grid, hipStream_t s, const DevTa
 }
 
 template <typename T>
+void launch_strip_t(int mode, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
+                    const int64_t *coltab, const Bases &bases) {
+  const dim3 grid(n), block(NT);
+  if (mode == LOAD_PAIR_M)
+    hipLaunchKernelGGL((strip_gemm_kernel<T, LOAD_PAIR_M>), grid, block, 0, s, tasks, tiles, coltab, bases);
+  else if (mode == LOAD_PAIR_K)
+    hipLaunchKernelGGL((strip_gemm_kernel<T, LOAD_PAIR_K>), grid, block, 0, s, tasks, tiles, coltab, bases);
+  else
+    hipLaunchKernelGGL((strip_gemm_kernel<T, LOAD_SINGLE>), grid, block, 0, s, tasks, tiles, coltab, bases);
+}
+
+template <typename T>
 void launch_grouped_t(int stage, int mode, int bn, unsigned n, hipStream_t s, const DevTask *tasks,
                       const DevTile *tiles, const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const T a = (T)alpha, b = (T)beta, c = preload_scale<T>(alpha, beta);
   const dim3 grid(n);
-  if (bn == Blk<4>::KBN)
+  if (bn == STRIP_W)
+    launch_strip_t<T>(mode, n, s, tasks, tiles, coltab, bases);
+  else if (bn == Blk<4>::KBN)
     launch_grouped_w<T, 4>(stage, mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
   else
     launch_grouped_w<T, 8>(stage, mode, grid, s, tasks, tiles, coltab, bases, a, b, c);
@@ -668,7 +824,7 @@ int launch_grouped(tlr_dtype dt, int stage, int mode, int bn, const DevTask *tas
   if (dt == TLR_F16 || dt == TLR_BF16)
     return launch_grouped16(dt, stage, bn, tasks, tiles, n_tiles, coltab, bases, alpha, beta, stream);
   if (n_tiles <= 0) return 0;
-  if (bn != Blk<4>::KBN && bn != Blk<8>::KBN) return (int)hipErrorInvalidValue;
+  if (bn != Blk<4>::KBN && bn != Blk<8>::KBN && !(bn == STRIP_W && stage == 2)) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64)
     launch_grouped_t<double>(stage, mode, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);

@@ -538,8 +538,16 @@ static int launch_bn(int stage, const TaskList &tl) {
   return blocks < 4 * 256 ? BN_NARROW : BN;
 }
 
+// A right/left-product task that the strip kernel runs: at most one K segment
+// of at most STRIP_K, B N-contiguous, output C = acc (32/64-bit types).
+static bool strip_task(const DevTask &d) {
+  if (d.final_ || d.nseg > 1) return false;
+  return d.nseg == 0 || (d.seg[0].K <= STRIP_K && d.seg[0].b.trans == 1);
+}
+
 // Appends one launch of `tl` (nothing when empty) and returns its index, or -1.
-static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
+// A strip launch takes 128 x STRIP_W blocks.
+static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl, bool strip = false) {
   if (tl.t.empty()) return -1;
   Launch L;
   L.stage = stage;
@@ -553,7 +561,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
   L.executed_flops = 0;
   const int32_t task0 = (int32_t)p.tasks.size();
   L.task_off = task0;
-  L.bn = launch_bn(stage, tl);
+  L.bn = strip ? STRIP_W : launch_bn(stage, tl);
   L.bm = BM;
   if (stage == 3 && p.es == 2) L.bm = L.bn = BW16;   // the 16-bit final update: 256 x 256 blocks
   const int bm = L.bm, bn = L.bn;
@@ -604,11 +612,32 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl) {
 // products that read only inputs on the side stream (forked before stage 1, so
 // they run beside stages 1 and 2), the right/left product (stage 2) and the
 // final update (stage 3), which waits for the side launch.
+// On 32/64-bit types the right/left product is split: tasks with K <= STRIP_K
+// go to a strip launch, the rest to the grouped kernel, one after the other.
+// The split is made only when the strip launch would fill the chip twice
+// (STRIP_MIN_BLOCKS workgroups); a handful of strip tasks behind the grouped
+// launch measured slower than leaving them in it.
+constexpr int64_t STRIP_MIN_BLOCKS = 2 * 256;
 static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &side, TaskList &l2,
                         TaskList &l3) {
   const int a = emit_launch(p, 1, group, rect, l1);
   const int d = emit_launch(p, STAGE_SIDE, group, rect, side);
-  emit_launch(p, 2, group, rect, l2);
+  TaskList l2s, l2g;
+  int64_t strip_blocks = 0;
+  for (size_t t = 0; t < l2.t.size(); ++t) {
+    const DevTask &x = l2.t[t];
+    const bool s = p.es != 2 && strip_task(x);
+    if (s) strip_blocks += ceil_div(x.M, BM) * ceil_div(x.N, STRIP_W);
+    TaskList &dst = s ? l2s : l2g;
+    dst.t.push_back(x);
+    dst.useful.push_back(l2.useful[t]);
+  }
+  if (strip_blocks < STRIP_MIN_BLOCKS) {
+    l2g = l2;
+    l2s = TaskList();
+  }
+  emit_launch(p, 2, group, rect, l2g);
+  emit_launch(p, 2, group, rect, l2s, true);
   const int c = emit_launch(p, 3, group, rect, l3);
   if (d < 0) return;
   // fork before the coupling launch, so that the side launch runs beside
@@ -1002,12 +1031,18 @@ static tlr_status validate(const Plan &p, bool deep) {
   // workgroup tables: each block of each task exactly once
   std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), -1);
   for (const Launch &L : p.launches) {
-    const bool shape_ok = L.bm == BM ? (L.bn == BN || L.bn == BN_NARROW)
-                                     : (L.bm == BW16 && L.bn == BW16 && L.stage == 3 && p.es == 2);
+    const bool strip = L.bm == BM && L.bn == STRIP_W;
+    const bool shape_ok = strip ? (L.stage == 2 && p.es != 2)
+                          : L.bm == BM ? (L.bn == BN || L.bn == BN_NARROW)
+                                       : (L.bm == BW16 && L.bn == BW16 && L.stage == 3 && p.es == 2);
     if (!shape_ok || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
       return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block shape or task range");
-    for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t)
+    for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t) {
+      // the strip kernel holds one K stage and fills LDS from an N-contiguous B
+      if (strip && !strip_task(p.tasks[t]))
+        return fail(TLR_ERR_INVALID_ARG, "internal: task in a strip launch that the strip kernel cannot run");
       want[t] = ceil_div(p.tasks[t].M, L.bm) * ceil_div(p.tasks[t].N, L.bn);
+    }
   }
   for (const Launch &L : p.launches) {
     if (L.tile_off < 0 || L.tile_off + L.n_tiles > (int64_t)p.tiles.size() || L.n_tiles % NUM_XCD)

@@ -15,6 +15,8 @@ constexpr int BM = 128;            // workgroup block rows of every grouped laun
 constexpr int BN = 128;            // block columns: wide launches
 constexpr int BN_NARROW = 64;      // block columns: narrow launches (see launch_bn)
 constexpr int BW16 = 256;          // block rows and columns of the 16-bit final update
+constexpr int STRIP_W = 512;        // block columns of a strip launch (right/left product, K <= 16)
+constexpr int STRIP_K = 16;         // largest K of a strip task: one K stage of the kernel
 constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
 constexpr int NUM_XCD = 8;         // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int AUX_PER_GROUP = 3;   // auxiliary streams of a group: two for load modes, one side lane
@@ -56,7 +58,7 @@ struct Launch {
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
   int bm;            // block rows of the launch's workgroups (BM, or BW16 for a 16-bit final update)
-  int bn;            // block columns (BN or BN_NARROW; BW16 with bm = BW16)
+  int bn;            // block columns (BN or BN_NARROW; BW16 with bm = BW16; STRIP_W for a strip launch)
   bool beta_one;     // a later pass of the per-k loop over C: its updates use beta = 1
   int64_t task_off;  // the launch's tasks are tasks[task_off, task_off + n_tasks)
   int64_t tile_off;  // first DevTile of the launch in the tile table

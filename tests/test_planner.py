@@ -44,7 +44,8 @@ def test_worked_example(cand):
     s = [b] * 3
     assert info["flops_right"] == pa.useful_flops(RA, RB, [b, b], s, s, False, False, "right")
     assert info["flops_left"] == pa.useful_flops(RA, RB, [b, b], s, s, False, False, "left")
-    # three grouped launches per rectangle
+    # three grouped launches per rectangle (the right product's three tasks
+    # with rank(B_kj) <= 16 are too few for a strip launch of their own)
     assert info["launches"] == 3
     stages = [T.tlr_plan_launch(p, l)["stage"] for l in range(3)]
     assert stages == [1, 2, 3]
@@ -56,6 +57,36 @@ def _rand_ranks(rng, q, b, diag, lo=0, hi=None):
     if diag:
         np.fill_diagonal(R, 0)
     return R
+
+
+def test_strip_split():
+    """Right/left-product tasks with K <= 16 (here rank(A_ik) <= 16, left order)
+    go to a strip launch of 128 x 512 blocks after the grouped launch of the
+    others, when they make at least 512 blocks; 16-bit plans and small grids
+    keep one launch."""
+    rng = np.random.default_rng(11)
+    q, b = 24, 256
+    RA = _rand_ranks(rng, q, b, True, lo=0, hi=24)
+    RB = _rand_ranks(rng, q, b, True, lo=1, hi=24)
+    A, B = T.Shape(q * b, q * b, b, RA, True), T.Shape(q * b, q * b, b, RB, True)
+    flags = T.TLR_PLAN_FORCE_LEFT | T.TLR_PLAN_VALIDATE
+    p = T.tlr_gemm_analyze("f64", "N", A, "N", B, ldc=q * b, flags=flags)
+    L = [T.tlr_plan_launch(p, l) for l in range(T.tlr_plan_info(p)["launches"])]
+    st2 = [x for x in L if x["stage"] == 2]
+    SN = RB.sum(axis=1)          # coupling columns of contraction tile k
+    tasks = [(i, k) for i in range(q) for k in range(q) if k != i and SN[k] > 0]
+    small = [(i, k) for (i, k) in tasks if RA[i, k] <= 16]
+    assert [x["tasks"] for x in st2] == [len(tasks) - len(small), len(small)]
+    blocks = sum(2 * -(-int(SN[k]) // 512) for (_, k) in small)
+    assert blocks >= 512
+    assert st2[1]["workgroups"] >= blocks and st2[1]["workgroups"] % 8 == 0
+    assert st2[1]["useful_flops"] == sum(2.0 * b * SN[k] * RA[i, k] for (i, k) in small)
+    A8, B8 = (T.Shape(q * b, q * b, b, (R + 7) // 8 * 8, True) for R in (RA, RB))   # 16-bit: ranks of 8
+    p16 = T.tlr_gemm_analyze("f16", "N", A8, "N", B8, ldc=q * b, flags=flags)
+    assert sum(T.tlr_plan_launch(p16, l)["stage"] == 2 for l in range(T.tlr_plan_info(p16)["launches"])) == 1
+    A4, B4 = (T.Shape(4 * b, 4 * b, b, R[:4, :4].copy(), True) for R in (RA, RB))
+    p4 = T.tlr_gemm_analyze("f64", "N", A4, "N", B4, ldc=4 * b, flags=flags)
+    assert sum(T.tlr_plan_launch(p4, l)["stage"] == 2 for l in range(T.tlr_plan_info(p4)["launches"])) == 1
 
 
 CASES = [(0, 5, 4, 0, True), (1, 4, 3, 2, True), (2, 3, 5, 4, False), (3, 6, 2, 1, True), (4, 1, 8, 0, True),

@@ -27,6 +27,8 @@ def test_short_names():
         == "wide_gemm16_kernel<half>"
     assert P._short("_ZN3tlr12_GLOBAL__N_119grouped_gemm_kernelIfLi1ELi0ELi4EEEvPK") \
         == "grouped_gemm_kernel<float, 1, 0, 4>"
+    assert P._short("_ZN3tlr12_GLOBAL__N_117strip_gemm_kernelIdLi1EEEvPKNS_7DevTaskEPKNS_7DevTileEPKlNS_5BasesE") \
+        == "strip_gemm_kernel<double, 1>"
 
 
 def test_trace_stats_groups_by_kernel_and_grid(tmp_path):
