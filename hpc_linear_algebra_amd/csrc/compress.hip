@@ -160,33 +160,50 @@ __device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *
 }
 
 // The same QR for a panel held in LDS (column stride ld), by NTH = 512
-// threads: for reflector k, w = A[k:m, k+1:n]^T v is formed as 8 partial
-// sums per column (thread (column, part) adds rows part, part + 8, ..., four
-// rows per step with the loads first) combined by shuffles among the 8 lanes
-// of the column, then every thread applies its share of the rank-1 update
-// A -= beta v w^T, four columns per step.  Q is formed backwards the same
-// way.  A wave's partial sums read 8 rows of 8 columns; with ld = m + 8 two
-// neighbouring columns sit on complementary halves of the banks (at
-// ld = m = 256 all eight fell on the same banks).
+// threads, in two phases per reflector with one barrier after each:
+//   phase A (reflector k): every thread derives alpha, v_k = x_k - alpha and
+//     beta from the tail norm left by the previous phase, then
+//     w = A[k:m, k+1:n]^T v is formed as 8 partial sums per column (thread
+//     (column, part) adds rows part, part + 8, ..., four rows per step with
+//     the loads first; v_k comes from the register, the panel still holds x_k)
+//     combined by shuffles among the 8 lanes of the column;
+//   phase B: the rank-1 update A -= beta v w^T, four columns per step per
+//     thread, v_k stored into the panel, and the squares of the updated
+//     column k+1 below its diagonal summed per wave: the tail norm of the next
+//     reflector.
+// Q is formed backwards in the same two phases: phase A forms w for the
+// columns already formed and keeps v in vcol, phase B applies the reflector
+// to them and writes column k of Q.  A wave's partial sums read 8 rows of 8
+// columns; with ld = m + 8 two neighbouring columns sit on complementary
+// halves of the banks (at ld = m = 256 all eight fell on the same banks).
 constexpr int QR_STAGED_THREADS = 512;
 constexpr int QR_PARTS = QR_STAGED_THREADS / S_MAX;   // 8 partial sums per column
 constexpr int QR_ROWS = 256;                           // rows of a staged panel (b <= 256); two threads per row
 template <typename T>
-__device__ __forceinline__ void qr_panel_lds(T *a, int m, int ld, T *rr, int n, T *red, T *beta_s, T *wv) {
+__device__ __forceinline__ void qr_panel_lds(T *a, int m, int ld, T *rr, int n, T *red, T *beta_s, T *wv,
+                                             T *vcol) {
   constexpr int NTH = QR_STAGED_THREADS;
-  const int tid = threadIdx.x;
+  constexpr int NW = NTH / 64;
+  constexpr int CS = NTH / QR_ROWS;                       // column step of the update
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pp = tid % QR_PARTS, cc = tid / QR_PARTS;     // (part, column) of the partial sums
+  const int ru = tid % QR_ROWS, h = tid / QR_ROWS;        // (row offset, column half) of the update
   const int kmax = min(m, n);
   if (rr)
     for (int e = tid; e < n * n; e += NTH) rr[e] = 0;
-  // w_c = sum_{r >= r0} a[r, k] a[r, c] for columns c in (k, n), into wv[c]
-  auto apply_vt = [&](int k, int r0) {
+  // w_c = sum_{r >= r0} v_r a[r, c] for the columns c in (k, n), into wv[c];
+  // v_r = a[r, k], except v_k = vk when own_vk (then r0 = k)
+  auto apply_vt = [&](int k, int r0, bool own_vk, T vk) {
     const int c = k + 1 + cc;
     T acc = 0;
     if (c < n) {
-      // four rows per step, loads first, so that eight LDS loads are in flight
       T acc1 = 0;
       int r = r0 + pp;
+      if (own_vk && pp == 0) {
+        acc = vk * a[k + c * ld];
+        r += QR_PARTS;
+      }
+      // four rows per step, loads first, so that eight LDS loads are in flight
       for (; r + 3 * QR_PARTS < m; r += 4 * QR_PARTS) {
         const T v0 = a[r + k * ld], v1 = a[r + QR_PARTS + k * ld], v2 = a[r + 2 * QR_PARTS + k * ld],
                 v3 = a[r + 3 * QR_PARTS + k * ld];
@@ -202,82 +219,91 @@ __device__ __forceinline__ void qr_panel_lds(T *a, int m, int ld, T *rr, int n, 
 #pragma unroll
     for (int d = 1; d < QR_PARTS; d <<= 1) acc += __shfl_xor(acc, d, QR_PARTS);
     if (pp == 0 && c < n) wv[c] = acc;
-    __syncthreads();
   };
+  // A[r, c] = (top ? 0 : A[r, c]) - vb w_c for the columns c > k of this
+  // thread's half: c = k + 1 + h, k + 1 + h + CS, ...
+  auto update_row = [&](int k, int r, T vb, bool top) {
+    int c = k + 1 + h;
+    for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
+      const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
+              x3 = a[r + (c + 3 * CS) * ld];
+      const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
+      a[r + c * ld] = (top ? T(0) : x0) - vb * w0;
+      a[r + (c + CS) * ld] = (top ? T(0) : x1) - vb * w1;
+      a[r + (c + 2 * CS) * ld] = (top ? T(0) : x2) - vb * w2;
+      a[r + (c + 3 * CS) * ld] = (top ? T(0) : x3) - vb * w3;
+    }
+    for (; c < n; c += CS) a[r + c * ld] = (top ? T(0) : a[r + c * ld]) - vb * wv[c];
+  };
+
+  // tail norm of column 0, per wave
+  {
+    T part = 0;
+    if (kmax > 0)
+      for (int r = 1 + tid; r < m; r += NTH) part += a[r] * a[r];
+    part = wave_sum(part);
+    if (lane == 0) red[wave] = part;
+  }
+  __syncthreads();
   for (int k = 0; k < kmax; ++k) {
+    // phase A
     T tail = 0;
-    for (int r = k + 1 + tid; r < m; r += NTH) tail += a[r + k * ld] * a[r + k * ld];
-    tail = block_sum<T, NTH>(tail, red);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tail += red[w];
     const T x0 = a[k + k * ld];
     const T nrm = sqrt(tail + x0 * x0);
     const T alpha = x0 >= T(0) ? -nrm : nrm;
     const T v0 = x0 - alpha;
     const T vtv = tail + v0 * v0;
     const T beta = vtv > T(0) ? T(2) / vtv : T(0);
-    __syncthreads();
     if (tid == 0) {
-      a[k + k * ld] = v0;
       beta_s[k] = beta;
       if (rr) rr[k + k * n] = alpha;
     }
+    if (rr && k > 0)   // row k-1 of R is final since the previous phase B
+      for (int c = k + tid; c < n; c += NTH) rr[(k - 1) + c * n] = a[(k - 1) + c * ld];
+    apply_vt(k, k, true, v0);
     __syncthreads();
-    apply_vt(k, k);
-    // A[r, c] -= beta w_c v_r for r >= k, c > k: thread (row r, half h) takes
-    // the columns c = k + 1 + h, k + 3 + h, ...
+    // phase B
+    T part = 0;
     {
-      const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
+      const int r = k + ru;
       if (r < m) {
-        const T vb = beta * a[r + k * ld];
-        constexpr int CS = QR_STAGED_THREADS / QR_ROWS;   // column step
-        int c = k + 1 + h;
-        for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
-          const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
-                  x3 = a[r + (c + 3 * CS) * ld];
-          const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
-          a[r + c * ld] = x0 - vb * w0;
-          a[r + (c + CS) * ld] = x1 - vb * w1;
-          a[r + (c + 2 * CS) * ld] = x2 - vb * w2;
-          a[r + (c + 3 * CS) * ld] = x3 - vb * w3;
+        update_row(k, r, beta * (r == k ? v0 : a[r + k * ld]), false);
+        if (r == k && h == 0) a[k + k * ld] = v0;
+        if (h == 0 && r > k + 1 && k + 1 < n) {
+          const T y = a[r + (k + 1) * ld];
+          part = y * y;
         }
-        for (; c < n; c += CS) a[r + c * ld] -= vb * wv[c];
       }
     }
+    part = wave_sum(part);
+    if (lane == 0) red[wave] = part;
     __syncthreads();
-    if (rr)
-      for (int c = k + 1 + tid; c < n; c += NTH) rr[k + c * n] = a[k + c * ld];
   }
+  if (rr && kmax > 0)
+    for (int c = kmax + tid; c < n; c += NTH) rr[(kmax - 1) + c * n] = a[(kmax - 1) + c * ld];
   for (int c = kmax; c < n; ++c)
     for (int r = tid; r < m; r += NTH) a[r + c * ld] = 0;
   __syncthreads();
   for (int k = kmax - 1; k >= 0; --k) {
     const T beta = beta_s[k];
-    // rows <= k of the columns c > k are zero here: w_c = sum_{r > k} v_r Q[r, c]
-    apply_vt(k, k + 1);
     const T v0 = a[k + k * ld];
-    {
-      // row k of the columns c > k was zero: it becomes -beta w_c v0
-      const int r = k + (tid % QR_ROWS), h = tid / QR_ROWS;
-      if (r < m) {
-        const T vb = beta * a[r + k * ld];
-        const bool top = r == k;   // row k of these columns held R: it starts from zero
-        constexpr int CS = QR_STAGED_THREADS / QR_ROWS;   // column step
-        int c = k + 1 + h;
-        for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
-          const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
-                  x3 = a[r + (c + 3 * CS) * ld];
-          const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
-          a[r + c * ld] = (top ? T(0) : x0) - vb * w0;
-          a[r + (c + CS) * ld] = (top ? T(0) : x1) - vb * w1;
-          a[r + (c + 2 * CS) * ld] = (top ? T(0) : x2) - vb * w2;
-          a[r + (c + 3 * CS) * ld] = (top ? T(0) : x3) - vb * w3;
-        }
-        for (; c < n; c += CS) a[r + c * ld] = (top ? T(0) : a[r + c * ld]) - vb * wv[c];
-      }
-    }
+    // phase A: rows <= k of the columns c > k are zero in Q here (the panel
+    // still holds R there): w_c = sum_{r > k} v_r Q[r, c]; v kept in vcol
+    apply_vt(k, k + 1, false, T(0));
+    for (int r = k + tid; r < m; r += NTH) vcol[r] = a[r + k * ld];
     __syncthreads();
-    for (int r = tid; r < m; r += NTH) {
-      const T vr = a[r + k * ld];
-      a[r + k * ld] = r < k ? T(0) : (r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr);
+    // phase B: the reflector on the columns c > k (row k held R: it starts
+    // from zero), and column k of Q: H_k e_k
+    {
+      const int r = k + ru;
+      if (r < m) {
+        const T vr = vcol[r];
+        update_row(k, r, beta * vr, r == k);
+        if (h == 1) a[r + k * ld] = r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr;
+      }
+      for (int r2 = tid; r2 < k; r2 += NTH) a[r2 + k * ld] = 0;
     }
     __syncthreads();
   }
@@ -307,11 +333,12 @@ __global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kern
   if constexpr (STAGED) {
     __shared__ T panel[QrPanel<T>::ELEMS];
     __shared__ T wv[S_MAX];
+    __shared__ T vcol[QR_ROWS];
     const int ld = m + QR_PAD;
     for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
       for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) panel[r + c * ld] = a[r + (int64_t)c * lda];
     __syncthreads();
-    qr_panel_lds<T>(panel, m, ld, rr, n, red, beta_s, wv);
+    qr_panel_lds<T>(panel, m, ld, rr, n, red, beta_s, wv, vcol);
     for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
       for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) a[r + (int64_t)c * lda] = panel[r + c * ld];
   } else {
