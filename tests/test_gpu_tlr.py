@@ -4,7 +4,8 @@ tails: every op combination, beta in {0 (NaN-filled C), 0.5, 1}, both forced
 association orders and the planner's own choice, rank-0 tiles, operands
 without dense diagonals, boundary tiles (N not a multiple of b) with the
 boundary regions on their own streams, workspace budgets that split C into
-several rectangles, leading dimensions above the row count, fp64 and fp32.
+several rectangles, leading dimensions above the row count, fp64 and fp32,
+and a grid large enough for the strip launch of the right/left product.
 Bar: relative Frobenius error <= 1e-12 (fp64), <= 1e-5 (fp32)."""
 import itertools
 
@@ -222,3 +223,18 @@ def test_tiny_alpha_large_c_does_not_overflow(dtype, alpha):
     C = 1e10 * np.random.default_rng(52).standard_normal((200, 200))
     check_tlr(A, B, "N", "N", alpha, 1.0, C)
     check_tlr(A, B, "T", "N", alpha, -0.5, C, flags=F_LEFT)
+
+
+@pytest.mark.parametrize("dtype,opA,opB,flags", [("f64", "T", "N", F_LEFT), ("f64", "N", "T", F_RIGHT),
+                                                 ("f32", "N", "N", F_LEFT), ("f32", "T", "T", F_RIGHT)])
+def test_strip_launches(dtype, opA, opB, flags):
+    """A 28 x 28 grid of b = 128 with ranks 0-20: the right or left product's
+    tasks of rank <= 16 make enough 128 x 512 blocks for a strip launch, the
+    others stay in the grouped launch; both against the oracle."""
+    n, b = 28 * 128, 128
+    A, B, C = _pair(4200 + flags, n, b, dtype=dtype, lo=0, hi=20)
+    say(f"strip launches {dtype} {opA}{opB} flags={flags}")
+    check_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags)
+    got, g = run_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags, return_plan=True)
+    stage2 = [x for x in g.launches() if x["stage"] == 2]
+    assert len(stage2) == 2 and min(x["tasks"] for x in stage2) > 0, stage2
