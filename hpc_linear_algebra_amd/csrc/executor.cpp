@@ -105,7 +105,7 @@ tlr_status plan_bind(Plan *p, void *dev, size_t bytes, void *stream) {
   for (size_t g = 0; g < p->groups.size(); ++g) {
     hipEvent_t je = nullptr;
     bool any = false;
-    for (int l : p->groups[g].launches) any = any || p->launches[l].stage == STAGE_SIDE;
+    for (int l : p->groups[g].launches) any = any || p->launches[l].stage == STAGE_SIDE || p->launches[l].on_side;
     if (any) HIP_TRY(hipEventCreateWithFlags(&je, hipEventDisableTiming));
     p->side_join.push_back(je);
   }
@@ -235,7 +235,7 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
   // the stream a launch runs on (its first load-mode part, for a split launch)
   auto launch_stream = [&](int l) -> hipStream_t {
     const Launch &L = p->launches[l];
-    return L.stage == STAGE_SIDE ? aux(L.group, AUX_PER_GROUP - 1) : stream_of(L.group);
+    return L.stage == STAGE_SIDE || L.on_side ? aux(L.group, AUX_PER_GROUP - 1) : stream_of(L.group);
   };
   const bool prof = p->prof_count < p->prof_max;
   const size_t nl = p->launches.size();
@@ -283,17 +283,17 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
         if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sl));
         continue;
       }
-      if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sg));
+      if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sl));
       if (pairs_ok) {
         // one kernel per load mode; several non-empty ones run side by side
         // (the first on the group's stream, the others on its auxiliary
         // streams) so that a small sub-table does not run alone on the GPU
         int part = 0;
         hipEvent_t fork = static_cast<hipEvent_t>(p->mode_events[3 * l]);
-        if (fork) HIP_TRY(hipEventRecord(fork, sg));   // before the first sub-launch: all start together
+        if (fork) HIP_TRY(hipEventRecord(fork, sl));   // before the first sub-launch: all start together
         for (int m = 0; m < NUM_LOAD_MODES; ++m) {
           if (L.mode_tiles[m] == 0) continue;
-          hipStream_t sm = sg;
+          hipStream_t sm = sl;
           if (part > 0) {
             sm = aux(L.group, part - 1);
             HIP_TRY(hipStreamWaitEvent(sm, fork, 0));
@@ -304,17 +304,17 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
           if (part > 0) {
             hipEvent_t join = static_cast<hipEvent_t>(p->mode_events[3 * l + part]);
             HIP_TRY(hipEventRecord(join, sm));
-            HIP_TRY(hipStreamWaitEvent(sg, join, 0));
+            HIP_TRY(hipStreamWaitEvent(sl, join, 0));
           }
           ++part;
         }
       } else {
         int e = launch_grouped(p->dt, L.stage, LOAD_SINGLE, L.bn, tasks, tiles + L.tile_off, L.n_tiles, ctab, bases,
-                               alpha, L.beta_one ? 1.0 : beta, sg);
+                               alpha, L.beta_one ? 1.0 : beta, sl);
         if (e) return fail(TLR_ERR_HIP, std::string("grouped GEMM launch: ") + hipGetErrorString((hipError_t)e));
       }
-      if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sg));
-      if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sg));
+      if (prof) HIP_TRY(hipEventRecord(pev(l, 1), sl));
+      if (p->dep_events[l]) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(p->dep_events[l]), sl));
     }
     if (p->side_join[g]) {   // every side launch of the group ends before the group does
       hipEvent_t je = static_cast<hipEvent_t>(p->side_join[g]);

@@ -555,6 +555,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl, bo
   L.rect = rect;
   L.wait_launch = -1;
   L.fork_at = -1;
+  L.on_side = false;
   L.beta_one = false;
   L.n_tasks = (int64_t)tl.t.size();
   L.useful_flops = 0;
@@ -636,9 +637,20 @@ static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &si
     l2g = l2;
     l2s = TaskList();
   }
-  emit_launch(p, 2, group, rect, l2g);
+  // Beside a strip launch the grouped one goes to the side stream, after the
+  // side launch, waiting for the coupling: its MFMA-heavy blocks then run
+  // beside the strip launch's stores instead of before them.  (Waiting for
+  // the coupling also orders it after everything the group's stream held
+  // before, the previous rectangle's final update included.)
+  const bool split = !l2s.t.empty() && !l2g.t.empty() && a >= 0;
+  const int g2 = emit_launch(p, 2, group, rect, l2g);
+  if (split) {
+    p.launches[g2].on_side = true;
+    p.launches[g2].wait_launch = a;
+  }
   emit_launch(p, 2, group, rect, l2s, true);
   const int c = emit_launch(p, 3, group, rect, l3);
+  if (split && c >= 0) p.launches[c].wait_launch = g2;   // the side stream holds the side launch before it
   if (d < 0) return;
   // fork before the coupling launch, so that the side launch runs beside
   // stages 1 and 2.  Without a coupling launch the fork is the side launch's
@@ -647,7 +659,7 @@ static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &si
   // waits on it.  A later launch (stage 2 or 3) would record the event only
   // after the side stream's wait has been enqueued, which orders nothing.
   p.launches[d].fork_at = a;
-  if (c >= 0) p.launches[c].wait_launch = d;
+  if (c >= 0 && !split) p.launches[c].wait_launch = d;
 }
 
 static void emit_rect(Plan &p, const Sums &s, int rect) {

@@ -57,6 +57,7 @@ struct Launch {
   int rect;
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
+  bool on_side;      // a stage-1-3 launch that runs on the group's side stream (after the side launch)
   int bm;            // block rows of the launch's workgroups (BM, or BW16 for a 16-bit final update)
   int bn;            // block columns (BN or BN_NARROW; BW16 with bm = BW16; STRIP_W for a strip launch)
   bool beta_one;     // a later pass of the per-k loop over C: its updates use beta = 1
