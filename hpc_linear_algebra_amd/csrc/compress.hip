@@ -349,6 +349,11 @@ __global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kern
 // Threads per column pair: 8 consecutive lanes of one wave take rows part,
 // part + 8, ... of a pair and combine their partial sums with lane shuffles.
 constexpr int JPARTS = 8;
+// LDS column stride of M and J: 72 doubles put the 64-byte row runs of
+// consecutive columns on four different quarters of the banks (at 64 every
+// column started on the same banks, and the eight columns a wave reads at
+// once conflicted eight ways)
+constexpr int JLD = S_MAX + 8;
 
 // One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
 // then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
@@ -361,8 +366,8 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
                                                         int32_t *ranks, int32_t *flags, const T *norms2, int qr,
                                                         int qc, int n, int max_rank, T tol, T conv,
                                                         int skip_diag) {
-  __shared__ T Ms[S_MAX * S_MAX];
-  __shared__ T Js[S_MAX * S_MAX];
+  __shared__ T Ms[JLD * S_MAX];
+  __shared__ T Js[JLD * S_MAX];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
   __shared__ T offw[1 + 32];          // [1 + p]: largest |cos| pair thread p met in the sweep
@@ -379,8 +384,8 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   const T *rt = R + (int64_t)t * n * n;
   for (int e = tid; e < S_MAX * S_MAX; e += CT) {
     const int r = e % S_MAX, c = e / S_MAX;
-    Ms[e] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
-    Js[e] = r == c ? T(1) : T(0);
+    Ms[r + c * JLD] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
+    Js[r + c * JLD] = r == c ? T(1) : T(0);
   }
   if (tid < 33) offw[tid] = 0;
   __syncthreads();
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
         if (p > q) { const int x = p; p = q; q = x; }
         T al = 0, be = 0, ga = 0;
         for (int r = jpart; r < np; r += JPARTS) {
-          const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
+          const T mp = Ms[r + p * JLD], mq = Ms[r + q * JLD];
           al += mp * mp;
           be += mq * mq;
           ga += mp * mq;
@@ -425,12 +430,12 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
           const T cs = T(1) / sqrt(T(1) + tt * tt);
           const T sn = cs * tt;
           for (int r = jpart; r < np; r += JPARTS) {
-            const T mp = Ms[r + p * S_MAX], mq = Ms[r + q * S_MAX];
-            Ms[r + p * S_MAX] = cs * mp - sn * mq;
-            Ms[r + q * S_MAX] = sn * mp + cs * mq;
-            const T jpv = Js[r + p * S_MAX], jqv = Js[r + q * S_MAX];
-            Js[r + p * S_MAX] = cs * jpv - sn * jqv;
-            Js[r + q * S_MAX] = sn * jpv + cs * jqv;
+            const T mp = Ms[r + p * JLD], mq = Ms[r + q * JLD];
+            Ms[r + p * JLD] = cs * mp - sn * mq;
+            Ms[r + q * JLD] = sn * mp + cs * mq;
+            const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
+            Js[r + p * JLD] = cs * jpv - sn * jqv;
+            Js[r + q * JLD] = sn * jpv + cs * jqv;
           }
         }
       }
@@ -447,7 +452,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   // column norms, the order of decreasing sigma (ties by column index)
   for (int c = wave; c < n; c += CT / 64) {
     T s = 0;
-    for (int r = lane; r < np; r += 64) s += Ms[r + c * S_MAX] * Ms[r + c * S_MAX];
+    for (int r = lane; r < np; r += 64) s += Ms[r + c * JLD] * Ms[r + c * JLD];
     s = wave_sum(s);
     if (lane == 0) sig2[c] = s;
   }
@@ -462,8 +467,8 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   T *jt = Jout + (int64_t)t * n * n;
   for (int e = tid; e < n * n; e += CT) {
     const int r = e % n, c = e / n;
-    wt[e] = Ms[r + c * S_MAX];
-    jt[e] = Js[r + c * S_MAX];
+    wt[e] = Ms[r + c * JLD];
+    jt[e] = Js[r + c * JLD];
   }
   for (int c = tid; c < n; c += CT) perm[(int64_t)t * n + c] = order[c];
   if (tid == 0) {
