@@ -286,8 +286,9 @@ tlr_status plan_execute(Plan *p, double alpha, const tlr_buffers *A, const tlr_b
       if (prof) HIP_TRY(hipEventRecord(pev(l, 0), sl));
       if (pairs_ok) {
         // one kernel per load mode; several non-empty ones run side by side
-        // (the first on the group's stream, the others on its auxiliary
-        // streams) so that a small sub-table does not run alone on the GPU
+        // (the first on the launch's stream, the others on the group's
+        // auxiliary streams) so that a small sub-table does not run alone on
+        // the GPU
         int part = 0;
         hipEvent_t fork = static_cast<hipEvent_t>(p->mode_events[3 * l]);
         if (fork) HIP_TRY(hipEventRecord(fork, sl));   // before the first sub-launch: all start together

@@ -614,10 +614,10 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl, bo
 // they run beside stages 1 and 2), the right/left product (stage 2) and the
 // final update (stage 3), which waits for the side launch.
 // On 32/64-bit types the right/left product is split: tasks with K <= STRIP_K
-// go to a strip launch, the rest to the grouped kernel, one after the other.
-// The split is made only when the strip launch would fill the chip twice
-// (STRIP_MIN_BLOCKS workgroups); a handful of strip tasks behind the grouped
-// launch measured slower than leaving them in it.
+// go to a strip launch on the group's stream, the rest to a grouped launch on
+// the side stream (below).  The split is made only when the strip launch
+// would fill the chip twice (STRIP_MIN_BLOCKS workgroups); a handful of strip
+// tasks beside the grouped launch measured slower than leaving them in it.
 constexpr int64_t STRIP_MIN_BLOCKS = 2 * 256;
 static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &side, TaskList &l2,
                         TaskList &l3) {

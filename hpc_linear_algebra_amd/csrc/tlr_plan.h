@@ -48,7 +48,8 @@ struct Rect {
 // (X = D W or X' = V^T D, and the D W / D^T V blocks of the terminal
 // matrices).  It runs on the group's side stream, forked from the group's
 // stream just before `fork_at` is enqueued, beside stages 1 and 2; the final
-// update waits for it.
+// update waits for it (or for the grouped stage-2 launch that follows it on
+// the side stream, see Launch::on_side).
 constexpr int STAGE_SIDE = 4;
 
 struct Launch {
