@@ -238,3 +238,36 @@ def test_strip_launches(dtype, opA, opB, flags):
     got, g = run_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags, return_plan=True)
     stage2 = [x for x in g.launches() if x["stage"] == 2]
     assert len(stage2) == 2 and min(x["tasks"] for x in stage2) > 0, stage2
+
+
+@pytest.mark.parametrize("flags", [F_LEFT, F_RIGHT])
+def test_strip_split_back_to_back_executes(flags):
+    """Strip launches with the grouped right/left-product launch on the side
+    stream, a budget that splits C into two rectangles sharing one workspace
+    arena, and two executes of one plan enqueued back to back with different
+    values of B.  Each rectangle's grouped launch must wait for its coupling
+    (and so for the previous rectangle's and execute's final update), and the
+    final update for it.  Both results against the oracle."""
+    import torch
+    from hpc_linear_algebra_amd import tlrgemm as T
+    from hpc_linear_algebra_amd.device import DeviceTLR, TLRGemm, dense_from_device, dense_to_device
+    n, b = 40 * 128, 128
+    A, B1, C = _pair(4300 + flags, n, b, lo=0, hi=20)
+    B2 = padded_tlr(B1, 0)               # same ranks, new values
+    rng = np.random.default_rng(4400 + flags)
+    B2.U = {k: rng.standard_normal(v.shape) / np.sqrt(b) for k, v in B1.U.items()}
+    B2.V = {k: rng.standard_normal(v.shape) / np.sqrt(b) for k, v in B1.V.items()}
+    dA, dB1, dB2 = DeviceTLR(A), DeviceTLR(B1), DeviceTLR(B2)
+    w = T.tlr_gemm_workspace_bytes("f64", "N", dA.shape, "N", dB1.shape, flags=flags, runs=2)
+    g = TLRGemm("f64", "N", dA, "N", dB1, ldc=n, budget=w, flags=flags)
+    assert g.info["runs"] == 2
+    assert sum(L["stage"] == 2 for L in g.launches()) == 4   # strip and grouped launch per rectangle
+    Cs = [dense_to_device(C) for _ in range(2)]
+    say(f"strip split back to back flags={flags}")
+    for db, Cd in zip((dB1, dB2), Cs):
+        g(1.0, dA, db, 0.5, Cd)
+    torch.cuda.synchronize()
+    for bb, Cd in zip((B1, B2), Cs):
+        got = dense_from_device(Cd, n, n)
+        ref = reference.gemm_reference(1.0, "N", A, "N", bb, 0.5, C)
+        assert reference.rel_fro(got, ref) <= 1e-12
