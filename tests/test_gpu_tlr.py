@@ -225,15 +225,18 @@ def test_tiny_alpha_large_c_does_not_overflow(dtype, alpha):
     check_tlr(A, B, "T", "N", alpha, -0.5, C, flags=F_LEFT)
 
 
-@pytest.mark.parametrize("dtype,opA,opB,flags", [("f64", "T", "N", F_LEFT), ("f64", "N", "T", F_RIGHT),
-                                                 ("f32", "N", "N", F_LEFT), ("f32", "T", "T", F_RIGHT)])
-def test_strip_launches(dtype, opA, opB, flags):
-    """A 28 x 28 grid of b = 128 with ranks 0-20: the right or left product's
-    tasks of rank <= 16 make enough 128 x 512 blocks for a strip launch, the
-    others stay in the grouped launch; both against the oracle."""
-    n, b = 28 * 128, 128
+@pytest.mark.parametrize("dtype,opA,opB,flags,b", [("f64", "T", "N", F_LEFT, 128), ("f64", "N", "T", F_RIGHT, 128),
+                                                   ("f32", "N", "N", F_LEFT, 128), ("f32", "T", "T", F_RIGHT, 128),
+                                                   ("f64", "T", "N", F_LEFT, 129), ("f32", "N", "N", F_RIGHT, 129)])
+def test_strip_launches(dtype, opA, opB, flags, b):
+    """A 28 x 28 grid with ranks 0-20: the right or left product's tasks of
+    rank <= 16 make enough 128 x 512 blocks for a strip launch, the others
+    stay in the grouped launch; both against the oracle.  An odd tile size
+    (b = 129: odd leading dimensions) puts the tasks in single-element load
+    mode and gives every tile a one-row block."""
+    n = 28 * b
     A, B, C = _pair(4200 + flags, n, b, dtype=dtype, lo=0, hi=20)
-    say(f"strip launches {dtype} {opA}{opB} flags={flags}")
+    say(f"strip launches {dtype} {opA}{opB} flags={flags} b={b}")
     check_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags)
     got, g = run_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags, return_plan=True)
     stage2 = [x for x in g.launches() if x["stage"] == 2]
