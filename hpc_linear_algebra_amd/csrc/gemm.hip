@@ -545,10 +545,10 @@ void single_gemm_kernel(DevTask t, Bases bases, T alpha, T beta, T cscale, int m
 }
 
 // One task per tile of a regular grid (TileGemm): workgroup x = (tile, row
-// block); the tile's task (N <= 128, one block column) is built from the
-// tile's extents.  C = A B, no alpha / beta.
-template <typename T, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+// block); the tile's task (N <= 128, one block column of 16 NJ columns) is
+// built from the tile's extents.  C = A B, no alpha / beta.
+template <typename T, int MODE, int NJ>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Blk<NJ>::WAVES_PER_EU)))
 void tile_gemm_kernel(TileGemm g, Bases bases, int mb_per_tile) {
   const int t = blockIdx.x / mb_per_tile, mb = blockIdx.x - t * mb_per_tile;
   if (t >= g.qr * g.qc) return;
@@ -583,7 +583,7 @@ void tile_gemm_kernel(TileGemm g, Bases bases, int mb_per_tile) {
   task.seg[0].b = opnd(g.bop);
   task.seg[0].K = K;
   task.seg[0].pad = 0;
-  gemm_block<T, MODE, 8>(task, mb * KBM, 0, nullptr, bases, T(1), T(0), T(0));
+  gemm_block<T, MODE, NJ>(task, mb * KBM, 0, nullptr, bases, T(1), T(0), T(0));
 }
 
 // Strip blocks for the right/left product (stage 2).  Its tasks have one K
@@ -855,17 +855,26 @@ int launch_tile_gemm(tlr_dtype dt, int mode, const TileGemm &g, const Bases &bas
   if (mb <= 0) return 0;
   const dim3 grid((unsigned)((int64_t)g.qr * g.qc * mb)), block(NT);
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define TLR_TILE_LAUNCH(TT)                                                                                    \
+  // tiles of at most 64 columns (the sketch width of a TLR output) take
+  // 128 x 64 blocks: half the MFMA work of a 128 x 128 block and one more
+  // workgroup per CU
+#define TLR_TILE_LAUNCH(TT, NJ)                                                                                \
   do {                                                                                                         \
     if (mode == LOAD_PAIR_M)                                                                                   \
-      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_M>), grid, block, 0, s, g, bases, mb);                \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_M, NJ>), grid, block, 0, s, g, bases, mb);            \
     else if (mode == LOAD_PAIR_K)                                                                              \
-      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_K>), grid, block, 0, s, g, bases, mb);                \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_PAIR_K, NJ>), grid, block, 0, s, g, bases, mb);            \
     else                                                                                                       \
-      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_SINGLE>), grid, block, 0, s, g, bases, mb);                \
+      hipLaunchKernelGGL((tile_gemm_kernel<TT, LOAD_SINGLE, NJ>), grid, block, 0, s, g, bases, mb);            \
   } while (0)
-  if (dt == TLR_F64) TLR_TILE_LAUNCH(double);
-  else TLR_TILE_LAUNCH(float);
+  const bool narrow = g.n <= Blk<4>::KBN;
+  if (dt == TLR_F64) {
+    if (narrow) TLR_TILE_LAUNCH(double, 4);
+    else TLR_TILE_LAUNCH(double, 8);
+  } else {
+    if (narrow) TLR_TILE_LAUNCH(float, 4);
+    else TLR_TILE_LAUNCH(float, 8);
+  }
 #undef TLR_TILE_LAUNCH
   return (int)hipGetLastError();
 }
