@@ -31,6 +31,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "tlr_plan.h"
@@ -159,170 +160,17 @@ __device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *
   }
 }
 
-// The same QR for a panel held in LDS (column stride ld), by NTH = 512
-// threads, in two phases per reflector with one barrier after each:
-//   phase A (reflector k): every thread derives alpha, v_k = x_k - alpha and
-//     beta from the tail norm left by the previous phase, then
-//     w = A[k:m, k+1:n]^T v is formed as 8 partial sums per column (thread
-//     (column, part) adds rows part, part + 8, ..., four rows per step with
-//     the loads first; v_k comes from the register, the panel still holds x_k)
-//     combined by shuffles among the 8 lanes of the column;
-//   phase B: the rank-1 update A -= beta v w^T, four columns per step per
-//     thread, v_k stored into the panel, and the squares of the updated
-//     column k+1 below its diagonal summed per wave: the tail norm of the next
-//     reflector.
-// Q is formed backwards in the same two phases: phase A forms w for the
-// columns already formed and keeps v in vcol, phase B applies the reflector
-// to them and writes column k of Q.  A wave's partial sums read 8 rows of 8
-// columns; with ld = m + 8 two neighbouring columns sit on complementary
-// halves of the banks (at ld = m = 256 all eight fell on the same banks).
-constexpr int QR_STAGED_THREADS = 512;
-constexpr int QR_PARTS = QR_STAGED_THREADS / S_MAX;   // 8 partial sums per column
-constexpr int QR_ROWS = 256;                           // rows of a staged panel (b <= 256); two threads per row
-template <typename T>
-__device__ __forceinline__ void qr_panel_lds(T *a, int m, int ld, T *rr, int n, T *red, T *beta_s, T *wv,
-                                             T *vcol) {
-  constexpr int NTH = QR_STAGED_THREADS;
-  constexpr int NW = NTH / 64;
-  constexpr int CS = NTH / QR_ROWS;                       // column step of the update
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int pp = tid % QR_PARTS, cc = tid / QR_PARTS;     // (part, column) of the partial sums
-  const int ru = tid % QR_ROWS, h = tid / QR_ROWS;        // (row offset, column half) of the update
-  const int kmax = min(m, n);
-  if (rr)
-    for (int e = tid; e < n * n; e += NTH) rr[e] = 0;
-  // w_c = sum_{r >= r0} v_r a[r, c] for the columns c in (k, n), into wv[c];
-  // v_r = a[r, k], except v_k = vk when own_vk (then r0 = k)
-  auto apply_vt = [&](int k, int r0, bool own_vk, T vk) {
-    const int c = k + 1 + cc;
-    T acc = 0;
-    if (c < n) {
-      T acc1 = 0;
-      int r = r0 + pp;
-      if (own_vk && pp == 0) {
-        acc = vk * a[k + c * ld];
-        r += QR_PARTS;
-      }
-      // four rows per step, loads first, so that eight LDS loads are in flight
-      for (; r + 3 * QR_PARTS < m; r += 4 * QR_PARTS) {
-        const T v0 = a[r + k * ld], v1 = a[r + QR_PARTS + k * ld], v2 = a[r + 2 * QR_PARTS + k * ld],
-                v3 = a[r + 3 * QR_PARTS + k * ld];
-        const T y0 = a[r + c * ld], y1 = a[r + QR_PARTS + c * ld], y2 = a[r + 2 * QR_PARTS + c * ld],
-                y3 = a[r + 3 * QR_PARTS + c * ld];
-        acc += v0 * y0 + v2 * y2;
-        acc1 += v1 * y1 + v3 * y3;
-      }
-      for (; r < m; r += QR_PARTS) acc += a[r + k * ld] * a[r + c * ld];
-      acc += acc1;
-    }
-    // the QR_PARTS partial sums of column c sit in consecutive lanes
-#pragma unroll
-    for (int d = 1; d < QR_PARTS; d <<= 1) acc += __shfl_xor(acc, d, QR_PARTS);
-    if (pp == 0 && c < n) wv[c] = acc;
-  };
-  // A[r, c] = (top ? 0 : A[r, c]) - vb w_c for the columns c > k of this
-  // thread's half: c = k + 1 + h, k + 1 + h + CS, ...
-  auto update_row = [&](int k, int r, T vb, bool top) {
-    int c = k + 1 + h;
-    for (; c + 3 * CS < n; c += 4 * CS) {   // four columns per step, loads first
-      const T x0 = a[r + c * ld], x1 = a[r + (c + CS) * ld], x2 = a[r + (c + 2 * CS) * ld],
-              x3 = a[r + (c + 3 * CS) * ld];
-      const T w0 = wv[c], w1 = wv[c + CS], w2 = wv[c + 2 * CS], w3 = wv[c + 3 * CS];
-      a[r + c * ld] = (top ? T(0) : x0) - vb * w0;
-      a[r + (c + CS) * ld] = (top ? T(0) : x1) - vb * w1;
-      a[r + (c + 2 * CS) * ld] = (top ? T(0) : x2) - vb * w2;
-      a[r + (c + 3 * CS) * ld] = (top ? T(0) : x3) - vb * w3;
-    }
-    for (; c < n; c += CS) a[r + c * ld] = (top ? T(0) : a[r + c * ld]) - vb * wv[c];
-  };
-
-  // tail norm of column 0, per wave
-  {
-    T part = 0;
-    if (kmax > 0)
-      for (int r = 1 + tid; r < m; r += NTH) part += a[r] * a[r];
-    part = wave_sum(part);
-    if (lane == 0) red[wave] = part;
-  }
-  __syncthreads();
-  for (int k = 0; k < kmax; ++k) {
-    // phase A
-    T tail = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) tail += red[w];
-    const T x0 = a[k + k * ld];
-    const T nrm = sqrt(tail + x0 * x0);
-    const T alpha = x0 >= T(0) ? -nrm : nrm;
-    const T v0 = x0 - alpha;
-    const T vtv = tail + v0 * v0;
-    const T beta = vtv > T(0) ? T(2) / vtv : T(0);
-    if (tid == 0) {
-      beta_s[k] = beta;
-      if (rr) rr[k + k * n] = alpha;
-    }
-    if (rr && k > 0)   // row k-1 of R is final since the previous phase B
-      for (int c = k + tid; c < n; c += NTH) rr[(k - 1) + c * n] = a[(k - 1) + c * ld];
-    apply_vt(k, k, true, v0);
-    __syncthreads();
-    // phase B
-    T part = 0;
-    {
-      const int r = k + ru;
-      if (r < m) {
-        update_row(k, r, beta * (r == k ? v0 : a[r + k * ld]), false);
-        if (r == k && h == 0) a[k + k * ld] = v0;
-        if (h == 0 && r > k + 1 && k + 1 < n) {
-          const T y = a[r + (k + 1) * ld];
-          part = y * y;
-        }
-      }
-    }
-    part = wave_sum(part);
-    if (lane == 0) red[wave] = part;
-    __syncthreads();
-  }
-  if (rr && kmax > 0)
-    for (int c = kmax + tid; c < n; c += NTH) rr[(kmax - 1) + c * n] = a[(kmax - 1) + c * ld];
-  for (int c = kmax; c < n; ++c)
-    for (int r = tid; r < m; r += NTH) a[r + c * ld] = 0;
-  __syncthreads();
-  for (int k = kmax - 1; k >= 0; --k) {
-    const T beta = beta_s[k];
-    const T v0 = a[k + k * ld];
-    // phase A: rows <= k of the columns c > k are zero in Q here (the panel
-    // still holds R there): w_c = sum_{r > k} v_r Q[r, c]; v kept in vcol
-    apply_vt(k, k + 1, false, T(0));
-    for (int r = k + tid; r < m; r += NTH) vcol[r] = a[r + k * ld];
-    __syncthreads();
-    // phase B: the reflector on the columns c > k (row k held R: it starts
-    // from zero), and column k of Q: H_k e_k
-    {
-      const int r = k + ru;
-      if (r < m) {
-        const T vr = vcol[r];
-        update_row(k, r, beta * vr, r == k);
-        if (h == 1) a[r + k * ld] = r == k ? T(1) - beta * v0 * v0 : -beta * v0 * vr;
-      }
-      for (int r2 = tid; r2 < k; r2 += NTH) a[r2 + k * ld] = 0;
-    }
-    __syncthreads();
-  }
-}
+constexpr int QR_ROWS = 256;   // rows of a register-resident panel (b <= 256)
 
 // QR of every tile's m x n panel (tile t at A + t * stride, leading dim lda),
-// m = s_i (m_sel 0) or s_j (m_sel 1); R (optional) at R + t * n * n.  STAGED:
-// the panel is copied into LDS ((m + QR_PAD) * n <= ELEMS), factorised there and
-// copied back, by 512 threads; otherwise it is factorised in place in global
-// memory by 256 threads.
-constexpr int QR_PAD = 8;   // LDS column stride of a staged panel: m + QR_PAD
-template <typename T> struct QrPanel { static constexpr int ELEMS = 135168 / sizeof(T); };   // (256 + 8) x 64 doubles
-
-template <typename T, bool STAGED>
-__global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kernel(
-    T *A, int lda, int64_t stride, T *R, int qr, int qc, int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
-    int skip_diag) {
-  constexpr int NTH = STAGED ? QR_STAGED_THREADS : CT;
-  __shared__ T red[NTH / 64];
+// m = s_i (m_sel 0) or s_j (m_sel 1); R (optional) at R + t * n * n,
+// factorised in place in global memory by CT threads (tiles of more than
+// QR_ROWS rows; smaller ones take qr_reg_kernel below).
+template <typename T>
+__global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
+                                                       int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
+                                                       int skip_diag) {
+  __shared__ T red[CT / 64];
   __shared__ T beta_s[S_MAX];
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
@@ -330,19 +178,183 @@ __global__ __launch_bounds__(STAGED ? QR_STAGED_THREADS : CT) void qr_tiles_kern
   const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
   T *a = A + (int64_t)t * stride;
   T *rr = R ? R + (int64_t)t * n * n : nullptr;
-  if constexpr (STAGED) {
-    __shared__ T panel[QrPanel<T>::ELEMS];
-    __shared__ T wv[S_MAX];
-    __shared__ T vcol[QR_ROWS];
-    const int ld = m + QR_PAD;
-    for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
-      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) panel[r + c * ld] = a[r + (int64_t)c * lda];
-    __syncthreads();
-    qr_panel_lds<T>(panel, m, ld, rr, n, red, beta_s, wv, vcol);
-    for (int c = threadIdx.x / QR_ROWS; c < n; c += NTH / QR_ROWS)
-      for (int r = threadIdx.x % QR_ROWS; r < m; r += QR_ROWS) a[r + (int64_t)c * lda] = panel[r + c * ld];
-  } else {
-    qr_panel<T, NTH>(a, lda, rr, m, n, red, beta_s);
+  qr_panel<T, CT>(a, lda, rr, m, n, red, beta_s);
+}
+
+// The same QR for panels of at most QR_ROWS rows, held in registers.  Thread
+// (c, p) of QRR_THREADS (8 consecutive lanes per column) holds column c of the
+// panel at rows p, p + 8, ..., p + 248 (QRR_REGS registers, zero past m) for
+// the whole factorisation and for the forming of Q.  Reflector k:
+//   * the 8 threads of column k form the tail norm (lane shuffles), alpha,
+//     beta and v, write v (zero above row k) into an LDS buffer and beta into
+//     beta_s, and keep v below their R part;
+//   * one barrier;
+//   * the threads of every column c > k read v at their rows, form their part
+//     of w_c = v^T A[:, c], sum the 8 parts by shuffles and update their
+//     registers: A[:, c] -= beta v w_c.
+// Rows above k of a column c > k hold finished entries of R; v is zero there,
+// so they drop out without a mask.  The v buffers alternate, so the readers of
+// one reflector and the writers of the next never meet: one barrier per
+// reflector and 2 KB of LDS traffic, where a panel kept in LDS moves through
+// it at every reflector (its update was bound by LDS bandwidth).  Row k sits in register k / 8 of lane k % 8: the
+// reflectors go in blocks of 8 with the loop over blocks unrolled, so every
+// register index is static.  Q is formed backwards the same way: the threads
+// of column k broadcast v_k, then hold column k of Q (H_k e_k); the columns
+// c > k take H_k.
+constexpr int QRR_PARTS = 8;                      // threads per column
+constexpr int QRR_REGS = QR_ROWS / QRR_PARTS;     // rows per thread
+constexpr int QRR_THREADS = QRR_PARTS * S_MAX;    // 512
+constexpr int QRR_BLOCKS = S_MAX / QRR_PARTS;     // blocks of 8 reflectors
+
+template <typename T>
+__device__ __forceinline__ T part_sum8(T x) {
+  x += __shfl_xor(x, 1, QRR_PARTS);
+  x += __shfl_xor(x, 2, QRR_PARTS);
+  x += __shfl_xor(x, 4, QRR_PARTS);
+  return x;
+}
+
+template <typename T>
+__global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void qr_reg_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
+                                                            int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
+                                                            int skip_diag) {
+  __shared__ T vbuf[2][QR_ROWS];
+  __shared__ T beta_s[S_MAX];
+  const int t = blockIdx.x;
+  const int i = t % qr, j = t / qr;
+  if (skip_diag && i == j) return;
+  const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
+  T *a = A + (int64_t)t * stride;
+  T *rr = R ? R + (int64_t)t * n * n : nullptr;
+  const int tid = threadIdx.x, c = tid / QRR_PARTS, p = tid % QRR_PARTS;
+  const int kmax = min(m, n);
+  T y[QRR_REGS];
+#pragma unroll
+  for (int q = 0; q < QRR_REGS; ++q) {
+    const int r = QRR_PARTS * q + p;
+    y[q] = (c < n && r < m) ? a[r + (int64_t)c * lda] : T(0);
+  }
+  if (rr)
+    for (int e = tid; e < n * n; e += QRR_THREADS) rr[e] = 0;
+  __syncthreads();
+
+  // v of reflector k = 8K + kk into vb (rows >= 8K; zero above row k), from
+  // the registers of column k, whose row k holds v0
+  auto put_v = [&](T *vb, auto Kc, int kk, T v0) {
+    constexpr int K = decltype(Kc)::value;
+#pragma unroll
+    for (int q = K; q < QRR_REGS; ++q)
+      vb[QRR_PARTS * q + p] = q > K ? y[q] : (p > kk ? y[K] : (p == kk ? v0 : T(0)));
+  };
+  // A[:, c] -= beta v (v^T A[:, c]) for this thread's column
+  auto reflect = [&](const T *vb, auto Kc, T beta) {
+    constexpr int K = decltype(Kc)::value;
+    T w = 0, w1 = 0;
+#pragma unroll
+    for (int q = K; q < QRR_REGS; q += 2) {
+      w += vb[QRR_PARTS * q + p] * y[q];
+      if (q + 1 < QRR_REGS) w1 += vb[QRR_PARTS * (q + 1) + p] * y[q + 1];
+    }
+    const T bw = beta * part_sum8(w + w1);
+    // v is read again rather than held: 32 more registers would leave one
+    // workgroup per CU instead of two
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = K; q < QRR_REGS; ++q) y[q] -= vb[QRR_PARTS * q + p] * bw;
+  };
+
+  // factorisation
+  auto forward = [&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    for (int kk = 0; kk < QRR_PARTS; ++kk) {
+      const int k = QRR_PARTS * K + kk;
+      if (k >= kmax) break;
+      T *vb = vbuf[k & 1];
+      if (c == k) {
+        T tail = 0;
+#pragma unroll
+        for (int q = K; q < QRR_REGS; ++q)
+          if (q > K || p > kk) tail += y[q] * y[q];
+        tail = part_sum8(tail);
+        const T x0 = __shfl(y[K], kk, QRR_PARTS);
+        const T nrm = sqrt(tail + x0 * x0);
+        const T alpha = x0 >= T(0) ? -nrm : nrm;
+        const T v0 = x0 - alpha;
+        const T vtv = tail + v0 * v0;
+        const T beta = vtv > T(0) ? T(2) / vtv : T(0);
+        put_v(vb, Kc, kk, v0);
+        if (p == kk) y[K] = v0;
+        if (p == 0) {
+          beta_s[k] = beta;
+          if (rr) rr[k + k * n] = alpha;
+        }
+      }
+      __syncthreads();
+      if (c > k && c < n) reflect(vb, Kc, beta_s[k]);
+    }
+  };
+  forward(std::integral_constant<int, 0>());
+  forward(std::integral_constant<int, 1>());
+  forward(std::integral_constant<int, 2>());
+  forward(std::integral_constant<int, 3>());
+  forward(std::integral_constant<int, 4>());
+  forward(std::integral_constant<int, 5>());
+  forward(std::integral_constant<int, 6>());
+  forward(std::integral_constant<int, 7>());
+  static_assert(QRR_BLOCKS == 8, "one forward/backward call per block of 8 reflectors");
+
+  // R above the diagonal: rows r < c of column c are final
+  if (rr && c < n) {
+#pragma unroll
+    for (int q = 0; q < QRR_REGS; ++q) {
+      const int r = QRR_PARTS * q + p;
+      if (r < c && r < kmax) rr[r + c * n] = y[q];
+    }
+  }
+  // columns past the last reflector are zero in Q
+  if (c >= kmax) {
+#pragma unroll
+    for (int q = 0; q < QRR_REGS; ++q) y[q] = 0;
+  }
+  __syncthreads();   // the last reflector's readers are done with its v buffer
+
+  // Q = H_0 ... H_{kmax-1} [I; 0], formed backwards
+  auto backward = [&](auto Kc) {
+    constexpr int K = decltype(Kc)::value;
+    for (int kk = QRR_PARTS - 1; kk >= 0; --kk) {
+      const int k = QRR_PARTS * K + kk;
+      if (k >= kmax) continue;
+      T *vb = vbuf[k & 1];
+      const T beta = beta_s[k];
+      if (c == k) {
+        const T v0 = __shfl(y[K], kk, QRR_PARTS);
+        put_v(vb, Kc, kk, v0);
+        // column k of Q: H_k e_k
+#pragma unroll
+        for (int q = 0; q < QRR_REGS; ++q) {
+          const int r = QRR_PARTS * q + p;
+          y[q] = q < K ? T(0) : (r == k ? T(1) - beta * v0 * v0 : (r > k ? -beta * v0 * y[q] : T(0)));
+        }
+      }
+      __syncthreads();
+      if (c > k && c < n) reflect(vb, Kc, beta);
+    }
+  };
+  backward(std::integral_constant<int, 7>());
+  backward(std::integral_constant<int, 6>());
+  backward(std::integral_constant<int, 5>());
+  backward(std::integral_constant<int, 4>());
+  backward(std::integral_constant<int, 3>());
+  backward(std::integral_constant<int, 2>());
+  backward(std::integral_constant<int, 1>());
+  backward(std::integral_constant<int, 0>());
+
+  if (c < n) {
+#pragma unroll
+    for (int q = 0; q < QRR_REGS; ++q) {
+      const int r = QRR_PARTS * q + p;
+      if (r < m) a[r + (int64_t)c * lda] = y[q];
+    }
   }
 }
 
@@ -870,14 +882,13 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   if (st != TLR_OK) return st;
   MARK(pm.end());
   // 2. Y_t = Q R, Q kept in place
-  const bool staged = b <= QR_ROWS && (b + QR_PAD) * n <= QrPanel<T>::ELEMS;
   auto qr_launch = [&](T *A, T *R, int m_sel) {
-    if (staged)
-      hipLaunchKernelGGL((qr_tiles_kernel<T, true>), dim3(nt), dim3(QR_STAGED_THREADS), 0, s, A, (int)b, panel, R,
-                         L.qr, L.qc, rows, cols, b, m_sel, n, skip);
-    else
-      hipLaunchKernelGGL((qr_tiles_kernel<T, false>), dim3(nt), dim3(CT), 0, s, A, (int)b, panel, R, L.qr, L.qc,
+    if (b <= QR_ROWS && n <= S_MAX)
+      hipLaunchKernelGGL((qr_reg_kernel<T>), dim3(nt), dim3(QRR_THREADS), 0, s, A, (int)b, panel, R, L.qr, L.qc,
                          rows, cols, b, m_sel, n, skip);
+    else
+      hipLaunchKernelGGL((qr_tiles_kernel<T>), dim3(nt), dim3(CT), 0, s, A, (int)b, panel, R, L.qr, L.qc, rows,
+                         cols, b, m_sel, n, skip);
   };
   MARK(pm.begin(2));
   qr_launch(as<T>(w + L.y), (T *)nullptr, 0);
