@@ -382,7 +382,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   __shared__ T Js[JLD * S_MAX];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
-  __shared__ T offw[1 + 32];          // [1 + p]: largest |cos| pair thread p met in the sweep
+  __shared__ T offw[1 + 32];          // [1 + p]: largest cos^2 pair thread p met in the sweep
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -421,12 +421,19 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
       if (jp < npairs) {
         int p = player(jp), q = player(np - 1 - jp);
         if (p > q) { const int x = p; p = q; q = x; }
+        // the pair's rows of M stay in registers for the rotation (its rows
+        // of J are read only when it rotates: most pairs of a late sweep do not)
+        constexpr int JROWS = S_MAX / JPARTS;
+        T mp[JROWS], mq[JROWS];
         T al = 0, be = 0, ga = 0;
-        for (int r = jpart; r < np; r += JPARTS) {
-          const T mp = Ms[r + p * JLD], mq = Ms[r + q * JLD];
-          al += mp * mp;
-          be += mq * mq;
-          ga += mp * mq;
+#pragma unroll
+        for (int e = 0; e < JROWS; ++e) {
+          const int r = jpart + JPARTS * e;
+          mp[e] = r < np ? Ms[r + p * JLD] : T(0);
+          mq[e] = r < np ? Ms[r + q * JLD] : T(0);
+          al += mp[e] * mp[e];
+          be += mq[e] * mq[e];
+          ga += mp[e] * mq[e];
         }
 #pragma unroll
         for (int d = 1; d < JPARTS; d <<= 1) {
@@ -434,32 +441,40 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
           be += __shfl_xor(be, d, JPARTS);
           ga += __shfl_xor(ga, d, JPARTS);
         }
-        const T den = sqrt(al * be);
-        if (al > negligible && be > negligible && fabs(ga) > conv * den) {
-          if (jpart == 0 && fabs(ga) / den > offw[1 + jp]) offw[1 + jp] = fabs(ga) / den;
-          const T zeta = (be - al) / (T(2) * ga);
-          const T tt = (zeta >= T(0) ? T(1) : T(-1)) / (fabs(zeta) + sqrt(T(1) + zeta * zeta));
+        // |cos| of the pair's angle against conv, squared (no square root);
+        // the rotation's tangent tt = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
+        // zeta = (be - al) / (2 ga), written with one division and one root
+        const T g2 = ga * ga, ab = al * be;
+        if (al > negligible && be > negligible && g2 > conv * conv * ab) {
+          const T c2 = g2 / ab;
+          if (jpart == 0 && c2 > offw[1 + jp]) offw[1 + jp] = c2;
+          const T d = be - al;
+          const T sg = (d == T(0) || (d > T(0)) == (ga > T(0))) ? T(1) : T(-1);
+          const T tt = sg * T(2) * fabs(ga) / (fabs(d) + sqrt(d * d + T(4) * g2));
           const T cs = T(1) / sqrt(T(1) + tt * tt);
           const T sn = cs * tt;
-          for (int r = jpart; r < np; r += JPARTS) {
-            const T mp = Ms[r + p * JLD], mq = Ms[r + q * JLD];
-            Ms[r + p * JLD] = cs * mp - sn * mq;
-            Ms[r + q * JLD] = sn * mp + cs * mq;
-            const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
-            Js[r + p * JLD] = cs * jpv - sn * jqv;
-            Js[r + q * JLD] = sn * jpv + cs * jqv;
+#pragma unroll
+          for (int e = 0; e < JROWS; ++e) {
+            const int r = jpart + JPARTS * e;
+            if (r < np) {
+              const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
+              Ms[r + p * JLD] = cs * mp[e] - sn * mq[e];
+              Ms[r + q * JLD] = sn * mp[e] + cs * mq[e];
+              Js[r + p * JLD] = cs * jpv - sn * jqv;
+              Js[r + q * JLD] = sn * jpv + cs * jqv;
+            }
           }
         }
       }
       __syncthreads();
     }
-    // largest |cos| of the sweep (each pair thread kept its own maximum)
+    // largest cos^2 of the sweep (each pair thread kept its own maximum)
     T mx = 0;
     for (int x = 0; x < 32; ++x) mx = fmax(mx, offw[1 + x]);
     __syncthreads();
     if (tid < 32) offw[1 + tid] = 0;
     __syncthreads();
-    if (mx <= conv) break;
+    if (mx <= conv * conv) break;
   }
   // column norms, the order of decreasing sigma (ties by column index)
   for (int c = wave; c < n; c += CT / 64) {
