@@ -361,11 +361,12 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
 // Threads per column pair: 8 consecutive lanes of one wave take rows part,
 // part + 8, ... of a pair and combine their partial sums with lane shuffles.
 constexpr int JPARTS = 8;
-// LDS column stride of M and J: 72 doubles put the 64-byte row runs of
-// consecutive columns on four different quarters of the banks (at 64 every
-// column started on the same banks, and the eight columns a wave reads at
-// once conflicted eight ways)
-constexpr int JLD = S_MAX + 8;
+// M and J live in dynamic LDS sized to the tile: np columns of stride
+// jacobi_ld(np) = np + 2 each (2 x 56 x 58 doubles at the sketch width 56,
+// 52 KB: three workgroups per CU, where arrays sized for S_MAX took 74 KB
+// and allowed two).  An even stride that is not a multiple of 32 doubles
+// starts the eight columns a wave reads at once on different banks.
+__host__ __device__ constexpr int jacobi_ld(int np) { return np + 2; }
 
 // One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
 // then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
@@ -378,8 +379,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
                                                         int32_t *ranks, int32_t *flags, const T *norms2, int qr,
                                                         int qc, int n, int max_rank, T tol, T conv,
                                                         int skip_diag) {
-  __shared__ T Ms[JLD * S_MAX];
-  __shared__ T Js[JLD * S_MAX];
+  extern __shared__ __attribute__((aligned(16))) unsigned char jacobi_lds[];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
   __shared__ T offw[1 + 32];          // [1 + p]: largest cos^2 pair thread p met in the sweep
@@ -393,16 +393,19 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     }
     return;
   }
+  const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
+  const int npairs = np / 2;
+  const int JLD = jacobi_ld(np);
+  T *Ms = reinterpret_cast<T *>(jacobi_lds);
+  T *Js = Ms + JLD * np;
   const T *rt = R + (int64_t)t * n * n;
-  for (int e = tid; e < S_MAX * S_MAX; e += CT) {
-    const int r = e % S_MAX, c = e / S_MAX;
+  for (int e = tid; e < np * np; e += CT) {
+    const int r = e % np, c = e / np;
     Ms[r + c * JLD] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
     Js[r + c * JLD] = r == c ? T(1) : T(0);
   }
   if (tid < 33) offw[tid] = 0;
   __syncthreads();
-  const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
-  const int npairs = np / 2;
   // thread (pair, part): pair jp = tid / 8 (CT / 8 = 32 pairs at most), rows
   // part, part + 8, ...  The eight lanes of a pair form its 2 x 2 Gram block,
   // each computes the rotation and applies it to its own rows: one barrier
@@ -922,7 +925,22 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   MARK(pm.end());
   // 5. Jacobi on M = R2^T, ranks
   MARK(pm.begin(5));
-  hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 0, s, as<T>(w + L.r2), as<T>(w + L.w),
+  const int jnp = (n + 1) & ~1;
+  {
+    // the widest sketch (S_MAX columns) needs more than the default 64 KB of
+    // dynamic LDS in fp64
+    static std::once_flag lds_attr;
+    static hipError_t lds_err = hipSuccess;
+    std::call_once(lds_attr, [] {
+      lds_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&jacobi_rank_kernel<T>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(2 * S_MAX * jacobi_ld(S_MAX) * sizeof(T)));
+    });
+    if (lds_err != hipSuccess)
+      return fail(TLR_ERR_HIP, std::string("Jacobi SVD LDS attribute: ") + hipGetErrorString(lds_err));
+  }
+  hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 2 * jnp * jacobi_ld(jnp) * sizeof(T), s,
+                     as<T>(w + L.r2), as<T>(w + L.w),
                      as<T>(w + L.j), as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
                      norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
   CHECK_LAUNCH("Jacobi SVD");
