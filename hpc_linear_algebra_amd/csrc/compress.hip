@@ -206,11 +206,40 @@ constexpr int QRR_REGS = QR_ROWS / QRR_PARTS;     // rows per thread
 constexpr int QRR_THREADS = QRR_PARTS * S_MAX;    // 512
 constexpr int QRR_BLOCKS = S_MAX / QRR_PARTS;     // blocks of 8 reflectors
 
+// Sum over each group of 8 consecutive lanes, every lane getting it, with
+// DPP lane moves (VALU, no LDS round trip): partner i ^ 1 and i ^ 2 by quad
+// permutations, then the other half of the 8 by the half-row mirror (lane i
+// of a group reads lane 7 - i, which after two steps holds the other quad's
+// sum).  Each step adds a pair in either order, so all lanes agree exactly.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// x from lane `lane` of the wave (a wave-uniform lane index: v_readlane)
+__device__ __forceinline__ double lane_value(double x, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror
 template <typename T>
 __device__ __forceinline__ T part_sum8(T x) {
-  x += __shfl_xor(x, 1, QRR_PARTS);
-  x += __shfl_xor(x, 2, QRR_PARTS);
-  x += __shfl_xor(x, 4, QRR_PARTS);
+  x += dpp_move<DPP_QUAD_XOR1>(x);
+  x += dpp_move<DPP_QUAD_XOR2>(x);
+  x += dpp_move<DPP_HALF_MIRROR>(x);
   return x;
 }
 
@@ -276,7 +305,8 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         for (int q = K; q < QRR_REGS; ++q)
           if (q > K || p > kk) tail += y[q] * y[q];
         tail = part_sum8(tail);
-        const T x0 = __shfl(y[K], kk, QRR_PARTS);
+        // row k: register K of lane kk of column k's lanes (wave k / 8)
+        const T x0 = lane_value(y[K], QRR_PARTS * (k % (64 / QRR_PARTS)) + kk);
         const T nrm = sqrt(tail + x0 * x0);
         const T alpha = x0 >= T(0) ? -nrm : nrm;
         const T v0 = x0 - alpha;
@@ -327,7 +357,7 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       T *vb = vbuf[k & 1];
       const T beta = beta_s[k];
       if (c == k) {
-        const T v0 = __shfl(y[K], kk, QRR_PARTS);
+        const T v0 = lane_value(y[K], QRR_PARTS * (k % (64 / QRR_PARTS)) + kk);
         put_v(vb, Kc, kk, v0);
         // column k of Q: H_k e_k
 #pragma unroll
@@ -373,12 +403,13 @@ __host__ __device__ constexpr int jacobi_ld(int np) { return np + 2; }
 // sigma_k) to Wout + t n n, J to Jout + t n n, the columns in decreasing
 // order of sigma to perm + t n, the rank to ranks[t] (0 for a skipped
 // diagonal tile) and flags[t] = 1 when the tolerance was not met within
-// max_rank columns (the rank is then max_rank).
+// max_rank columns (the rank is then max_rank); jstat[2t], jstat[2t + 1] =
+// the sweeps run and the rotations applied (the measure of its work).
 template <typename T>
 __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T *Jout, int32_t *perm,
-                                                        int32_t *ranks, int32_t *flags, const T *norms2, int qr,
-                                                        int qc, int n, int max_rank, T tol, T conv,
-                                                        int skip_diag) {
+                                                        int32_t *ranks, int32_t *flags, int32_t *jstat,
+                                                        const T *norms2, int qr, int qc, int n, int max_rank, T tol,
+                                                        T conv, int skip_diag) {
   extern __shared__ __attribute__((aligned(16))) unsigned char jacobi_lds[];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
@@ -390,9 +421,13 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     if (tid == 0) {
       ranks[t] = 0;
       flags[t] = 0;
+      jstat[2 * t] = 0;
+      jstat[2 * t + 1] = 0;
     }
     return;
   }
+  __shared__ int nrot;
+  if (tid == 0) nrot = 0;
   const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
   const int npairs = np / 2;
   const int JLD = jacobi_ld(np);
@@ -417,13 +452,16 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   // every sweep would run).
   const T eps = sizeof(T) == 8 ? T(2.220446049250313e-16) : T(1.1920929e-7);
   const T negligible = (T(n) * eps) * (T(n) * eps) * norms2[t];
+  int sweeps = 0, my_rot = 0;
   for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
+    ++sweeps;
+    // round-robin: position 0 holds player 0, position x >= 1 player
+    // 1 + (x - 1 + round) mod (np - 1), i.e. x at round 0, and each round
+    // every player but 0 moves on by one (np - 1 wrapping to 1)
+    int pa = jp, pb = np - 1 - jp;        // the players at this pair's two positions
     for (int round = 0; round < np - 1; ++round) {
-      // round-robin: position 0 holds player 0, position x >= 1 player 1 + (x - 1 + round) mod (np - 1)
-      auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + round) % (np - 1); };
       if (jp < npairs) {
-        int p = player(jp), q = player(np - 1 - jp);
-        if (p > q) { const int x = p; p = q; q = x; }
+        const int p = min(pa, pb), q = max(pa, pb);
         // the pair's rows of M stay in registers for the rotation (its rows
         // of J are read only when it rotates: most pairs of a late sweep do not)
         constexpr int JROWS = S_MAX / JPARTS;
@@ -438,19 +476,20 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
           be += mq[e] * mq[e];
           ga += mp[e] * mq[e];
         }
-#pragma unroll
-        for (int d = 1; d < JPARTS; d <<= 1) {
-          al += __shfl_xor(al, d, JPARTS);
-          be += __shfl_xor(be, d, JPARTS);
-          ga += __shfl_xor(ga, d, JPARTS);
-        }
+        static_assert(JPARTS == QRR_PARTS, "the 8-lane sums serve both kernels");
+        al = part_sum8(al);
+        be = part_sum8(be);
+        ga = part_sum8(ga);
         // |cos| of the pair's angle against conv, squared (no square root);
         // the rotation's tangent tt = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
         // zeta = (be - al) / (2 ga), written with one division and one root
         const T g2 = ga * ga, ab = al * be;
         if (al > negligible && be > negligible && g2 > conv * conv * ab) {
           const T c2 = g2 / ab;
-          if (jpart == 0 && c2 > offw[1 + jp]) offw[1 + jp] = c2;
+          if (jpart == 0) {
+            if (c2 > offw[1 + jp]) offw[1 + jp] = c2;
+            ++my_rot;
+          }
           const T d = be - al;
           const T sg = (d == T(0) || (d > T(0)) == (ga > T(0))) ? T(1) : T(-1);
           const T tt = sg * T(2) * fabs(ga) / (fabs(d) + sqrt(d * d + T(4) * g2));
@@ -469,6 +508,8 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
           }
         }
       }
+      if (pa != 0) pa = pa == np - 1 ? 1 : pa + 1;
+      pb = pb == np - 1 ? 1 : pb + 1;
       __syncthreads();
     }
     // largest cos^2 of the sweep (each pair thread kept its own maximum)
@@ -479,6 +520,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     __syncthreads();
     if (mx <= conv * conv) break;
   }
+  if (my_rot > 0) atomicAdd(&nrot, my_rot);   // LDS; read after the barriers below
   // column norms, the order of decreasing sigma (ties by column index)
   for (int c = wave; c < n; c += CT / 64) {
     T s = 0;
@@ -527,13 +569,16 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     }
     ranks[t] = r;
     flags[t] = fl;
+    jstat[2 * t] = sweeps;
+    jstat[2 * t + 1] = nrot;
   }
 }
 
 // Prefix sums of the ranks: outer offsets in tile-row order, inner offsets
 // in tile-column order, one thread per tile row (then per tile column) and
 // one thread for the scan of the q row sums.  info[0] = columns in all,
-// info[1] = tiles flagged, info[2] = 1 when the columns exceed the capacity.
+// info[1] = tiles flagged, info[2] = 1 when the columns exceed the capacity,
+// info[3], info[4] = Jacobi sweeps and rotations summed over the tiles.
 constexpr int SCAN_THREADS = 256;
 __device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, int skip_diag, int64_t *ooff,
                                          int64_t *ioff, int64_t *sums, int64_t *total_out) {
@@ -588,24 +633,37 @@ __device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, i
   }
 }
 
-__global__ __launch_bounds__(SCAN_THREADS) void rank_scan_kernel(const int32_t *ranks, const int32_t *flags, int qr,
-                                                                int qc, int skip_diag, int64_t *ooff, int64_t *ioff,
-                                                                int64_t *sums, int64_t capacity, int32_t *info) {
+__global__ __launch_bounds__(SCAN_THREADS) void rank_scan_kernel(const int32_t *ranks, const int32_t *flags,
+                                                                const int32_t *jstat, int qr, int qc, int skip_diag,
+                                                                int64_t *ooff, int64_t *ioff, int64_t *sums,
+                                                                int64_t capacity, int32_t *info) {
   __shared__ int64_t total;
-  __shared__ int nflag_w[SCAN_THREADS / 64];
+  __shared__ int64_t part_w[3][SCAN_THREADS / 64];
   offsets_by_rows_and_cols(ranks, qr, qc, skip_diag, ooff, ioff, sums, &total);
-  int nf = 0;
-  for (int t = threadIdx.x; t < qr * qc; t += SCAN_THREADS)
+  int64_t nf = 0, nsw = 0, nrot = 0;
+  for (int t = threadIdx.x; t < qr * qc; t += SCAN_THREADS) {
     if (!(skip_diag && t % qr == t / qr)) nf += flags[t];
+    nsw += jstat[2 * t];
+    nrot += jstat[2 * t + 1];
+  }
   nf = wave_sum(nf);
-  if ((threadIdx.x & 63) == 0) nflag_w[threadIdx.x >> 6] = nf;
+  nsw = wave_sum(nsw);
+  nrot = wave_sum(nrot);
+  if ((threadIdx.x & 63) == 0) {
+    part_w[0][threadIdx.x >> 6] = nf;
+    part_w[1][threadIdx.x >> 6] = nsw;
+    part_w[2][threadIdx.x >> 6] = nrot;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int nflag = 0;
-    for (int w = 0; w < SCAN_THREADS / 64; ++w) nflag += nflag_w[w];
+    int64_t x[3] = {0, 0, 0};
+    for (int k = 0; k < 3; ++k)
+      for (int w = 0; w < SCAN_THREADS / 64; ++w) x[k] += part_w[k][w];
     info[0] = (int32_t)min<int64_t>(total, 0x7fffffff);
-    info[1] = nflag;
+    info[1] = (int32_t)x[0];
     info[2] = total > capacity ? 1 : 0;
+    info[3] = (int32_t)min<int64_t>(x[1], 0x7fffffff);
+    info[4] = (int32_t)min<int64_t>(x[2], 0x7fffffff);
   }
 }
 
@@ -730,8 +788,8 @@ T *as(void *p) { return static_cast<T *>(p); }
 struct CompressLayout {
   int qr = 0, qc = 0, s = 0;
   int64_t ntile = 0;
-  size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, ooff = 0,
-         ioff = 0, sums = 0, total = 0;
+  size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, jstat = 0,
+         ooff = 0, ioff = 0, sums = 0, total = 0;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -755,6 +813,7 @@ CompressLayout compress_layout(int64_t rows, int64_t cols, int64_t b, int max_ra
   L.perm = o; o += al256((size_t)L.ntile * L.s * 4);
   L.ranks = o; o += al256((size_t)L.ntile * 4);
   L.flags = o; o += al256((size_t)L.ntile * 4);
+  L.jstat = o; o += al256((size_t)L.ntile * 8);
   L.ooff = o; o += al256((size_t)L.ntile * 8);
   L.ioff = o; o += al256((size_t)L.ntile * 8);
   L.sums = o; o += al256((size_t)std::max(L.qr, L.qc) * 8);
@@ -942,7 +1001,7 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 2 * jnp * jacobi_ld(jnp) * sizeof(T), s,
                      as<T>(w + L.r2), as<T>(w + L.w),
                      as<T>(w + L.j), as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
-                     norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
+                     as<int32_t>(w + L.jstat), norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
   CHECK_LAUNCH("Jacobi SVD");
   MARK(pm.end());
   // 6. U_t = Q_t W_t, V_t = Q2_t J_t        (s_i x s, s_j x s)
@@ -957,7 +1016,7 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   // 7. offsets, 8. packed factors and diagonal slots
   MARK(pm.begin(7));
   hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, as<int32_t>(w + L.ranks),
-                     as<int32_t>(w + L.flags), L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
+                     as<int32_t>(w + L.flags), as<int32_t>(w + L.jstat), L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
                      as<int64_t>(w + L.sums), capacity, info);
   CHECK_LAUNCH("rank scan");
   MARK(pm.end());

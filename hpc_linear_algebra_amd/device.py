@@ -130,7 +130,7 @@ class TLROutputGemm:
     dense.  Three library calls on one stream: tlr_expand of C into a dense
     scratch (skipped when beta == 0), tlr_gemm_execute into that scratch, and
     tlr_compress of it into the result buffers (device ranks, diagonal slots,
-    packed factors with room for ``capacity`` columns, info[3])."""
+    packed factors with room for ``capacity`` columns, info[5])."""
 
     def __init__(self, dtype: str, opA: str, A: DeviceTLR, opB: str, B: DeviceTLR, b: int, has_diag: bool,
                  max_rank: int, capacity: Optional[int] = None, budget: int = 0, device="cuda"):
@@ -153,7 +153,7 @@ class TLROutputGemm:
         self.diag = torch.zeros((max(1, self.qr) * b * b) if has_diag else 1, dtype=tdt, device=device)
         self.outer = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
         self.inner = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
-        self.info = torch.zeros(3, dtype=torch.int32, device=device)
+        self.info = torch.zeros(5, dtype=torch.int32, device=device)
 
     def __call__(self, alpha: float, A: DeviceTLR, B: DeviceTLR, beta: float, C: Optional[DeviceTLR], tol: float,
                  omega: torch.Tensor, stream: Optional[int] = None):
