@@ -77,12 +77,29 @@ __global__ __launch_bounds__(CT) void tile_norms_kernel(const T *X, int64_t ldx,
   const int i = t % qr, j = t / qr;
   const int si = tile_rows(rows, b, i), sj = tile_rows(cols, b, j);
   const T *x = X + (int64_t)i * b + (int64_t)j * b * ldx;
-  T acc = 0;
-  for (int c = 0; c < sj; ++c)
-    for (int r = threadIdx.x; r < si; r += CT) {
-      const T v = x[r + (int64_t)c * ldx];
-      acc += v * v;
+  // eight columns per step with their own partial sums: eight loads in
+  // flight per thread instead of one serial chain
+  constexpr int CU = 8;
+  T part[CU];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) part[u] = 0;
+  for (int r = threadIdx.x; r < si; r += CT) {
+    int c = 0;
+    for (; c + CU <= sj; c += CU) {
+      T v[CU];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) v[u] = x[r + (int64_t)(c + u) * ldx];
+#pragma unroll
+      for (int u = 0; u < CU; ++u) part[u] += v[u] * v[u];
     }
+    for (; c < sj; ++c) {
+      const T v = x[r + (int64_t)c * ldx];
+      part[0] += v * v;
+    }
+  }
+  T acc = 0;
+#pragma unroll
+  for (int u = 0; u < CU; ++u) acc += part[u];
   acc = block_sum(acc, red);
   if (threadIdx.x == 0) norms2[t] = acc;
 }
