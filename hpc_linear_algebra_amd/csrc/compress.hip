@@ -701,9 +701,20 @@ __global__ __launch_bounds__(CT) void pack_kernel(const T *X, int64_t ldx, const
     if (threadIdx.x == 0) ranks_out[t] = 0;
     const T *x = X + (int64_t)i * b + (int64_t)j * b * ldx;
     T *d = diag + (int64_t)i * b * b;
-    for (int e = threadIdx.x; e < si * si; e += CT) {
-      const int r = e % si, c = e / si;
-      d[r + (int64_t)c * b] = x[r + (int64_t)c * ldx];
+    // eight elements per thread and step, loads first: eight in flight
+    constexpr int PU = 8;
+    for (int e0 = 0; e0 < si * si; e0 += PU * CT) {
+      T v[PU];
+#pragma unroll
+      for (int u = 0; u < PU; ++u) {
+        const int e = e0 + u * CT + threadIdx.x;
+        v[u] = e < si * si ? x[e % si + (int64_t)(e / si) * ldx] : T(0);
+      }
+#pragma unroll
+      for (int u = 0; u < PU; ++u) {
+        const int e = e0 + u * CT + threadIdx.x;
+        if (e < si * si) d[e % si + (int64_t)(e / si) * b] = v[u];
+      }
     }
     return;
   }
@@ -712,12 +723,27 @@ __global__ __launch_bounds__(CT) void pack_kernel(const T *X, int64_t ldx, const
   if (info[2]) return;
   const T *uf = Uf + (int64_t)t * fstride;
   const T *vf = Vf + (int64_t)t * fstride;
-  for (int k = 0; k < r; ++k) {
-    const int src = perm[(int64_t)t * n + k];
-    T *uo = outer + (ooff[t] + k) * b;
-    T *vo = inner + (ioff[t] + k) * b;
-    for (int e = threadIdx.x; e < si; e += CT) uo[e] = uf[e + (int64_t)src * b];
-    for (int e = threadIdx.x; e < sj; e += CT) vo[e] = vf[e + (int64_t)src * b];
+  // kept column k: U from column perm[k] of Uf, V from Vf; eight columns
+  // per step, loads first
+  constexpr int PK = 8;
+  const int64_t o0 = ooff[t], i0 = ioff[t];
+  for (int k0 = 0; k0 < r; k0 += PK) {
+    for (int e = threadIdx.x; e < max(si, sj); e += CT) {
+      T uv[PK], vv[PK];
+#pragma unroll
+      for (int u = 0; u < PK; ++u) {
+        const int k = k0 + u;
+        const int src = k < r ? perm[(int64_t)t * n + k] : 0;
+        uv[u] = (k < r && e < si) ? uf[e + (int64_t)src * b] : T(0);
+        vv[u] = (k < r && e < sj) ? vf[e + (int64_t)src * b] : T(0);
+      }
+#pragma unroll
+      for (int u = 0; u < PK; ++u) {
+        const int k = k0 + u;
+        if (k < r && e < si) outer[(o0 + k) * b + e] = uv[u];
+        if (k < r && e < sj) inner[(i0 + k) * b + e] = vv[u];
+      }
+    }
   }
 }
 
