@@ -408,12 +408,14 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
 // Threads per column pair: 8 consecutive lanes of one wave take rows part,
 // part + 8, ... of a pair and combine their partial sums with lane shuffles.
 constexpr int JPARTS = 8;
-// M and J live in dynamic LDS sized to the tile: np columns of stride
-// jacobi_ld(np) = np + 2 each (2 x 56 x 58 doubles at the sketch width 56,
-// 52 KB: three workgroups per CU, where arrays sized for S_MAX took 74 KB
+// M and J live in dynamic LDS sized to the tile: np columns of 8 RPL rows
+// (RPL = jacobi_rpl(np) rows per lane of a pair, the rows past n zero) at
+// stride jacobi_ld(RPL) = 8 RPL + 2 (2 x 56 x 58 doubles at the sketch width
+// 56, 52 KB: three workgroups per CU, where arrays sized for S_MAX took 74 KB
 // and allowed two).  An even stride that is not a multiple of 32 doubles
 // starts the eight columns a wave reads at once on different banks.
-__host__ __device__ constexpr int jacobi_ld(int np) { return np + 2; }
+__host__ __device__ constexpr int jacobi_rpl(int np) { return (np + JPARTS - 1) / JPARTS; }
+__host__ __device__ constexpr int jacobi_ld(int rpl) { return JPARTS * rpl + 2; }
 
 // One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
 // then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
@@ -422,7 +424,9 @@ __host__ __device__ constexpr int jacobi_ld(int np) { return np + 2; }
 // diagonal tile) and flags[t] = 1 when the tolerance was not met within
 // max_rank columns (the rank is then max_rank); jstat[2t], jstat[2t + 1] =
 // the sweeps run and the rotations applied (the measure of its work).
-template <typename T>
+// RPL = jacobi_rpl(np) is a compile-time count, so the row loops of a round
+// run without guards: the kernel is bound by VALU issue, not by LDS.
+template <typename T, int RPL>
 __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T *Jout, int32_t *perm,
                                                         int32_t *ranks, int32_t *flags, int32_t *jstat,
                                                         const T *norms2, int qr, int qc, int n, int max_rank, T tol,
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   extern __shared__ __attribute__((aligned(16))) unsigned char jacobi_lds[];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
-  __shared__ T offw[1 + 32];          // [1 + p]: largest cos^2 pair thread p met in the sweep
+  __shared__ T offw[2][32];           // [sweep % 2][pair]: the pair slot's largest cos^2 in the sweep
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -447,16 +451,16 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   if (tid == 0) nrot = 0;
   const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
   const int npairs = np / 2;
-  const int JLD = jacobi_ld(np);
+  constexpr int JLD = jacobi_ld(RPL), ROWS = JPARTS * RPL;
   T *Ms = reinterpret_cast<T *>(jacobi_lds);
   T *Js = Ms + JLD * np;
   const T *rt = R + (int64_t)t * n * n;
-  for (int e = tid; e < np * np; e += CT) {
-    const int r = e % np, c = e / np;
+  for (int e = tid; e < ROWS * np; e += CT) {
+    const int r = e % ROWS, c = e / ROWS;
     Ms[r + c * JLD] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
     Js[r + c * JLD] = r == c ? T(1) : T(0);
   }
-  if (tid < 33) offw[tid] = 0;
+  if (tid < 64) offw[tid / 32][tid % 32] = 0;
   __syncthreads();
   // thread (pair, part): pair jp = tid / 8 (CT / 8 = 32 pairs at most), rows
   // part, part + 8, ...  The eight lanes of a pair form its 2 x 2 Gram block,
@@ -476,19 +480,19 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     // 1 + (x - 1 + round) mod (np - 1), i.e. x at round 0, and each round
     // every player but 0 moves on by one (np - 1 wrapping to 1)
     int pa = jp, pb = np - 1 - jp;        // the players at this pair's two positions
+    T cmax = 0;                            // this pair slot's largest cos^2 in the sweep
     for (int round = 0; round < np - 1; ++round) {
       if (jp < npairs) {
         const int p = min(pa, pb), q = max(pa, pb);
         // the pair's rows of M stay in registers for the rotation (its rows
         // of J are read only when it rotates: most pairs of a late sweep do not)
-        constexpr int JROWS = S_MAX / JPARTS;
-        T mp[JROWS], mq[JROWS];
+        T mp[RPL], mq[RPL];
         T al = 0, be = 0, ga = 0;
 #pragma unroll
-        for (int e = 0; e < JROWS; ++e) {
+        for (int e = 0; e < RPL; ++e) {
           const int r = jpart + JPARTS * e;
-          mp[e] = r < np ? Ms[r + p * JLD] : T(0);
-          mq[e] = r < np ? Ms[r + q * JLD] : T(0);
+          mp[e] = Ms[r + p * JLD];
+          mq[e] = Ms[r + q * JLD];
           al += mp[e] * mp[e];
           be += mq[e] * mq[e];
           ga += mp[e] * mq[e];
@@ -502,39 +506,35 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
         // zeta = (be - al) / (2 ga), written with one division and one root
         const T g2 = ga * ga, ab = al * be;
         if (al > negligible && be > negligible && g2 > conv * conv * ab) {
-          const T c2 = g2 / ab;
-          if (jpart == 0) {
-            if (c2 > offw[1 + jp]) offw[1 + jp] = c2;
-            ++my_rot;
-          }
+          cmax = fmax(cmax, g2 / ab);
+          if (jpart == 0) ++my_rot;
           const T d = be - al;
           const T sg = (d == T(0) || (d > T(0)) == (ga > T(0))) ? T(1) : T(-1);
           const T tt = sg * T(2) * fabs(ga) / (fabs(d) + sqrt(d * d + T(4) * g2));
           const T cs = T(1) / sqrt(T(1) + tt * tt);
           const T sn = cs * tt;
 #pragma unroll
-          for (int e = 0; e < JROWS; ++e) {
+          for (int e = 0; e < RPL; ++e) {
             const int r = jpart + JPARTS * e;
-            if (r < np) {
-              const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
-              Ms[r + p * JLD] = cs * mp[e] - sn * mq[e];
-              Ms[r + q * JLD] = sn * mp[e] + cs * mq[e];
-              Js[r + p * JLD] = cs * jpv - sn * jqv;
-              Js[r + q * JLD] = sn * jpv + cs * jqv;
-            }
+            const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
+            Ms[r + p * JLD] = cs * mp[e] - sn * mq[e];
+            Ms[r + q * JLD] = sn * mp[e] + cs * mq[e];
+            Js[r + p * JLD] = cs * jpv - sn * jqv;
+            Js[r + q * JLD] = sn * jpv + cs * jqv;
           }
         }
+        // the slot's maximum, before the sweep's last barrier; the buffers
+        // alternate by sweep, so the next sweep's writes never meet this
+        // sweep's reads
+        if (jpart == 0 && round == np - 2) offw[sweep & 1][jp] = cmax;
       }
       if (pa != 0) pa = pa == np - 1 ? 1 : pa + 1;
       pb = pb == np - 1 ? 1 : pb + 1;
       __syncthreads();
     }
-    // largest cos^2 of the sweep (each pair thread kept its own maximum)
+    // largest cos^2 of the sweep
     T mx = 0;
-    for (int x = 0; x < 32; ++x) mx = fmax(mx, offw[1 + x]);
-    __syncthreads();
-    if (tid < 32) offw[1 + tid] = 0;
-    __syncthreads();
+    for (int x = 0; x < npairs; ++x) mx = fmax(mx, offw[sweep & 1][x]);
     if (mx <= conv * conv) break;
   }
   if (my_rot > 0) atomicAdd(&nrot, my_rot);   // LDS; read after the barriers below
@@ -877,6 +877,27 @@ tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t
 template <typename T>
 T conv_tol() { return sizeof(T) == 8 ? T(1e-12) : T(1e-5f); }   // |cos| between kept columns after Jacobi
 
+// One launch of the Jacobi kernel for RPL rows per lane; the widest sketch
+// (S_MAX columns, RPL = 8) needs more than the default 64 KB of dynamic LDS
+// in fp64, which is raised once per instantiation.
+template <typename T, int RPL, typename... Args>
+tlr_status launch_jacobi(int64_t nt, int np, hipStream_t s, Args... args) {
+  const size_t lds = 2 * (size_t)np * jacobi_ld(RPL) * sizeof(T);
+  if (lds > 65536) {
+    static std::once_flag once;
+    static hipError_t err = hipSuccess;
+    std::call_once(once, [] {
+      err = hipFuncSetAttribute(reinterpret_cast<const void *>(&jacobi_rank_kernel<T, RPL>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(2 * JPARTS * RPL * jacobi_ld(RPL) * sizeof(T)));
+    });
+    if (err != hipSuccess)
+      return fail(TLR_ERR_HIP, std::string("Jacobi SVD LDS attribute: ") + hipGetErrorString(err));
+  }
+  hipLaunchKernelGGL((jacobi_rank_kernel<T, RPL>), dim3((unsigned)nt), dim3(CT), lds, s, args...);
+  return TLR_OK;
+}
+
 // Optional event pairs around the kernel groups of a compression
 // (tlr_compress_profile): 0 tile norms, 1 sketch product, 2 QR of the
 // sketches, 3 projection product, 4 QR of the projections, 5 Jacobi SVD and
@@ -1029,22 +1050,26 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   MARK(pm.begin(5));
   const int jnp = (n + 1) & ~1;
   {
-    // the widest sketch (S_MAX columns) needs more than the default 64 KB of
-    // dynamic LDS in fp64
-    static std::once_flag lds_attr;
-    static hipError_t lds_err = hipSuccess;
-    std::call_once(lds_attr, [] {
-      lds_err = hipFuncSetAttribute(reinterpret_cast<const void *>(&jacobi_rank_kernel<T>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)(2 * S_MAX * jacobi_ld(S_MAX) * sizeof(T)));
-    });
-    if (lds_err != hipSuccess)
-      return fail(TLR_ERR_HIP, std::string("Jacobi SVD LDS attribute: ") + hipGetErrorString(lds_err));
+    tlr_status js = TLR_OK;
+    auto jac = [&](auto rc) {
+      constexpr int RPL = decltype(rc)::value;
+      js = launch_jacobi<T, RPL>(nt, jnp, s, as<T>(w + L.r2), as<T>(w + L.w), as<T>(w + L.j),
+                                 as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
+                                 as<int32_t>(w + L.jstat), norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(),
+                                 skip);
+    };
+    switch (jacobi_rpl(jnp)) {
+      case 1: jac(std::integral_constant<int, 1>()); break;
+      case 2: jac(std::integral_constant<int, 2>()); break;
+      case 3: jac(std::integral_constant<int, 3>()); break;
+      case 4: jac(std::integral_constant<int, 4>()); break;
+      case 5: jac(std::integral_constant<int, 5>()); break;
+      case 6: jac(std::integral_constant<int, 6>()); break;
+      case 7: jac(std::integral_constant<int, 7>()); break;
+      default: jac(std::integral_constant<int, 8>()); break;
+    }
+    if (js != TLR_OK) return js;
   }
-  hipLaunchKernelGGL(jacobi_rank_kernel<T>, dim3(nt), dim3(CT), 2 * jnp * jacobi_ld(jnp) * sizeof(T), s,
-                     as<T>(w + L.r2), as<T>(w + L.w),
-                     as<T>(w + L.j), as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
-                     as<int32_t>(w + L.jstat), norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(), skip);
   CHECK_LAUNCH("Jacobi SVD");
   MARK(pm.end());
   // 6. U_t = Q_t W_t, V_t = Q2_t J_t        (s_i x s, s_j x s)
