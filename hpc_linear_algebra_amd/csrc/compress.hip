@@ -295,13 +295,11 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   // A[:, c] -= beta v (v^T A[:, c]) for this thread's column
   auto reflect = [&](const T *vb, auto Kc, T beta) {
     constexpr int K = decltype(Kc)::value;
-    T w = 0, w1 = 0;
+    // four partial sums: chains of at most 8 dependent FMAs
+    T w4[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int q = K; q < QRR_REGS; q += 2) {
-      w += vb[QRR_PARTS * q + p] * y[q];
-      if (q + 1 < QRR_REGS) w1 += vb[QRR_PARTS * (q + 1) + p] * y[q + 1];
-    }
-    const T bw = beta * part_sum8(w + w1);
+    for (int q = K; q < QRR_REGS; ++q) w4[(q - K) & 3] += vb[QRR_PARTS * q + p] * y[q];
+    const T bw = beta * part_sum8((w4[0] + w4[1]) + (w4[2] + w4[3]));
     // v is read again rather than held: 32 more registers would leave one
     // workgroup per CU instead of two
     asm volatile("" ::: "memory");
@@ -317,11 +315,11 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       if (k >= kmax) break;
       T *vb = vbuf[k & 1];
       if (c == k) {
-        T tail = 0;
+        T t4[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int q = K; q < QRR_REGS; ++q)
-          if (q > K || p > kk) tail += y[q] * y[q];
-        tail = part_sum8(tail);
+          if (q > K || p > kk) t4[(q - K) & 3] += y[q] * y[q];
+        const T tail = part_sum8((t4[0] + t4[1]) + (t4[2] + t4[3]));
         // row k: register K of lane kk of column k's lanes (wave k / 8)
         const T x0 = lane_value(y[K], QRR_PARTS * (k % (64 / QRR_PARTS)) + kk);
         const T nrm = sqrt(tail + x0 * x0);
