@@ -2,8 +2,9 @@
 //
 // The same task tables as the 32/64-bit kernel (tlr_desc.h): each workgroup
 // reads one entry (task, m0, n0) and computes a 128 x BN block of that task's
-// output (BN = 128 or 64, chosen per launch; the final update uses a second
-// kernel with 256 x 256 blocks, further down), accumulating over the task's K
+// output (BN = 128 or 64, chosen per launch; the final update and other
+// launches large enough use a second kernel with 256 x 256 blocks, further
+// down), accumulating over the task's K
 // segments in float with v_mfma_f32_16x16x32_{f16,bf16}, then writes
 // C = alpha*acc + beta*C (final update) or C = acc (workspace intermediates),
 // rounded once to the 16-bit type.
@@ -291,12 +292,14 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
   }
 }
 
-// ---- 256 x 256 blocks for the final update ----------------------------------
+// ---- 256 x 256 blocks -----------------------------------------------------
 //
 // A 128 x 128 block moves one operand byte from L2 into LDS per 64 flops; at
 // the 16-bit matrix-core rate that is more traffic than the caches deliver,
 // so the final update (the launch with long K and whole output tiles) runs in
-// 256 x 256 blocks instead.  Eight wave64s, two per SIMD, each own 128 x 64
+// 256 x 256 blocks instead, and so do other launches with enough such blocks
+// to fill the chip (there a 128 x 128 block's 32 KB of output is too little
+// to carry the fixed cost of a block).  Eight wave64s, two per SIMD, each own 128 x 64
 // of the block (8 x 4 MFMA tiles: 128 accumulator registers, half of what a
 // wave may hold at two waves per SIMD; one workgroup per CU).
 //
@@ -585,7 +588,9 @@ __device__ __forceinline__ void gemm_block16w(const DevTask &t, int m0, int n0, 
   }
 }
 
-template <typename H>
+// STAGE only names the launch (1, 2, 3 or STAGE_SIDE), so that profiles tell
+// the final update from the other wide launches.
+template <typename H, int STAGE>
 __global__ __launch_bounds__(NTW) void wide_gemm16_kernel(const DevTask *__restrict__ tasks,
                                                           const DevTile *__restrict__ tiles,
                                                           const int64_t *__restrict__ coltab, Bases bases,
@@ -647,9 +652,17 @@ template <typename H>
 void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                 const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const float a = (float)alpha, b = (float)beta, c = preload_scale16(alpha, beta);
-  if (bn == BW)
-    hipLaunchKernelGGL(wide_gemm16_kernel<H>, dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
-  else if (bn == Blk16<2>::BN)
+  if (bn == BW) {
+    if (stage == 1)
+      hipLaunchKernelGGL((wide_gemm16_kernel<H, 1>), dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
+    else if (stage == 2)
+      hipLaunchKernelGGL((wide_gemm16_kernel<H, 2>), dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
+    else if (stage == 3)
+      hipLaunchKernelGGL((wide_gemm16_kernel<H, 3>), dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
+    else
+      hipLaunchKernelGGL((wide_gemm16_kernel<H, STAGE_SIDE>), dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases,
+                         a, b, c);
+  } else if (bn == Blk16<2>::BN)
     launch16_w<H, 2>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
   else
     launch16_w<H, 4>(stage, dim3(n), s, tasks, tiles, coltab, bases, a, b, c);
@@ -661,7 +674,6 @@ int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, cons
                      const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
   if (n_tiles <= 0) return 0;
   if (bn != Blk16<2>::BN && bn != Blk16<4>::BN && bn != BW) return (int)hipErrorInvalidValue;
-  if (bn == BW && stage != 3) return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F16)
     launch16_t<_Float16>(stage, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);

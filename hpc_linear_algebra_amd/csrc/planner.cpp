@@ -531,6 +531,19 @@ static double task_exec_flops(const DevTask &d) {
 // others go narrow when 128 x 128 blocks would give fewer than four workgroups
 // per CU (the coupling and diagonal-term GEMMs: few, with K = b).  Measured on
 // the store-bound right/left product, narrow blocks were no faster.
+// 16-bit launches whose 256 x 256 blocks still fill the chip twice take them
+// (the final update always): a 128 x 128 block of the store-bound
+// right/left product writes only 32 KB and spends most of its time on the
+// fixed cost of a block.  Measured on N = 32768 (heavy ranks): right/left
+// product 1.22 -> 1.10 ms, coupling 0.44 -> 0.39 ms; launches of fewer
+// wide blocks (the couplings at N = 16384) ran slower in them.
+static bool wide16(int stage, const TaskList &tl) {
+  if (stage == 3) return true;
+  int64_t blocks = 0;
+  for (const DevTask &d : tl.t) blocks += ceil_div(d.M, BW16) * ceil_div(d.N, BW16);
+  return blocks >= 2 * 256;
+}
+
 static int launch_bn(int stage, const TaskList &tl) {
   if (stage == 3) return BN;
   int64_t blocks = 0;
@@ -564,7 +577,7 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl, bo
   L.task_off = task0;
   L.bn = strip ? STRIP_W : launch_bn(stage, tl);
   L.bm = BM;
-  if (stage == 3 && p.es == 2) L.bm = L.bn = BW16;   // the 16-bit final update: 256 x 256 blocks
+  if (p.es == 2 && !strip && wide16(stage, tl)) L.bm = L.bn = BW16;   // 16-bit: 256 x 256 blocks
   const int bm = L.bm, bn = L.bn;
   struct TaskCost { int32_t t; int64_t per_block, blocks; int mode; };
   std::vector<TaskCost> order;
@@ -1046,7 +1059,7 @@ static tlr_status validate(const Plan &p, bool deep) {
     const bool strip = L.bm == BM && L.bn == STRIP_W;
     const bool shape_ok = strip ? (L.stage == 2 && p.es != 2)
                           : L.bm == BM ? (L.bn == BN || L.bn == BN_NARROW)
-                                       : (L.bm == BW16 && L.bn == BW16 && L.stage == 3 && p.es == 2);
+                                       : (L.bm == BW16 && L.bn == BW16 && p.es == 2);
     if (!shape_ok || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
       return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block shape or task range");
     for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t) {

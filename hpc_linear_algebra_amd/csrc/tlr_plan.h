@@ -14,7 +14,7 @@ namespace tlr {
 constexpr int BM = 128;            // workgroup block rows of every grouped launch
 constexpr int BN = 128;            // block columns: wide launches
 constexpr int BN_NARROW = 64;      // block columns: narrow launches (see launch_bn)
-constexpr int BW16 = 256;          // block rows and columns of the 16-bit final update
+constexpr int BW16 = 256;          // block rows and columns of the wide 16-bit launches (final update, large ones)
 constexpr int STRIP_W = 512;        // block columns of a strip launch (right/left product, K <= 16)
 constexpr int STRIP_K = 16;         // largest K of a strip task: one K stage of the kernel
 constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
@@ -59,7 +59,7 @@ struct Launch {
   int wait_launch;   // >= 0: this launch's stream first waits for that launch (another stream)
   int fork_at;       // side launch: the launch of the group's stream it forks before; else -1
   bool on_side;      // a stage-1-3 launch that runs on the group's side stream (after the side launch)
-  int bm;            // block rows of the launch's workgroups (BM, or BW16 for a 16-bit final update)
+  int bm;            // block rows of the launch's workgroups (BM, or BW16 for a wide 16-bit launch)
   int bn;            // block columns (BN or BN_NARROW; BW16 with bm = BW16; STRIP_W for a strip launch)
   bool beta_one;     // a later pass of the per-k loop over C: its updates use beta = 1
   int64_t task_off;  // the launch's tasks are tasks[task_off, task_off + n_tasks)

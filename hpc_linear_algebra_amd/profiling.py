@@ -120,12 +120,18 @@ def kernel_source_hash(sixteen_bit: bool = False) -> str:
     return h.hexdigest()[:16]
 
 
+def _matches(rx: str, name: str) -> bool:
+    """rx found in a kernel name as the profiler wrote it (mangled or not) or
+    in its short form (as the summaries print it)."""
+    return re.search(rx, name) is not None or re.search(rx, _short(name)) is not None
+
+
 def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, kernel_regex, copy_bytes=1 << 30):
     """HBM bytes per dispatch of the kernels matching kernel_regex: FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
     reads for a plain device copy of copy_bytes."""
     def mean_for(d, counter, rx):
-        v = [x for (k, c), xs in _counter_means(d).items() if c == counter and re.search(rx, k) for x in xs]
+        v = [x for (k, c), xs in _counter_means(d).items() if c == counter and _matches(rx, k) for x in xs]
         return sum(v) / len(v) if v else None
     cf = mean_for(cfetch_dir, "FETCH_SIZE", "copyBuffer")
     cw = mean_for(cwrite_dir, "WRITE_SIZE", "copyBuffer")
@@ -152,7 +158,7 @@ def mfma_busy(pmc_dir, kernel_regex):
     vals = _counter_means(pmc_dir)
 
     def mean_for(counter):
-        v = [x for (k, c), xs in vals.items() if c == counter and re.search(kernel_regex, k) for x in xs]
+        v = [x for (k, c), xs in vals.items() if c == counter and _matches(kernel_regex, k) for x in xs]
         return sum(v) / len(v) if v else None
     busy, active = mean_for("SQ_VALU_MFMA_BUSY_CYCLES"), mean_for("GRBM_GUI_ACTIVE")
     frac = busy / (SIMDS * active / XCDS) if busy is not None and active else None
