@@ -202,22 +202,22 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
 // (c, p) of QRR_THREADS (8 consecutive lanes per column) holds column c of the
 // panel at rows p, p + 8, ..., p + 248 (QRR_REGS registers, zero past m) for
 // the whole factorisation and for the forming of Q.  Reflector k:
-//   * the 8 threads of column k form the tail norm (lane shuffles), alpha,
+//   * the 8 threads of column k form the tail norm (an 8-lane sum), alpha,
 //     beta and v, write v (zero above row k) into an LDS buffer and beta into
 //     beta_s, and keep v below their R part;
 //   * one barrier;
 //   * the threads of every column c > k read v at their rows, form their part
-//     of w_c = v^T A[:, c], sum the 8 parts by shuffles and update their
+//     of w_c = v^T A[:, c], sum the 8 parts (part_sum8) and update their
 //     registers: A[:, c] -= beta v w_c.
 // Rows above k of a column c > k hold finished entries of R; v is zero there,
 // so they drop out without a mask.  The v buffers alternate, so the readers of
 // one reflector and the writers of the next never meet: one barrier per
 // reflector and 2 KB of LDS traffic, where a panel kept in LDS moves through
-// it at every reflector (its update was bound by LDS bandwidth).  Row k sits in register k / 8 of lane k % 8: the
-// reflectors go in blocks of 8 with the loop over blocks unrolled, so every
-// register index is static.  Q is formed backwards the same way: the threads
-// of column k broadcast v_k, then hold column k of Q (H_k e_k); the columns
-// c > k take H_k.
+// it at every reflector (its update was bound by LDS bandwidth).  Row k sits
+// in register k / 8 of lane k % 8: the reflectors go in blocks of 8 with the
+// loop over blocks unrolled, so every register index is static.  Q is formed
+// backwards the same way: the threads of column k broadcast v_k, then hold
+// column k of Q (H_k e_k); the columns c > k take H_k.
 constexpr int QRR_PARTS = 8;                      // threads per column
 constexpr int QRR_REGS = QR_ROWS / QRR_PARTS;     // rows per thread
 constexpr int QRR_THREADS = QRR_PARTS * S_MAX;    // 512
