@@ -292,6 +292,113 @@ __device__ __forceinline__ void gemm_block16(const DevTask &t, int m0, int n0, c
   }
 }
 
+// ---- strips of the right/left product ------------------------------------
+//
+// A right/left-product task of K <= 32 (one k-step of the 16-bit MFMA) does a
+// few MFMAs per 128 x 128 block and then stores it, so block overheads (the
+// task read, the operand fetch and its latency) sit in front of every 32 KB
+// of stores.  A strip block covers 128 rows and STRIP_W = 512 columns: the A
+// tile (128 x 32) and the B strip (32 x 512) go to LDS once, as in
+// gemm_block16 (K-contiguous rows, A rows placed by a_lds_row), then four
+// 128-column chunks run back to back, each 16 MFMAs per wave followed by its
+// stores in gemm_block16's epilogue layout, with no barrier between chunks.
+// 50 KB of LDS: three workgroups per CU.
+template <typename H>
+__global__ __launch_bounds__(NT16) __attribute__((amdgpu_waves_per_eu(3)))
+void strip_gemm16_kernel(const DevTask *__restrict__ tasks, const DevTile *__restrict__ tiles,
+                         const int64_t *__restrict__ coltab, Bases bases) {
+  constexpr int NJ = 4, BN = Blk16<NJ>::BN;   // a chunk: two waves along N, 4 tiles of 16 columns each
+  static_assert(STRIP_W % BN == 0 && STRIP_W == 2 * NT16, "strip fill: two B units per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM16 * LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[STRIP_W * LROW];
+  const DevTile e = tiles[blockIdx.x];
+  if (e.task < 0) return;
+  const DevTask &t = tasks[e.task];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  const int M = t.M, N = t.N, m0 = e.m0, n0 = e.n0;
+  const int nrem = min(N - n0, STRIP_W);
+  const int K = t.nseg > 0 ? t.seg[0].K : 0;   // a task without a segment stores zeros
+  uint16_t *C = static_cast<uint16_t *>(const_cast<void *>(bases.p[t.c_base])) + t.c_off;
+
+  // one operand unit of the single stage (the fields of gemm_block16's Unit)
+  auto unit = [&](const DevOperand &o, bool is_a, int uidx, int first, int rem) {
+    Unit u;
+    const uint16_t *p = static_cast<const uint16_t *>(bases.p[o.base]) + o.off;
+    const int64_t ld = o.ld;
+    u.kc = is_a ? o.trans == 1 : o.trans == 0;
+    u.base = u.kc ? p + (int64_t)first * ld : p + first;
+    u.kstep = u.kc ? KS : (int64_t)KS * ld;
+    u.ldb = (uint32_t)(ld * 2);
+    const int srow = u.kc ? 4 * (uidx >> 2) : 4 * (uidx & 7), ccol = u.kc ? 8 * (uidx & 3) : 8 * (uidx >> 3);
+    u.lane = (uint32_t)((int64_t)srow * ld + ccol) * 2u;
+    u.s0 = srow;
+    u.c0 = ccol;
+    u.s_lim = u.kc ? rem : 0;
+    u.c_lim = u.kc ? 0 : rem;
+    return u;
+  };
+  if (K > 0) {
+    const DevSeg &d = t.seg[0];
+    u4 x[4];
+    if (tid < BM16) {   // the A tile: 128 units
+      const Unit u = unit(d.a, true, tid, m0, M - m0);
+      load_unit(u, 0, K, x);
+      store_unit<true>(As, u.kc ? tid >> 2 : tid >> 3, u.kc ? tid & 3 : tid & 7, u.kc, x);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // the B strip: 512 units
+      const int uidx = tid + NT16 * h;
+      const Unit u = unit(d.b, false, uidx, n0, nrem);
+      load_unit(u, 0, K, x);
+      store_unit<false>(Bs, u.kc ? uidx >> 2 : uidx >> 3, u.kc ? uidx & 3 : uidx & 7, u.kc, x);
+    }
+  }
+  __syncthreads();
+  u4 af[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u4 *>(As + (64 * wm + 16 * i + r) * LROW + 8 * g);
+  const int nch = (nrem + BN - 1) / BN;
+  for (int ch = 0; ch < nch; ++ch) {
+    f4 acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f4{0, 0, 0, 0};
+    if (K > 0) {
+      u4 bf[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        bf[j] = *reinterpret_cast<const u4 *>(Bs + (ch * BN + wn * 16 * NJ + 16 * j + r) * LROW + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = M16<H>::mma(af[i], bf[j], acc[i][j]);
+    }
+    // stores: lane (r, g) holds rows 64 wm + 32 h + 8 g .. +7 of each of its columns
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int nl = ch * BN + wn * 16 * NJ + 16 * j + r;
+      if (nl >= nrem) continue;
+      const int n = n0 + nl;
+      const int64_t oc = t.ctab < 0 ? (int64_t)n * t.ldc : coltab[t.ctab + n];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = m0 + 64 * wm + 32 * h + 8 * g;
+        if (m >= M) continue;
+        u4 y;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          y[w] = (uint32_t)from_f<H>(acc[2 * h + (w >> 1)][j][2 * (w & 1)]) |
+                 ((uint32_t)from_f<H>(acc[2 * h + (w >> 1)][j][2 * (w & 1) + 1]) << 16);
+        *reinterpret_cast<u4 *>(C + oc + m) = y;
+      }
+    }
+  }
+}
+
 // ---- 256 x 256 blocks -----------------------------------------------------
 //
 // A 128 x 128 block moves one operand byte from L2 into LDS per 64 flops; at
@@ -652,7 +759,9 @@ template <typename H>
 void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tasks, const DevTile *tiles,
                 const int64_t *coltab, const Bases &bases, double alpha, double beta) {
   const float a = (float)alpha, b = (float)beta, c = preload_scale16(alpha, beta);
-  if (bn == BW) {
+  if (bn == STRIP_W) {
+    hipLaunchKernelGGL(strip_gemm16_kernel<H>, dim3(n), dim3(NT16), 0, s, tasks, tiles, coltab, bases);
+  } else if (bn == BW) {
     if (stage == 1)
       hipLaunchKernelGGL((wide_gemm16_kernel<H, 1>), dim3(n), dim3(NTW), 0, s, tasks, tiles, coltab, bases, a, b, c);
     else if (stage == 2)
@@ -673,7 +782,8 @@ void launch16_t(int stage, int bn, unsigned n, hipStream_t s, const DevTask *tas
 int launch_grouped16(tlr_dtype dt, int stage, int bn, const DevTask *tasks, const DevTile *tiles, int64_t n_tiles,
                      const int64_t *coltab, const Bases &bases, double alpha, double beta, void *stream) {
   if (n_tiles <= 0) return 0;
-  if (bn != Blk16<2>::BN && bn != Blk16<4>::BN && bn != BW) return (int)hipErrorInvalidValue;
+  if (bn != Blk16<2>::BN && bn != Blk16<4>::BN && bn != BW && !(bn == STRIP_W && stage == 2))
+    return (int)hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F16)
     launch16_t<_Float16>(stage, bn, (unsigned)n_tiles, s, tasks, tiles, coltab, bases, alpha, beta);

@@ -552,10 +552,13 @@ static int launch_bn(int stage, const TaskList &tl) {
 }
 
 // A right/left-product task that the strip kernel runs: at most one K segment
-// of at most STRIP_K, B N-contiguous, output C = acc (32/64-bit types).
-static bool strip_task(const DevTask &d) {
+// of at most STRIP_K, B N-contiguous, output C = acc (32/64-bit types); on
+// 16-bit types at most STRIP_K16, either layout of A and B.
+static bool strip_task(const Plan &p, const DevTask &d) {
   if (d.final_ || d.nseg > 1) return false;
-  return d.nseg == 0 || (d.seg[0].K <= STRIP_K && d.seg[0].b.trans == 1);
+  if (d.nseg == 0) return true;
+  if (p.es == 2) return d.seg[0].K <= STRIP_K16;
+  return d.seg[0].K <= STRIP_K && d.seg[0].b.trans == 1;
 }
 
 // Appends one launch of `tl` (nothing when empty) and returns its index, or -1.
@@ -626,9 +629,9 @@ static int emit_launch(Plan &p, int stage, int group, int rect, TaskList &tl, bo
 // products that read only inputs on the side stream (forked before stage 1, so
 // they run beside stages 1 and 2), the right/left product (stage 2) and the
 // final update (stage 3), which waits for the side launch.
-// On 32/64-bit types the right/left product is split: tasks with K <= STRIP_K
-// go to a strip launch on the group's stream, the rest to a grouped launch on
-// the side stream (below).  The split is made only when the strip launch
+// The right/left product is split: tasks with K <= STRIP_K (16-bit types:
+// STRIP_K16) go to a strip launch on the group's stream, the rest to a
+// grouped launch on the side stream (below).  The split is made only when the strip launch
 // would fill the chip twice (STRIP_MIN_BLOCKS workgroups); a handful of strip
 // tasks beside the grouped launch measured slower than leaving them in it.
 constexpr int64_t STRIP_MIN_BLOCKS = 2 * 256;
@@ -640,7 +643,7 @@ static void emit_stages(Plan &p, int group, int rect, TaskList &l1, TaskList &si
   int64_t strip_blocks = 0;
   for (size_t t = 0; t < l2.t.size(); ++t) {
     const DevTask &x = l2.t[t];
-    const bool s = p.es != 2 && strip_task(x);
+    const bool s = strip_task(p, x);
     if (s) strip_blocks += ceil_div(x.M, BM) * ceil_div(x.N, STRIP_W);
     TaskList &dst = s ? l2s : l2g;
     dst.t.push_back(x);
@@ -1057,14 +1060,14 @@ static tlr_status validate(const Plan &p, bool deep) {
   std::vector<int64_t> seen(p.tasks.size(), 0), want(p.tasks.size(), -1);
   for (const Launch &L : p.launches) {
     const bool strip = L.bm == BM && L.bn == STRIP_W;
-    const bool shape_ok = strip ? (L.stage == 2 && p.es != 2)
+    const bool shape_ok = strip ? L.stage == 2
                           : L.bm == BM ? (L.bn == BN || L.bn == BN_NARROW)
                                        : (L.bm == BW16 && L.bn == BW16 && p.es == 2);
     if (!shape_ok || L.task_off < 0 || L.task_off + L.n_tasks > (int64_t)p.tasks.size())
       return fail(TLR_ERR_INVALID_ARG, "internal: bad launch block shape or task range");
     for (int64_t t = L.task_off; t < L.task_off + L.n_tasks; ++t) {
       // the strip kernel holds one K stage and fills LDS from an N-contiguous B
-      if (strip && !strip_task(p.tasks[t]))
+      if (strip && !strip_task(p, p.tasks[t]))
         return fail(TLR_ERR_INVALID_ARG, "internal: task in a strip launch that the strip kernel cannot run");
       want[t] = ceil_div(p.tasks[t].M, L.bm) * ceil_div(p.tasks[t].N, L.bn);
     }

@@ -17,6 +17,7 @@ constexpr int BN_NARROW = 64;      // block columns: narrow launches (see launch
 constexpr int BW16 = 256;          // block rows and columns of the wide 16-bit launches (final update, large ones)
 constexpr int STRIP_W = 512;        // block columns of a strip launch (right/left product, K <= 16)
 constexpr int STRIP_K = 16;         // largest K of a strip task: one K stage of the kernel
+constexpr int STRIP_K16 = 32;       // the same for 16-bit types: one k-step of their MFMA
 constexpr size_t WS_ALIGN = 256;   // byte alignment of every workspace buffer
 constexpr int NUM_XCD = 8;         // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int AUX_PER_GROUP = 3;   // auxiliary streams of a group: two for load modes, one side lane

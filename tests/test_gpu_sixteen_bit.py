@@ -45,6 +45,23 @@ def test_tlr_tlr_ops(dtype, n, b, opA, opB):
         say(f"  rel error {e:.3e} (tol {TOL[dtype]:.1e})")
 
 
+@pytest.mark.parametrize("dtype,opA,opB,flags", [("f16", "T", "N", F_LEFT), ("bf16", "N", "T", F_RIGHT),
+                                                 ("f16", "N", "N", F_RIGHT), ("bf16", "T", "T", F_LEFT)])
+def test_strip_launches_sixteen_bit(dtype, opA, opB, flags):
+    """A 28 x 28 grid of 128-tiles with stored ranks 0-40: the right or left
+    product's tasks of rank <= 32 (one 16-bit k-step) make enough 128 x 512
+    blocks for a strip launch, the rank-40 tasks stay in the grouped launch;
+    both against the oracle."""
+    n, b = 28 * 128, 128
+    A, B, C = _pair(4600 + flags, n, b, dtype, lo=0, hi=40)
+    say(f"{dtype} strip launches {opA}{opB} flags={flags}")
+    e = check_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags)
+    say(f"  rel error {e:.3e} (tol {TOL[dtype]:.1e})")
+    _, g = run_tlr(A, B, opA, opB, 0.75, 0.5, C, flags=flags, return_plan=True)
+    stage2 = [x for x in g.launches() if x["stage"] == 2]
+    assert len(stage2) == 2 and min(x["tasks"] for x in stage2) > 0, stage2
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_large_blocks_and_full_ranks(dtype):
     # tiles of 256 with ranks up to 256: tasks of several blocks, K segments of many stages

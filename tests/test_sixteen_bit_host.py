@@ -93,30 +93,38 @@ def test_bfloat16_grid():
     assert on_grid(np.array([1 + 3 * 2.0 ** -8]), "bf16")[0] == 1 + 2.0 ** -6
 
 
-def test_sixteen_bit_wide_blocks_where_they_fill_the_chip():
-    """16-bit launches take 256 x 256 blocks when those still fill the chip
-    twice (512 blocks), the final update always; smaller launches keep
-    128-row blocks.  Grid: q = 32 tiles of b = 512, every off-diagonal rank
-    24, dense diagonals, the left order (T, N as the N = 16384 workload):
-      left product  992 tasks (i, k != i) of 512 x 744 -> 992 * 2 * 3 = 5952 wide blocks;
-      final update  1024 tiles of 512 x 512            -> 4096 wide blocks;
-      coupling      32 tasks of 744 x 744              -> 288 wide blocks: narrow,
-                    32 * 6 * 6 = 1152 blocks of 128 x 128;
-      side launch   32 of 744 x 512 and 32 of 512 x 744 -> 384 wide: narrow,
-                    64 * 24 = 1536 blocks of 128 x 128.
-    Workgroup counts are padded to whole multiples of 8 XCD lists."""
+def test_sixteen_bit_block_shapes_by_launch_size():
+    """16-bit launch shapes on a q = 32 grid of b = 512 tiles with dense
+    diagonals, the left order (T, N as the N = 16384 workload).  Workgroup
+    counts are padded to whole multiples of 8 XCD lists.
+    Ranks 24 (every right/left-product task K <= 32):
+      left product  992 tasks of 512 x 744 in 128 x 512 strips -> 992 * 4 * 2 = 7936;
+      final update  1024 tiles of 512 x 512 in 256 x 256 blocks -> 4096;
+      coupling      32 tasks of 744 x 744: 288 wide blocks, under 512, so
+                    128 x 128 blocks -> 32 * 6 * 6 = 1152;
+      side launch   32 of 744 x 512 and 32 of 512 x 744: 384 wide, so 1536 of 128 x 128.
+    Ranks 40 (K > 32: no strips):
+      left product  992 tasks of 512 x 1240 in 256 x 256 blocks -> 992 * 2 * 5 = 9920;
+      coupling      32 tasks of 1240 x 1240 -> 32 * 25 = 800 wide blocks (>= 512)."""
     q, b = 32, 512
-    s = _shape(q * b, b, _ranks(q, 24))
-    p = T.tlr_gemm_analyze("f16", "T", s, "N", s, ldc=q * b, flags=T.TLR_PLAN_FORCE_LEFT)
-    wg = {}
-    for l in range(T.tlr_plan_info(p)["launches"]):
-        L = T.tlr_plan_launch(p, l)
-        wg[L["stage"]] = L["workgroups"]
-    assert 5952 <= wg[2] < 5952 * 1.1
-    assert 4096 <= wg[3] < 4096 * 1.1
-    assert 1152 <= wg[1] < 1152 * 1.1
-    assert 1536 <= wg[4] < 1536 * 1.1
-    # the same grid in fp32 keeps 128-row blocks everywhere but for the strips
-    p32 = T.tlr_gemm_analyze("f32", "T", s, "N", s, ldc=q * b, flags=T.TLR_PLAN_FORCE_LEFT)
-    stages = [T.tlr_plan_launch(p32, l) for l in range(T.tlr_plan_info(p32)["launches"])]
-    assert max(L["workgroups"] for L in stages if L["stage"] == 3) >= 16384
+
+    def workgroups(rank, dt="f16"):
+        s = _shape(q * b, b, _ranks(q, rank))
+        p = T.tlr_gemm_analyze(dt, "T", s, "N", s, ldc=q * b, flags=T.TLR_PLAN_FORCE_LEFT)
+        wg = {}
+        for l in range(T.tlr_plan_info(p)["launches"]):
+            L = T.tlr_plan_launch(p, l)
+            wg.setdefault(L["stage"], []).append(L["workgroups"])
+        return wg
+
+    def near(x, want):
+        return want <= x < want * 1.1
+
+    wg = workgroups(24)
+    assert len(wg[2]) == 1 and near(wg[2][0], 7936)
+    assert near(wg[3][0], 4096) and near(wg[1][0], 1152) and near(wg[4][0], 1536)
+    wg = workgroups(40)
+    assert len(wg[2]) == 1 and near(wg[2][0], 9920)
+    assert near(wg[1][0], 800) and near(wg[3][0], 4096)
+    # fp32 keeps 128 x 128 blocks in its final update
+    assert workgroups(24, "f32")[3][0] >= 16384
