@@ -24,7 +24,7 @@ def _short(name: str) -> str:
     m = re.search(r"(grouped_gemm_kernel<[^>]*>|strip_gemm_kernel<[^>]*>|single_gemm_kernel<[^>]*>|scale_kernel<[^>]*>)", name)
     if m:
         return m.group(1)
-    m = re.search(r"(grouped_gemm16_kernel|wide_gemm16_kernel|scale16_kernel)I(DF16b|DF16_)((?:Li\d+E)*)", name)
+    m = re.search(r"(grouped_gemm16_kernel|wide_gemm16_kernel|strip_gemm16_kernel|scale16_kernel)I(DF16b|DF16_)((?:Li\d+E)*)", name)
     if m:
         t = "bfloat16" if m.group(2) == "DF16b" else "half"
         args = re.findall(r"Li(\d+)E", m.group(3))

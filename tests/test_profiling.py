@@ -27,6 +27,8 @@ def test_short_names():
         == "wide_gemm16_kernel<half>"
     assert P._short("_ZN3tlr12_GLOBAL__N_118wide_gemm16_kernelIDF16_Li3EEEvPKNS_7DevTaskEPKNS_7DevTileE") \
         == "wide_gemm16_kernel<half, 3>"
+    assert P._short("_ZN3tlr12_GLOBAL__N_119strip_gemm16_kernelIDF16bEEvPKNS_7DevTaskEPKNS_7DevTileE") \
+        == "strip_gemm16_kernel<bfloat16>"
     assert P._short("_ZN3tlr12_GLOBAL__N_119grouped_gemm_kernelIfLi1ELi0ELi4EEEvPK") \
         == "grouped_gemm_kernel<float, 1, 0, 4>"
     assert P._short("_ZN3tlr12_GLOBAL__N_117strip_gemm_kernelIdLi1EEEvPKNS_7DevTaskEPKNS_7DevTileEPKlNS_5BasesE") \
