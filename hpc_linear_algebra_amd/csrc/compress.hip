@@ -872,8 +872,14 @@ tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t
   return TLR_OK;
 }
 
+// The Jacobi sweeps stop once no pair's |cos| exceeds this bound.  The column
+// norms then equal the singular values to about bound^2 relative (the Gram
+// matrix's off-diagonal part moves its eigenvalues only to second order):
+// 1e-16 for fp64, its rounding, and 1e-10 for fp32, below its rounding.  The
+// truncation error itself is exact whatever the bound, since W J^T = M with J
+// orthogonal: dropping columns of W drops exactly their norms.
 template <typename T>
-T conv_tol() { return sizeof(T) == 8 ? T(1e-12) : T(1e-5f); }   // |cos| between kept columns after Jacobi
+T conv_tol() { return sizeof(T) == 8 ? T(1e-8) : T(1e-5f); }
 
 // One launch of the Jacobi kernel for RPL rows per lane; the widest sketch
 // (S_MAX columns, RPL = 8) needs more than the default 64 KB of dynamic LDS
