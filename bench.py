@@ -345,23 +345,29 @@ def bench_tlr_out(args):
     names = ["expand", "product", "compress"]
     dom = int(np.argmax(phases.mean(axis=0)))
     # the dominant kernel: the one-sided Jacobi SVD of the s x s cores (one
-    # launch per step), bound by its own arithmetic; its work from the sweeps
-    # and rotations it reports (info[3], info[4]): per sweep and tile,
-    # s/2 pairs x (s - 1) rounds of a 2 x 2 Gram block (3 dot products of
-    # length s, 6 s flops), per rotation 2 columns of M and 2 of J (12 s flops)
+    # launch per step), bound by its own arithmetic; its work from the pair
+    # visits and rotations it reports (info[3], info[4]): per visit a 2 x 2
+    # Gram block (3 dot products over the k rows a core has, 6 k flops), per
+    # rotation 2 columns of M and 2 of J (12 k flops), where k is the tile's
+    # count of sketch basis columns (info[5] sums them; the mean stands in for
+    # each tile's own)
     n_s = cfg["max_rank"] + 8           # sketch width
     sizes = [min(b, N - i * b) for i in range(q)]
+    tiles = q * (q - 1)
+    kbar = int(info[5]) / tiles
 
-    def qr_flops(m, n):
-        # per reflector k: w = A^T v and the rank-1 update on an (m-k) x (n-k-1)
-        # block, in the factorisation and again when Q is formed
-        return sum(8.0 * (m - k) * (n - k - 1) for k in range(min(m, n)))
-    qr_work = sum(qr_flops(sizes[i], n_s) for i in range(q) for j in range(q) if i != j)   # one launch
+    def qr_flops(m, n, k):
+        # per reflector j < k: w = A^T v and the rank-1 update on the
+        # (m-j) x (n-j-1) block (4 flops an element), then the forming of the
+        # k columns of Q the same way on (m-j) x (k-j-1)
+        return sum(4.0 * (m - j) * ((n - j - 1) + (k - j - 1)) for j in range(min(m, k)))
+    kr = int(round(kbar))
+    qr_work = 0.5 * sum(qr_flops(sizes[i], n_s, kr) + qr_flops(sizes[j], kr, kr)
+                        for i in range(q) for j in range(q) if i != j)   # one launch, the mean of the two
     qr_ms = (group_ms[2] + group_ms[4]) / (2 * calls)
     qr_tf = qr_work / (qr_ms * 1e-3) / 1e12
-    sweeps, rotations = int(info[3]), int(info[4])
-    np_s = n_s + (n_s & 1)
-    jac_work = sweeps * (np_s // 2) * (np_s - 1) * 6.0 * np_s + rotations * 12.0 * np_s
+    visits, rotations = int(info[3]), int(info[4])
+    jac_work = visits * 6.0 * kbar + rotations * 12.0 * kbar
     jac_ms = group_ms[5] / calls
     jac_tf = jac_work / (jac_ms * 1e-3) / 1e12
     vec_peak = VECTOR_PEAK[dtype]
@@ -411,10 +417,12 @@ def bench_tlr_out(args):
                      "frac": round(jac_tf / vec_peak, 4), "traffic": None,
                      "kernel": "one-sided Jacobi SVD of the s x s cores and the ranks (one launch per step)",
                      "launch_ms": round(jac_ms, 4), "algorithmic_flops": jac_work,
-                     "work": {"sweeps": sweeps, "rotations": rotations, "sketch_width": n_s}},
+                     "work": {"pair_visits": visits, "rotations": rotations, "sketch_width": n_s,
+                              "basis_columns_mean": round(kbar, 2)}},
         "panel_qr": {"bound": "alu", "achieved": round(qr_tf, 3), "peak": vec_peak, "unit": "TFLOP/s",
                      "frac": round(qr_tf / vec_peak, 4), "launch_ms": round(qr_ms, 4),
-                     "algorithmic_flops": qr_work, "note": "two launches per step (the sketches, the projections)"},
+                     "algorithmic_flops": qr_work, "note": "two launches per step (the sketches, the projections); "
+                     "each tile's basis columns replaced by their mean"},
         "cpu_baseline": cpu,
     }
     log(f"bench: {ms:.3f} ms/step ({', '.join(f'{n} {phases[:, k].mean():.3f}' for k, n in enumerate(names))}), "

@@ -105,17 +105,17 @@ __global__ __launch_bounds__(CT) void tile_norms_kernel(const T *X, int64_t ldx,
 }
 
 // Householder QR of one m x n panel a (column-major, leading dim lda; in LDS
-// or global memory), n <= S_MAX, by a workgroup of NTH threads.  The panel
-// is overwritten by the explicit Q (m x n, orthonormal columns; columns past
-// min(m, n) zero); with rr != nullptr the n x n upper factor is written to rr
+// or global memory), n <= S_MAX, by a workgroup of NTH threads, with at most
+// kcap reflectors.  The panel is overwritten by the explicit Q (m x n,
+// orthonormal columns; columns past min(m, n, kcap) zero); with rr != nullptr the n x n upper factor is written to rr
 // (column-major, zero below the diagonal).  Reflector k: v = x - alpha e_k with
 // alpha = -sign(x_k) ||x||, H = I - beta v v^T, beta = 2 / (v^T v); v stays in
 // column k (rows >= k) until Q is formed.
 template <typename T, int NTH>
-__device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *red, T *beta_s) {
+__device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, int kcap, T *red, T *beta_s) {
   constexpr int NW = NTH / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kmax = min(m, n);
+  const int kmax = min(min(m, n), kcap);
   if (rr)
     for (int e = tid; e < n * n; e += NTH) rr[e] = 0;
   for (int k = 0; k < kmax; ++k) {
@@ -179,6 +179,13 @@ __device__ __forceinline__ void qr_panel(T *a, int lda, T *rr, int m, int n, T *
 
 constexpr int QR_ROWS = 256;   // rows of a register-resident panel (b <= 256)
 
+// How a QR launch treats the per-tile column count kq (the columns of the
+// sketch basis Q that the later steps use):
+//   KQ_SET  the QR of the sketches: stop early where the sketch shows the
+//           rest of the tile to be negligible (qr_reg_kernel), write kq[t];
+//   KQ_CAP  the QR of the projections: at most kq[t] reflectors.
+enum KqMode : int { KQ_SET = 1, KQ_CAP = 2 };
+
 // QR of every tile's m x n panel (tile t at A + t * stride, leading dim lda),
 // m = s_i (m_sel 0) or s_j (m_sel 1); R (optional) at R + t * n * n,
 // factorised in place in global memory by CT threads (tiles of more than
@@ -186,7 +193,7 @@ constexpr int QR_ROWS = 256;   // rows of a register-resident panel (b <= 256)
 template <typename T>
 __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
                                                        int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
-                                                       int skip_diag) {
+                                                       int skip_diag, int32_t *kq, int kq_mode) {
   __shared__ T red[CT / 64];
   __shared__ T beta_s[S_MAX];
   const int t = blockIdx.x;
@@ -195,7 +202,9 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
   const int m = m_sel == 0 ? tile_rows(rows, b, i) : tile_rows(cols, b, j);
   T *a = A + (int64_t)t * stride;
   T *rr = R ? R + (int64_t)t * n * n : nullptr;
-  qr_panel<T, CT>(a, lda, rr, m, n, red, beta_s);
+  const int kcap = kq_mode == KQ_CAP ? kq[t] : n;
+  qr_panel<T, CT>(a, lda, rr, m, n, kcap, red, beta_s);
+  if (kq_mode == KQ_SET && threadIdx.x == 0) kq[t] = min(m, n);
 }
 
 // The same QR for panels of at most QR_ROWS rows, held in registers.  Thread
@@ -218,6 +227,20 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
 // loop over blocks unrolled, so every register index is static.  Q is formed
 // backwards the same way: the threads of column k broadcast v_k, then hold
 // column k of Q (H_k e_k); the columns c > k take H_k.
+//
+// With KQ_SET (the QR of the sketches Y = X Omega, Omega Gaussian) the
+// factorisation stops after a block of 8 reflectors once the rest of the
+// sketch is negligible: after k reflectors the rows >= k of the columns
+// c >= k hold the parts of y_c = X omega_c outside the span P_k of the first
+// k columns, and P_k depends on omega_0 .. omega_{k-1} only, so their energy
+// E is a sum of n - k independent samples of ||(I - P_k) X omega||^2, whose
+// mean is ||(I - P_k) X||_F^2 (the posterior error estimate of the
+// randomized range finder).  The QR stops at k when E <= stop (n - k)
+// ||X||_F^2 with at least OVERSAMPLE samples left; the energy it leaves out
+// of the basis then stays below 1e3 stop ||X||_F^2 unless a chi-square
+// variable of n - k >= 8 degrees of freedom falls under 1e-3 of its mean
+// (probability below 1e-11).  Q keeps k columns (the rest zero) and kq[t] = k
+// caps the QR of the projections and the Jacobi SVD that follow.
 constexpr int QRR_PARTS = 8;                      // threads per column
 constexpr int QRR_REGS = QR_ROWS / QRR_PARTS;     // rows per thread
 constexpr int QRR_THREADS = QRR_PARTS * S_MAX;    // 512
@@ -263,9 +286,11 @@ __device__ __forceinline__ T part_sum8(T x) {
 template <typename T>
 __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void qr_reg_kernel(T *A, int lda, int64_t stride, T *R, int qr, int qc,
                                                             int64_t rows, int64_t cols, int64_t b, int m_sel, int n,
-                                                            int skip_diag) {
+                                                            int skip_diag, int32_t *kq, int kq_mode,
+                                                            const T *norms2, T stop) {
   __shared__ T vbuf[2][QR_ROWS];
   __shared__ T beta_s[S_MAX];
+  __shared__ T ctail[S_MAX];
   const int t = blockIdx.x;
   const int i = t % qr, j = t / qr;
   if (skip_diag && i == j) return;
@@ -273,7 +298,11 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   T *a = A + (int64_t)t * stride;
   T *rr = R ? R + (int64_t)t * n * n : nullptr;
   const int tid = threadIdx.x, c = tid / QRR_PARTS, p = tid % QRR_PARTS;
-  const int kmax = min(m, n);
+  int kmax = min(m, n);   // the same in every thread
+  // columns that can be nonzero: with KQ_CAP those past kq[t] are zero (the
+  // sketch basis has kq[t] columns) and stay zero under every reflector
+  const int ncol = kq_mode == KQ_CAP ? min(n, kq[t]) : n;
+  kmax = min(kmax, ncol);
   T y[QRR_REGS];
 #pragma unroll
   for (int q = 0; q < QRR_REGS; ++q) {
@@ -335,7 +364,22 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         }
       }
       __syncthreads();
-      if (c > k && c < n) reflect(vb, Kc, beta_s[k]);
+      if (c > k && c < ncol) reflect(vb, Kc, beta_s[k]);
+    }
+    // the early stop after this block: E from the rows >= KN of the columns
+    // >= KN, summed in column order (the same value, so the same decision, in
+    // every thread)
+    constexpr int KN = QRR_PARTS * (K + 1);
+    if (kq_mode == KQ_SET && KN < kmax && KN + OVERSAMPLE <= n) {
+      T t4[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int q = K + 1; q < QRR_REGS; ++q) t4[(q - K - 1) & 3] += y[q] * y[q];
+      const T tl = part_sum8((t4[0] + t4[1]) + (t4[2] + t4[3]));
+      if (p == 0 && c >= KN && c < n) ctail[c] = tl;
+      __syncthreads();   // the next write of ctail is a block of reflectors later
+      T e = 0;
+      for (int x = KN; x < n; ++x) e += ctail[x];
+      if (e <= stop * T(n - KN) * norms2[t]) kmax = KN;
     }
   };
   forward(std::integral_constant<int, 0>());
@@ -347,6 +391,7 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
   forward(std::integral_constant<int, 6>());
   forward(std::integral_constant<int, 7>());
   static_assert(QRR_BLOCKS == 8, "one forward/backward call per block of 8 reflectors");
+  if (kq_mode == KQ_SET && tid == 0) kq[t] = kmax;
 
   // R above the diagonal: rows r < c of column c are final
   if (rr && c < n) {
@@ -382,7 +427,7 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
         }
       }
       __syncthreads();
-      if (c > k && c < n) reflect(vb, Kc, beta);
+      if (c > k && c < kmax) reflect(vb, Kc, beta);   // the columns past kmax are zero
     }
   };
   backward(std::integral_constant<int, 7>());
@@ -414,21 +459,24 @@ constexpr int JPARTS = 8;
 // starts the eight columns a wave reads at once on different banks.
 __host__ __device__ constexpr int jacobi_rpl(int np) { return (np + JPARTS - 1) / JPARTS; }
 __host__ __device__ constexpr int jacobi_ld(int rpl) { return JPARTS * rpl + 2; }
+__host__ __device__ constexpr int cmin(int a, int b) { return a < b ? a : b; }
 
-// One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n),
-// then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
+// One-sided Jacobi SVD of M = R2^T (n x n, R2 of every tile at R + t n n;
+// its rows and columns from kq[t] on are zero, so only the first kq[t]
+// columns take part in the rotations), then the rank at the tolerance.  Writes W = M J (n x n, column k of norm
 // sigma_k) to Wout + t n n, J to Jout + t n n, the columns in decreasing
 // order of sigma to perm + t n, the rank to ranks[t] (0 for a skipped
 // diagonal tile) and flags[t] = 1 when the tolerance was not met within
 // max_rank columns (the rank is then max_rank); jstat[2t], jstat[2t + 1] =
-// the sweeps run and the rotations applied (the measure of its work).
+// the pairs visited (sweeps x pairs x rounds: the 2 x 2 Gram blocks formed)
+// and the rotations applied (the measure of its work).
 // RPL = jacobi_rpl(np) is a compile-time count, so the row loops of a round
 // run without guards: the kernel is bound by VALU issue, not by LDS.
 template <typename T, int RPL>
 __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T *Jout, int32_t *perm,
                                                         int32_t *ranks, int32_t *flags, int32_t *jstat,
-                                                        const T *norms2, int qr, int qc, int n, int max_rank, T tol,
-                                                        T conv, int skip_diag) {
+                                                        const T *norms2, const int32_t *kq, int qr, int qc, int n,
+                                                        int max_rank, T tol, T conv, int skip_diag) {
   extern __shared__ __attribute__((aligned(16))) unsigned char jacobi_lds[];
   __shared__ T sig2[S_MAX];
   __shared__ int order[S_MAX];
@@ -447,13 +495,14 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   }
   __shared__ int nrot;
   if (tid == 0) nrot = 0;
-  const int np = (n + 1) & ~1;          // players of the round-robin (a zero column when n is odd)
+  const int nall = (n + 1) & ~1;        // columns held in LDS (a zero column when n is odd)
+  const int np = (min(n, kq[t]) + 1) & ~1;   // players of the round-robin
   const int npairs = np / 2;
   constexpr int JLD = jacobi_ld(RPL), ROWS = JPARTS * RPL;
   T *Ms = reinterpret_cast<T *>(jacobi_lds);
-  T *Js = Ms + JLD * np;
+  T *Js = Ms + JLD * nall;
   const T *rt = R + (int64_t)t * n * n;
-  for (int e = tid; e < ROWS * np; e += CT) {
+  for (int e = tid; e < ROWS * nall; e += CT) {
     const int r = e % ROWS, c = e / ROWS;
     Ms[r + c * JLD] = (r < n && c < n) ? rt[c + (int64_t)r * n] : T(0);    // M = R2^T
     Js[r + c * JLD] = r == c ? T(1) : T(0);
@@ -472,74 +521,91 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
   const T eps = sizeof(T) == 8 ? T(2.220446049250313e-16) : T(1.1920929e-7);
   const T negligible = (T(n) * eps) * (T(n) * eps) * norms2[t];
   int sweeps = 0, my_rot = 0;
-  for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
-    ++sweeps;
-    // round-robin: position 0 holds player 0, position x >= 1 player
-    // 1 + (x - 1 + round) mod (np - 1), i.e. x at round 0, and each round
-    // every player but 0 moves on by one (np - 1 wrapping to 1)
-    int pa = jp, pb = np - 1 - jp;        // the players at this pair's two positions
-    T cmax = 0;                            // this pair slot's largest cos^2 in the sweep
-    for (int round = 0; round < np - 1; ++round) {
-      if (jp < npairs) {
-        const int p = min(pa, pb), q = max(pa, pb);
-        // the pair's rows of M stay in registers for the rotation (its rows
-        // of J are read only when it rotates: most pairs of a late sweep do not)
-        T mp[RPL], mq[RPL];
-        T al = 0, be = 0, ga = 0;
-#pragma unroll
-        for (int e = 0; e < RPL; ++e) {
-          const int r = jpart + JPARTS * e;
-          mp[e] = Ms[r + p * JLD];
-          mq[e] = Ms[r + q * JLD];
-          al += mp[e] * mp[e];
-          be += mq[e] * mq[e];
-          ga += mp[e] * mq[e];
-        }
-        static_assert(JPARTS == QRR_PARTS, "the 8-lane sums serve both kernels");
-        al = part_sum8(al);
-        be = part_sum8(be);
-        ga = part_sum8(ga);
-        // |cos| of the pair's angle against conv, squared (no square root);
-        // the rotation's tangent tt = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
-        // zeta = (be - al) / (2 ga), written with one division and one root
-        const T g2 = ga * ga, ab = al * be;
-        if (al > negligible && be > negligible && g2 > conv * conv * ab) {
-          cmax = fmax(cmax, g2 / ab);
-          if (jpart == 0) ++my_rot;
-          const T d = be - al;
-          const T sg = (d == T(0) || (d > T(0)) == (ga > T(0))) ? T(1) : T(-1);
-          const T tt = sg * T(2) * fabs(ga) / (fabs(d) + sqrt(d * d + T(4) * g2));
-          const T cs = T(1) / sqrt(T(1) + tt * tt);
-          const T sn = cs * tt;
-#pragma unroll
-          for (int e = 0; e < RPL; ++e) {
+  // the sweeps over the rows < 8 RP that a core can have nonzero (RP =
+  // jacobi_rpl(np) for this tile: the rows from kq[t] on are zero in M and
+  // in the columns of J that rotate), so a tile with a short basis does
+  // proportionally less work per pair
+  auto run = [&](auto rc) {
+    constexpr int RP = decltype(rc)::value;
+    for (int sweep = 0; sweep < 40 && np > 1; ++sweep) {
+      ++sweeps;
+      // round-robin: position 0 holds player 0, position x >= 1 player
+      // 1 + (x - 1 + round) mod (np - 1), i.e. x at round 0, and each round
+      // every player but 0 moves on by one (np - 1 wrapping to 1)
+      int pa = jp, pb = np - 1 - jp;        // the players at this pair's two positions
+      T cmax = 0;                            // this pair slot's largest cos^2 in the sweep
+      for (int round = 0; round < np - 1; ++round) {
+        if (jp < npairs) {
+          const int p = min(pa, pb), q = max(pa, pb);
+          // the pair's rows of M stay in registers for the rotation (its rows
+          // of J are read only when it rotates: most pairs of a late sweep do not)
+          T mp[RP], mq[RP];
+          T al = 0, be = 0, ga = 0;
+  #pragma unroll
+          for (int e = 0; e < RP; ++e) {
             const int r = jpart + JPARTS * e;
-            const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
-            Ms[r + p * JLD] = cs * mp[e] - sn * mq[e];
-            Ms[r + q * JLD] = sn * mp[e] + cs * mq[e];
-            Js[r + p * JLD] = cs * jpv - sn * jqv;
-            Js[r + q * JLD] = sn * jpv + cs * jqv;
+            mp[e] = Ms[r + p * JLD];
+            mq[e] = Ms[r + q * JLD];
+            al += mp[e] * mp[e];
+            be += mq[e] * mq[e];
+            ga += mp[e] * mq[e];
           }
+          static_assert(JPARTS == QRR_PARTS, "the 8-lane sums serve both kernels");
+          al = part_sum8(al);
+          be = part_sum8(be);
+          ga = part_sum8(ga);
+          // |cos| of the pair's angle against conv, squared (no square root);
+          // the rotation's tangent tt = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)),
+          // zeta = (be - al) / (2 ga), written with one division and one root
+          const T g2 = ga * ga, ab = al * be;
+          if (al > negligible && be > negligible && g2 > conv * conv * ab) {
+            cmax = fmax(cmax, g2 / ab);
+            if (jpart == 0) ++my_rot;
+            const T d = be - al;
+            const T sg = (d == T(0) || (d > T(0)) == (ga > T(0))) ? T(1) : T(-1);
+            const T tt = sg * T(2) * fabs(ga) / (fabs(d) + sqrt(d * d + T(4) * g2));
+            const T cs = T(1) / sqrt(T(1) + tt * tt);
+            const T sn = cs * tt;
+  #pragma unroll
+            for (int e = 0; e < RP; ++e) {
+              const int r = jpart + JPARTS * e;
+              const T jpv = Js[r + p * JLD], jqv = Js[r + q * JLD];
+              Ms[r + p * JLD] = cs * mp[e] - sn * mq[e];
+              Ms[r + q * JLD] = sn * mp[e] + cs * mq[e];
+              Js[r + p * JLD] = cs * jpv - sn * jqv;
+              Js[r + q * JLD] = sn * jpv + cs * jqv;
+            }
+          }
+          // the slot's maximum, before the sweep's last barrier; the buffers
+          // alternate by sweep, so the next sweep's writes never meet this
+          // sweep's reads
+          if (jpart == 0 && round == np - 2) offw[sweep & 1][jp] = cmax;
         }
-        // the slot's maximum, before the sweep's last barrier; the buffers
-        // alternate by sweep, so the next sweep's writes never meet this
-        // sweep's reads
-        if (jpart == 0 && round == np - 2) offw[sweep & 1][jp] = cmax;
+        if (pa != 0) pa = pa == np - 1 ? 1 : pa + 1;
+        pb = pb == np - 1 ? 1 : pb + 1;
+        __syncthreads();
       }
-      if (pa != 0) pa = pa == np - 1 ? 1 : pa + 1;
-      pb = pb == np - 1 ? 1 : pb + 1;
-      __syncthreads();
+      // largest cos^2 of the sweep
+      T mx = 0;
+      for (int x = 0; x < npairs; ++x) mx = fmax(mx, offw[sweep & 1][x]);
+      if (mx <= conv * conv) break;
     }
-    // largest cos^2 of the sweep
-    T mx = 0;
-    for (int x = 0; x < npairs; ++x) mx = fmax(mx, offw[sweep & 1][x]);
-    if (mx <= conv * conv) break;
+  };
+  switch (jacobi_rpl(np)) {
+    case 1: run(std::integral_constant<int, cmin(1, RPL)>()); break;
+    case 2: run(std::integral_constant<int, cmin(2, RPL)>()); break;
+    case 3: run(std::integral_constant<int, cmin(3, RPL)>()); break;
+    case 4: run(std::integral_constant<int, cmin(4, RPL)>()); break;
+    case 5: run(std::integral_constant<int, cmin(5, RPL)>()); break;
+    case 6: run(std::integral_constant<int, cmin(6, RPL)>()); break;
+    case 7: run(std::integral_constant<int, cmin(7, RPL)>()); break;
+    default: run(std::integral_constant<int, RPL>()); break;
   }
   if (my_rot > 0) atomicAdd(&nrot, my_rot);   // LDS; read after the barriers below
   // column norms, the order of decreasing sigma (ties by column index)
   for (int c = wave; c < n; c += CT / 64) {
     T s = 0;
-    for (int r = lane; r < np; r += 64) s += Ms[r + c * JLD] * Ms[r + c * JLD];
+    for (int r = lane; r < nall; r += 64) s += Ms[r + c * JLD] * Ms[r + c * JLD];
     s = wave_sum(s);
     if (lane == 0) sig2[c] = s;
   }
@@ -584,7 +650,7 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
     }
     ranks[t] = r;
     flags[t] = fl;
-    jstat[2 * t] = sweeps;
+    jstat[2 * t] = sweeps * npairs * (np - 1);
     jstat[2 * t + 1] = nrot;
   }
 }
@@ -593,7 +659,8 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
 // in tile-column order, one thread per tile row (then per tile column) and
 // one thread for the scan of the q row sums.  info[0] = columns in all,
 // info[1] = tiles flagged, info[2] = 1 when the columns exceed the capacity,
-// info[3], info[4] = Jacobi sweeps and rotations summed over the tiles.
+// info[3], info[4] = Jacobi pair visits and rotations summed over the tiles,
+// info[5] = the sketch basis columns kept (kq) summed over the tiles.
 constexpr int SCAN_THREADS = 256;
 __device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, int skip_diag, int64_t *ooff,
                                          int64_t *ioff, int64_t *sums, int64_t *total_out) {
@@ -649,36 +716,43 @@ __device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, i
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void rank_scan_kernel(const int32_t *ranks, const int32_t *flags,
-                                                                const int32_t *jstat, int qr, int qc, int skip_diag,
+                                                                const int32_t *jstat, const int32_t *kq, int qr,
+                                                                int qc, int skip_diag,
                                                                 int64_t *ooff, int64_t *ioff, int64_t *sums,
                                                                 int64_t capacity, int32_t *info) {
   __shared__ int64_t total;
-  __shared__ int64_t part_w[3][SCAN_THREADS / 64];
+  __shared__ int64_t part_w[4][SCAN_THREADS / 64];
   offsets_by_rows_and_cols(ranks, qr, qc, skip_diag, ooff, ioff, sums, &total);
-  int64_t nf = 0, nsw = 0, nrot = 0;
+  int64_t nf = 0, nvis = 0, nrot = 0, nkq = 0;
   for (int t = threadIdx.x; t < qr * qc; t += SCAN_THREADS) {
-    if (!(skip_diag && t % qr == t / qr)) nf += flags[t];
-    nsw += jstat[2 * t];
+    if (!(skip_diag && t % qr == t / qr)) {   // kq of a skipped tile is never written
+      nf += flags[t];
+      nkq += kq[t];
+    }
+    nvis += jstat[2 * t];
     nrot += jstat[2 * t + 1];
   }
   nf = wave_sum(nf);
-  nsw = wave_sum(nsw);
+  nvis = wave_sum(nvis);
   nrot = wave_sum(nrot);
+  nkq = wave_sum(nkq);
   if ((threadIdx.x & 63) == 0) {
     part_w[0][threadIdx.x >> 6] = nf;
-    part_w[1][threadIdx.x >> 6] = nsw;
+    part_w[1][threadIdx.x >> 6] = nvis;
     part_w[2][threadIdx.x >> 6] = nrot;
+    part_w[3][threadIdx.x >> 6] = nkq;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t x[3] = {0, 0, 0};
-    for (int k = 0; k < 3; ++k)
+    int64_t x[4] = {0, 0, 0, 0};
+    for (int k = 0; k < 4; ++k)
       for (int w = 0; w < SCAN_THREADS / 64; ++w) x[k] += part_w[k][w];
     info[0] = (int32_t)min<int64_t>(total, 0x7fffffff);
     info[1] = (int32_t)x[0];
     info[2] = total > capacity ? 1 : 0;
     info[3] = (int32_t)min<int64_t>(x[1], 0x7fffffff);
     info[4] = (int32_t)min<int64_t>(x[2], 0x7fffffff);
+    info[5] = (int32_t)min<int64_t>(x[3], 0x7fffffff);
   }
 }
 
@@ -830,7 +904,7 @@ struct CompressLayout {
   int qr = 0, qc = 0, s = 0;
   int64_t ntile = 0;
   size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, jstat = 0,
-         ooff = 0, ioff = 0, sums = 0, total = 0;
+         kq = 0, ooff = 0, ioff = 0, sums = 0, total = 0;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -855,6 +929,7 @@ CompressLayout compress_layout(int64_t rows, int64_t cols, int64_t b, int max_ra
   L.ranks = o; o += al256((size_t)L.ntile * 4);
   L.flags = o; o += al256((size_t)L.ntile * 4);
   L.jstat = o; o += al256((size_t)L.ntile * 8);
+  L.kq = o; o += al256((size_t)L.ntile * 4);
   L.ooff = o; o += al256((size_t)L.ntile * 8);
   L.ioff = o; o += al256((size_t)L.ntile * 8);
   L.sums = o; o += al256((size_t)std::max(L.qr, L.qc) * 8);
@@ -880,6 +955,14 @@ tlr_status check_compress_args(tlr_dtype dt, int64_t rows, int64_t cols, int32_t
 // orthogonal: dropping columns of W drops exactly their norms.
 template <typename T>
 T conv_tol() { return sizeof(T) == 8 ? T(1e-8) : T(1e-5f); }
+
+// The early stop of the QR of the sketches: the basis stops growing once the
+// sketch puts the energy it leaves out near 1e-10 tol^2 ||X||_F^2, below
+// 1e-7 tol^2 ||X||_F^2 with probability above 1 - 1e-11.  That changes the
+// discarded energy the rank decision sees by at most 1e-7 of its bound and
+// the result tile by at most about 3e-4 tol ||X||_F.
+template <typename T>
+T range_stop(double tol) { return (T)(1e-10 * tol * tol); }
 
 // One launch of the Jacobi kernel for RPL rows per lane; the widest sketch
 // (S_MAX columns, RPL = 8) needs more than the default 64 KB of dynamic LDS
@@ -1027,16 +1110,17 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   if (st != TLR_OK) return st;
   MARK(pm.end());
   // 2. Y_t = Q R, Q kept in place
-  auto qr_launch = [&](T *A, T *R, int m_sel) {
+  int32_t *kq = as<int32_t>(w + L.kq);
+  auto qr_launch = [&](T *A, T *R, int m_sel, int kq_mode) {
     if (b <= QR_ROWS && n <= S_MAX)
       hipLaunchKernelGGL((qr_reg_kernel<T>), dim3(nt), dim3(QRR_THREADS), 0, s, A, (int)b, panel, R, L.qr, L.qc,
-                         rows, cols, b, m_sel, n, skip);
+                         rows, cols, b, m_sel, n, skip, kq, kq_mode, (const T *)norms, range_stop<T>(tol));
     else
       hipLaunchKernelGGL((qr_tiles_kernel<T>), dim3(nt), dim3(CT), 0, s, A, (int)b, panel, R, L.qr, L.qc, rows,
-                         cols, b, m_sel, n, skip);
+                         cols, b, m_sel, n, skip, kq, kq_mode);
   };
   MARK(pm.begin(2));
-  qr_launch(as<T>(w + L.y), (T *)nullptr, 0);
+  qr_launch(as<T>(w + L.y), (T *)nullptr, 0, KQ_SET);
   CHECK_LAUNCH("QR of the sketches");
   MARK(pm.end());
   // 3. Bt_t = X_t^T Q_t                      (s_j x s)
@@ -1047,7 +1131,7 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   MARK(pm.end());
   // 4. Bt_t = Q2 R2
   MARK(pm.begin(4));
-  qr_launch(as<T>(w + L.bt), as<T>(w + L.r2), 1);
+  qr_launch(as<T>(w + L.bt), as<T>(w + L.r2), 1, KQ_CAP);
   CHECK_LAUNCH("QR of the projections");
   MARK(pm.end());
   // 5. Jacobi on M = R2^T, ranks
@@ -1059,8 +1143,8 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
       constexpr int RPL = decltype(rc)::value;
       js = launch_jacobi<T, RPL>(nt, jnp, s, as<T>(w + L.r2), as<T>(w + L.w), as<T>(w + L.j),
                                  as<int32_t>(w + L.perm), as<int32_t>(w + L.ranks), as<int32_t>(w + L.flags),
-                                 as<int32_t>(w + L.jstat), norms, L.qr, L.qc, n, max_rank, (T)tol, conv_tol<T>(),
-                                 skip);
+                                 as<int32_t>(w + L.jstat), norms, (const int32_t *)kq, L.qr, L.qc, n, max_rank,
+                                 (T)tol, conv_tol<T>(), skip);
     };
     switch (jacobi_rpl(jnp)) {
       case 1: jac(std::integral_constant<int, 1>()); break;
@@ -1088,7 +1172,8 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   // 7. offsets, 8. packed factors and diagonal slots
   MARK(pm.begin(7));
   hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, as<int32_t>(w + L.ranks),
-                     as<int32_t>(w + L.flags), as<int32_t>(w + L.jstat), L.qr, L.qc, skip, as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
+                     as<int32_t>(w + L.flags), as<int32_t>(w + L.jstat), (const int32_t *)kq, L.qr, L.qc, skip,
+                     as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
                      as<int64_t>(w + L.sums), capacity, info);
   CHECK_LAUNCH("rank scan");
   MARK(pm.end());

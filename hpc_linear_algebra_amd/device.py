@@ -153,7 +153,7 @@ class TLROutputGemm:
         self.diag = torch.zeros((max(1, self.qr) * b * b) if has_diag else 1, dtype=tdt, device=device)
         self.outer = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
         self.inner = torch.zeros(max(1, self.capacity) * b, dtype=tdt, device=device)
-        self.info = torch.zeros(5, dtype=torch.int32, device=device)
+        self.info = torch.zeros(6, dtype=torch.int32, device=device)
 
     def __call__(self, alpha: float, A: DeviceTLR, B: DeviceTLR, beta: float, C: Optional[DeviceTLR], tol: float,
                  omega: torch.Tensor, stream: Optional[int] = None):

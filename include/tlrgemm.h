@@ -413,12 +413,16 @@ tlr_status tlr_compress_workspace_bytes(tlr_dtype dt, int64_t rows, int64_t cols
  *              columns each; tile (i,j) is written at the packed offsets of
  *              its new rank (U packed by tile row, V by tile column).  U has
  *              orthogonal columns of norms sigma_k, V orthonormal columns.
- *   info       device int32[5]: [0] columns used (sum of the new ranks),
+ *   info       device int32[6]: [0] columns used (sum of the new ranks),
  *              [1] tiles that did not meet tol within max_rank (their rank is
  *              max_rank), [2] 1 when [0] exceeds capacity (then no factor is
- *              written; ranks and diagonal are), [3] Jacobi sweeps and [4]
- *              Jacobi rotations summed over the tiles (the SVD's work, for
- *              measurement; [0], [3], [4] saturate at INT32_MAX).
+ *              written; ranks and diagonal are), [3] Jacobi pair visits
+ *              (2 x 2 Gram blocks formed) and [4] Jacobi rotations summed over
+ *              the tiles (the SVD's work, for measurement), [5] sketch basis
+ *              columns kept, summed over the tiles (the range finder stops
+ *              once the sketch shows the rest of a tile negligible; at most
+ *              max_rank + 8 per tile); [0], [3], [4], [5] saturate at
+ *              INT32_MAX.
  *   workspace  device, tlr_compress_workspace_bytes, 256-byte aligned.
  * Errors: TLR_ERR_INVALID_ARG, TLR_ERR_WORKSPACE, TLR_ERR_UNSUPPORTED (16-bit
  * types, max_rank > 56), TLR_ERR_HIP.

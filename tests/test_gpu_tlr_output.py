@@ -73,7 +73,7 @@ def _compress_on_gpu(X, b, has_diag, tol, max_rank, dtype="f64", capacity=None, 
     diag = torch.zeros(max(1, qr * b * b), dtype=tdt, device="cuda")
     outer = torch.full((max(1, capacity) * b,), 3.0, dtype=tdt, device="cuda")
     inner = torch.full((max(1, capacity) * b,), 3.0, dtype=tdt, device="cuda")
-    info = torch.full((5,), -1, dtype=torch.int32, device="cuda")
+    info = torch.full((6,), -1, dtype=torch.int32, device="cuda")
     ws = torch.empty(T.tlr_compress_workspace_bytes(dtype, rows, cols, b, max_rank), dtype=torch.uint8, device="cuda")
     T.tlr_compress(dtype, rows, cols, b, has_diag, Xd.data_ptr(), rows, tol, max_rank, om.data_ptr(),
                    ranks.data_ptr(), diag.data_ptr(), outer.data_ptr(), inner.data_ptr(), capacity, info.data_ptr(),
@@ -115,13 +115,16 @@ def test_compress_recovers_generated_ranks(n, b, diag):
     say(f"compress n={n} b={b}: info {info.tolist()}")
     assert info[1] == 0 and info[2] == 0 and info[0] == int(t.ranks.sum())
     assert np.array_equal(R, t.ranks)
-    # the Jacobi work counters: at least one sweep per compressed tile, at most
-    # the 40-sweep cap, and at most one rotation per pair and round
+    # the work counters: at least one pair visit per compressed tile, at most
+    # the 40-sweep cap of s/2 pairs in s - 1 rounds, at most one rotation per
+    # visit; the range finder keeps at least the tile's rank and at most s
+    # basis columns per tile
     q = -(-n // b)
     tiles = q * q - (q if diag else 0)
     s = 48 + 8
-    assert tiles <= info[3] <= 40 * tiles
-    assert 0 < info[4] <= int(info[3]) * (s // 2) * (s - 1)
+    assert tiles <= info[3] <= 40 * tiles * (s // 2) * (s - 1)
+    assert 0 < info[4] <= info[3]
+    assert int(R.sum()) <= info[5] <= s * tiles
     got = _unpacked(R, outer, inner, dg, n, n, b, diag, "f64")
     _check_against_oracle(got, X, 1e-7, "f64", ref_ranks=t.ranks, what=f"compress n={n}")
 
@@ -221,6 +224,10 @@ def test_full_tlr_output_workload():
     R, outer, inner, dg, info = g.host_result()
     say(f"tlr output workload: info {info.tolist()}")
     assert info[1] == 0 and info[2] == 0
+    # the tiles' singular values decay geometrically, so the range finder
+    # stops well short of the max_rank + 8 samples on this workload
+    tiles = (N // b) * (N // b - 1)
+    assert int(R.sum()) <= info[5] < (cfg["max_rank"] + 8) * tiles * 3 // 4
     got = _unpacked(R, outer, inner, dg, N, N, b, True, "f64")
     X = reference.gemm_reference(cfg["alpha"], cfg["opA"], A, cfg["opB"], B, cfg["beta"], reference.reconstruct(C))
     _check_against_oracle(got, X, cfg["tol"], "f64", what="tlr output workload")
