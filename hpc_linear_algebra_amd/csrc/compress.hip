@@ -656,73 +656,76 @@ __global__ __launch_bounds__(CT) void jacobi_rank_kernel(const T *R, T *Wout, T 
 }
 
 // Prefix sums of the ranks: outer offsets in tile-row order, inner offsets
-// in tile-column order, one thread per tile row (then per tile column) and
-// one thread for the scan of the q row sums.  info[0] = columns in all,
+// in tile-column order, each an exclusive scan over the q_r x q_c tiles in
+// that order by the whole workgroup, SCAN_THREADS tiles at a time (wave scans
+// by lane shuffles, then the wave totals).  info[0] = columns in all,
 // info[1] = tiles flagged, info[2] = 1 when the columns exceed the capacity,
 // info[3], info[4] = Jacobi pair visits and rotations summed over the tiles,
 // info[5] = the sketch basis columns kept (kq) summed over the tiles.
 constexpr int SCAN_THREADS = 256;
+
+// exclusive prefix sum of v over the workgroup; *total = the sum of all v
+// (in every thread)
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *wsum, int64_t *total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < SCAN_THREADS / 64; ++k) {
+    before += k < w ? wsum[k] : 0;
+    all += wsum[k];
+  }
+  __syncthreads();   // wsum is written again by the next call
+  *total = all;
+  return before + x - v;
+}
+
 __device__ void offsets_by_rows_and_cols(const int32_t *ranks, int qr, int qc, int skip_diag, int64_t *ooff,
-                                         int64_t *ioff, int64_t *sums, int64_t *total_out) {
-  const int tid = threadIdx.x;
+                                         int64_t *ioff, int64_t *total_out) {
+  __shared__ int64_t wsum[SCAN_THREADS / 64];
+  const int64_t nt = (int64_t)qr * qc;
   // outer: tile (i, j) after every tile of rows < i and tiles (i, j' < j)
-  for (int i = tid; i < qr; i += SCAN_THREADS) {
-    int64_t acc = 0;
-    for (int j = 0; j < qc; ++j) acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
-    sums[i] = acc;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < nt; base += SCAN_THREADS) {
+    const int64_t e = base + threadIdx.x;   // e = j + i qc
+    const int i = e < nt ? (int)(e / qc) : 0, j = e < nt ? (int)(e % qc) : 0;
+    const int64_t v = (e < nt && !(skip_diag && i == j)) ? ranks[i + (int64_t)j * qr] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan(v, wsum, &tot);
+    if (e < nt) ooff[i + (int64_t)j * qr] = carry + ex;
+    carry += tot;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int i = 0; i < qr; ++i) {
-      const int64_t x = sums[i];
-      sums[i] = acc;
-      acc += x;
-    }
-    *total_out = acc;
+  if (threadIdx.x == 0) *total_out = carry;
+  // inner: tile (i, j) after every tile of columns < j and tiles (i' < i, j),
+  // the storage order of the rank table
+  carry = 0;
+  for (int64_t base = 0; base < nt; base += SCAN_THREADS) {
+    const int64_t e = base + threadIdx.x;   // e = i + j qr
+    const int i = e < nt ? (int)(e % qr) : 0, j = e < nt ? (int)(e / qr) : 0;
+    const int64_t v = (e < nt && !(skip_diag && i == j)) ? ranks[e] : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan(v, wsum, &tot);
+    if (e < nt) ioff[e] = carry + ex;
+    carry += tot;
   }
-  __syncthreads();
-  for (int i = tid; i < qr; i += SCAN_THREADS) {
-    int64_t acc = sums[i];
-    for (int j = 0; j < qc; ++j) {
-      ooff[i + j * qr] = acc;
-      acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
-    }
-  }
-  __syncthreads();
-  // inner: tile (i, j) after every tile of columns < j and tiles (i' < i, j)
-  for (int j = tid; j < qc; j += SCAN_THREADS) {
-    int64_t acc = 0;
-    for (int i = 0; i < qr; ++i) acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
-    sums[j] = acc;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int j = 0; j < qc; ++j) {
-      const int64_t x = sums[j];
-      sums[j] = acc;
-      acc += x;
-    }
-  }
-  __syncthreads();
-  for (int j = tid; j < qc; j += SCAN_THREADS) {
-    int64_t acc = sums[j];
-    for (int i = 0; i < qr; ++i) {
-      ioff[i + j * qr] = acc;
-      acc += (skip_diag && i == j) ? 0 : ranks[i + j * qr];
-    }
-  }
+  __syncthreads();   // *total_out is read by every thread after this
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void rank_scan_kernel(const int32_t *ranks, const int32_t *flags,
                                                                 const int32_t *jstat, const int32_t *kq, int qr,
                                                                 int qc, int skip_diag,
-                                                                int64_t *ooff, int64_t *ioff, int64_t *sums,
-                                                                int64_t capacity, int32_t *info) {
+                                                                int64_t *ooff, int64_t *ioff, int64_t capacity,
+                                                                int32_t *info) {
   __shared__ int64_t total;
   __shared__ int64_t part_w[4][SCAN_THREADS / 64];
-  offsets_by_rows_and_cols(ranks, qr, qc, skip_diag, ooff, ioff, sums, &total);
+  offsets_by_rows_and_cols(ranks, qr, qc, skip_diag, ooff, ioff, &total);
   int64_t nf = 0, nvis = 0, nrot = 0, nkq = 0;
   for (int t = threadIdx.x; t < qr * qc; t += SCAN_THREADS) {
     if (!(skip_diag && t % qr == t / qr)) {   // kq of a skipped tile is never written
@@ -823,10 +826,9 @@ __global__ __launch_bounds__(CT) void pack_kernel(const T *X, int64_t ldx, const
 
 // Column offsets of every tile's factors from the device rank table.
 __global__ __launch_bounds__(SCAN_THREADS) void factor_offsets_kernel(const int32_t *ranks, int qr, int qc,
-                                                                     int has_diag, int64_t *ooff, int64_t *ioff,
-                                                                     int64_t *sums) {
+                                                                     int has_diag, int64_t *ooff, int64_t *ioff) {
   __shared__ int64_t total;
-  offsets_by_rows_and_cols(ranks, qr, qc, has_diag, ooff, ioff, sums, &total);
+  offsets_by_rows_and_cols(ranks, qr, qc, has_diag, ooff, ioff, &total);
 }
 
 // C[64 x 64 block of tile t] <- alpha X_t + beta C (C read only when beta != 0):
@@ -904,7 +906,7 @@ struct CompressLayout {
   int qr = 0, qc = 0, s = 0;
   int64_t ntile = 0;
   size_t y = 0, bt = 0, uf = 0, vf = 0, r2 = 0, w = 0, j = 0, norms = 0, perm = 0, ranks = 0, flags = 0, jstat = 0,
-         kq = 0, ooff = 0, ioff = 0, sums = 0, total = 0;
+         kq = 0, ooff = 0, ioff = 0, total = 0;
 };
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -932,7 +934,6 @@ CompressLayout compress_layout(int64_t rows, int64_t cols, int64_t b, int max_ra
   L.kq = o; o += al256((size_t)L.ntile * 4);
   L.ooff = o; o += al256((size_t)L.ntile * 8);
   L.ioff = o; o += al256((size_t)L.ntile * 8);
-  L.sums = o; o += al256((size_t)std::max(L.qr, L.qc) * 8);
   L.total = o;
   return L;
 }
@@ -1174,7 +1175,7 @@ tlr_status compress_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const
   hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, as<int32_t>(w + L.ranks),
                      as<int32_t>(w + L.flags), as<int32_t>(w + L.jstat), (const int32_t *)kq, L.qr, L.qc, skip,
                      as<int64_t>(w + L.ooff), as<int64_t>(w + L.ioff),
-                     as<int64_t>(w + L.sums), capacity, info);
+                     capacity, info);
   CHECK_LAUNCH("rank scan");
   MARK(pm.end());
   MARK(pm.begin(8));
@@ -1195,9 +1196,7 @@ tlr_status expand_t(int64_t rows, int64_t cols, int64_t b, int has_diag, const i
   const int64_t nt = (int64_t)qr * qc;
   int64_t *ooff = static_cast<int64_t *>(ws);
   int64_t *ioff = ooff + nt;
-  int64_t *sums = ioff + nt;
-  hipLaunchKernelGGL(factor_offsets_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, ranks, qr, qc, has_diag, ooff, ioff,
-                     sums);
+  hipLaunchKernelGGL(factor_offsets_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, ranks, qr, qc, has_diag, ooff, ioff);
   CHECK_LAUNCH("factor offsets");
   const int bpd = (int)((b + EB - 1) / EB);
   const int bpt = bpd * bpd;
@@ -1284,8 +1283,7 @@ tlr_status expand(tlr_dtype dt, int64_t rows, int64_t cols, int32_t b, int32_t h
   if (!C || !X || !ranks || !ws) return fail(TLR_ERR_INVALID_ARG, "expand: null buffer");
   if (has_diag && !X->diag) return fail(TLR_ERR_INVALID_ARG, "expand: null diagonal");
   const int64_t qrr = (rows + b - 1) / b, qcc = (cols + b - 1) / b, nt = qrr * qcc;
-  if (ws_bytes < (size_t)(16 * nt + 8 * std::max(qrr, qcc)))
-    return fail(TLR_ERR_WORKSPACE, "expand: workspace below 16 bytes per tile plus 8 per tile row or column");
+  if (ws_bytes < (size_t)(16 * nt)) return fail(TLR_ERR_WORKSPACE, "expand: workspace below 16 bytes per tile");
   if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(TLR_ERR_INVALID_ARG, "expand: workspace not 8-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == TLR_F64) return expand_t<double>(rows, cols, b, has_diag, ranks, X, alpha, beta, C, ldc, ws, s);

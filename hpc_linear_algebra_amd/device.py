@@ -146,7 +146,7 @@ class TLROutputGemm:
         self.capacity = n_off * max_rank if capacity is None else capacity
         tdt = _TORCH[dtype]
         self.scratch = torch.empty((self.n, self.m), dtype=tdt, device=device)     # column-major m x n
-        self.ews = torch.empty(max(16 * nt + 8 * max(self.qr, self.qc), 256), dtype=torch.uint8, device=device)
+        self.ews = torch.empty(max(16 * nt, 256), dtype=torch.uint8, device=device)
         self.cws = torch.empty(T.tlr_compress_workspace_bytes(dtype, self.m, self.n, b, max_rank),
                                dtype=torch.uint8, device=device)
         self.ranks = torch.zeros(nt, dtype=torch.int32, device=device)

@@ -378,8 +378,8 @@ tlr_status tlr_dense_gemm(tlr_dtype dt, tlr_op opA, tlr_op opB, int64_t m, int64
  *              dense diagonal): the layout of X's packed factors (as for
  *              tlr_shape.ranks).
  *   X          device buffers of the operand.
- *   workspace  device, at least 16 * q_r * q_c + 8 * max(q_r, q_c) bytes,
- *              8-byte aligned (the factor offsets, computed on the device).
+ *   workspace  device, at least 16 * q_r * q_c bytes, 8-byte aligned (the
+ *              factor offsets, computed on the device).
  * beta == 0 never reads C.  Errors: TLR_ERR_INVALID_ARG, TLR_ERR_WORKSPACE,
  * TLR_ERR_UNSUPPORTED (16-bit types), TLR_ERR_HIP.
  */
