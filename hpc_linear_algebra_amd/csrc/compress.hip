@@ -229,7 +229,7 @@ __global__ __launch_bounds__(CT) void qr_tiles_kernel(T *A, int lda, int64_t str
 // column k of Q (H_k e_k); the columns c > k take H_k.
 //
 // With KQ_SET (the QR of the sketches Y = X Omega, Omega Gaussian) the
-// factorisation stops after a block of 8 reflectors once the rest of the
+// factorisation stops after a multiple of 4 reflectors once the rest of the
 // sketch is negligible: after k reflectors the rows >= k of the columns
 // c >= k hold the parts of y_c = X omega_c outside the span P_k of the first
 // k columns, and P_k depends on omega_0 .. omega_{k-1} only, so their energy
@@ -365,21 +365,22 @@ __global__ __launch_bounds__(QRR_THREADS) __attribute__((amdgpu_waves_per_eu(4))
       }
       __syncthreads();
       if (c > k && c < ncol) reflect(vb, Kc, beta_s[k]);
-    }
-    // the early stop after this block: E from the rows >= KN of the columns
-    // >= KN, summed in column order (the same value, so the same decision, in
-    // every thread)
-    constexpr int KN = QRR_PARTS * (K + 1);
-    if (kq_mode == KQ_SET && KN < kmax && KN + OVERSAMPLE <= n) {
-      T t4[4] = {0, 0, 0, 0};
+      // the early stop after every fourth reflector: E from the rows >= KN
+      // of the columns >= KN, summed in column order (the same value, so the
+      // same decision, in every thread)
+      const int KN = k + 1;
+      if (kq_mode == KQ_SET && (kk & 3) == 3 && KN < kmax && KN + OVERSAMPLE <= n) {
+        T t4[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int q = K + 1; q < QRR_REGS; ++q) t4[(q - K - 1) & 3] += y[q] * y[q];
-      const T tl = part_sum8((t4[0] + t4[1]) + (t4[2] + t4[3]));
-      if (p == 0 && c >= KN && c < n) ctail[c] = tl;
-      __syncthreads();   // the next write of ctail is a block of reflectors later
-      T e = 0;
-      for (int x = KN; x < n; ++x) e += ctail[x];
-      if (e <= stop * T(n - KN) * norms2[t]) kmax = KN;
+        for (int q = K; q < QRR_REGS; ++q)
+          if (q > K || p > kk) t4[(q - K) & 3] += y[q] * y[q];
+        const T tl = part_sum8((t4[0] + t4[1]) + (t4[2] + t4[3]));
+        if (p == 0 && c >= KN && c < n) ctail[c] = tl;
+        __syncthreads();   // the next write of ctail is four reflectors later
+        T e = 0;
+        for (int x = KN; x < n; ++x) e += ctail[x];
+        if (e <= stop * T(n - KN) * norms2[t]) kmax = KN;
+      }
     }
   };
   forward(std::integral_constant<int, 0>());
