@@ -392,7 +392,8 @@ def bench_tlr_out(args):
         Lp = g.gemm.launches()[pl]
         ach = Lp["useful_flops"] / (prod[pl] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 3), "peak": PEAK[dtype], "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK[dtype], 4), "traffic": None,
+                    "frac": round(ach / PEAK[dtype], 4),
+                    "traffic": traffic_from_profiles(Lp["stage"], cfg["name"]),
                     "kernel": f"the product's stage {Lp['stage']} launch" +
                               (" (final update, segmented-K)" if Lp["stage"] == 3 else ""),
                     "launch_ms": round(prod[pl], 4), "algorithmic_flops": Lp["useful_flops"]}
